@@ -1,0 +1,181 @@
+// C ABI of the KDA forward library: argument validation, workspace layout and
+// kernel launches.  Declarations and the contract of every entry point are in
+// include/kda.h.
+//
+// Error conventions follow the chunk_kda integration described on the page
+// "feat(kda): integrate KDA attention with tokamax backend and CP support"
+// (Runtime guards; the review commits of its second copy): unsupported shapes
+// are NOT_IMPLEMENTED, invalid configurations (a safe-gate lower bound outside
+// [-5, 0), packed input without a positive segment bound) are
+// INVALID_ARGUMENT, and there is never a silent fallback to another path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kda.h"
+#include "kda_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status_t fail(kda_status_t st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+  int64_t nc_fixed = 0, cmax = 0, smax = 0, record_bytes = 0;
+  size_t off_hdr = 0, off_segs = 0, off_chunks = 0, off_records = 0, total = 0;
+};
+
+bool is_pow_ok(int64_t d) { return d == 64 || d == 128; }
+
+kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
+  if (d == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->B < 0 || d->T < 0 || d->H < 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "B, T and H must be >= 0");
+  if (d->T > (int64_t)1 << 30 || d->B * d->T > (int64_t)1 << 31)
+    return fail(KDA_ERR_NOT_IMPLEMENTED, "B*T above 2^31 tokens is not supported");
+  if (!is_pow_ok(d->K) || !is_pow_ok(d->V))
+    return fail(KDA_ERR_NOT_IMPLEMENTED, "K and V must each be 64 or 128");
+  if (d->dtype != KDA_F32 && d->dtype != KDA_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_F32 or KDA_BF16");
+  if (d->o_dtype != KDA_F32 && d->o_dtype != KDA_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "o_dtype must be KDA_F32 or KDA_BF16");
+  if (d->chunk_size != 64) return fail(KDA_ERR_NOT_IMPLEMENTED, "chunk_size must be 64");
+  if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
+  if (d->safe_gate != 0 && d->safe_gate != 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "safe_gate must be 0 or 1");
+  if (d->safe_gate && !(d->lower_bound >= -5.f && d->lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "with safe_gate, lower_bound must lie in [-5, 0)");
+  if (!std::isnan(d->scale) && !std::isfinite(d->scale))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite (or NaN for 1/sqrt(K))");
+  if (has_seg && d->max_segments < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "packed input (segment_ids) needs max_segments >= 1");
+
+  const kda::InType in = d->dtype == KDA_BF16 ? kda::InType::BF16 : kda::InType::F32;
+  Plan p;
+  p.nc_fixed = (d->T + 63) / 64;
+  p.record_bytes = kda::record_bytes(in, d->K, d->V);
+  if (has_seg) {
+    p.smax = d->B * (int64_t)d->max_segments;
+    p.cmax = d->B * (p.nc_fixed + d->max_segments);
+  } else {
+    p.smax = d->B;
+    p.cmax = d->B * p.nc_fixed;
+  }
+  size_t off = 0;
+  p.off_hdr = off;
+  off = align_up(off + sizeof(kda::TableHeader));
+  p.off_segs = off;
+  off = align_up(off + (has_seg ? (size_t)p.smax * sizeof(kda::SegEntry) : 0));
+  p.off_chunks = off;
+  off = align_up(off + (has_seg ? (size_t)p.cmax * sizeof(kda::ChunkEntry) : 0));
+  p.off_records = off;
+  off = align_up(off + (size_t)p.cmax * (size_t)d->H * (size_t)p.record_bytes);
+  p.total = off;
+  *plan = p;
+  return KDA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd_workspace_size(const kda_fwd_desc_t* desc, int has_segment_ids, size_t* bytes) {
+  if (bytes == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  Plan plan;
+  const kda_status_t st = validate(desc, has_segment_ids != 0, &plan);
+  if (st != KDA_OK) return st;
+  *bytes = plan.total;
+  return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, const float* initial_state,
+                           const int32_t* segment_ids, void* o, float* final_state, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  const bool has_seg = segment_ids != nullptr;
+  Plan plan;
+  kda_status_t st = validate(desc, has_seg, &plan);
+  if (st != KDA_OK) return st;
+  const kda_fwd_desc_t& d = *desc;
+  const int64_t tokens = d.B * d.T;
+  if (tokens > 0 && d.H > 0) {
+    if (!q || !k || !v || !g || !beta || !o)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-NULL");
+    const void* ptrs[] = {q, k, v, g, beta, o, initial_state, segment_ids, final_state, workspace};
+    for (const void* ptr : ptrs)
+      if (ptr && !aligned16(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
+  }
+  if (workspace_bytes < plan.total || (plan.total > 0 && workspace == nullptr))
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(plan.total) + " bytes, got " + std::to_string(workspace_bytes));
+
+  kda::CallArgs a{};
+  a.B = d.B; a.T = d.T; a.H = d.H; a.K = d.K; a.V = d.V;
+  a.in = d.dtype == KDA_BF16 ? kda::InType::BF16 : kda::InType::F32;
+  a.out = d.o_dtype == KDA_BF16 ? kda::OutType::BF16 : kda::OutType::F32;
+  a.scale = std::isnan(d.scale) ? (float)(1.0 / std::sqrt((double)d.K)) : d.scale;
+  a.l2norm = d.use_qk_l2norm;
+  a.n_max = has_seg ? d.max_segments : 0;
+  a.nc_fixed = plan.nc_fixed;
+  a.cmax = plan.cmax;
+  a.smax = plan.smax;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.init = initial_state;
+  a.seg_ids = segment_ids;
+  a.o = o;
+  a.fin = final_state;
+  char* ws = static_cast<char*>(workspace);
+  a.hdr = reinterpret_cast<kda::TableHeader*>(ws + plan.off_hdr);
+  a.segs = reinterpret_cast<kda::SegEntry*>(ws + plan.off_segs);
+  a.chunks = reinterpret_cast<kda::ChunkEntry*>(ws + plan.off_chunks);
+  a.records = ws + plan.off_records;
+  a.record_bytes = plan.record_bytes;
+  a.stream = static_cast<hipStream_t>(stream);
+
+  if (d.B == 0 || d.H == 0) return KDA_OK;
+  hipError_t e = hipSuccess;
+  if (has_seg) {
+    if (d.T == 0) return KDA_OK;
+    e = kda::launch_prep(a);
+  } else if (d.T == 0) {
+    e = kda::launch_zero_states(a);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+    return KDA_OK;
+  }
+  if (e == hipSuccess) e = kda::launch_intra(a);
+  if (e == hipSuccess) e = kda::launch_recur(a);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, void* stream, uint32_t* flags) {
+  if (flags == nullptr || workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (workspace_bytes < sizeof(kda::TableHeader))
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than its header");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipStreamSynchronize(s);
+  kda::TableHeader hdr;
+  if (e == hipSuccess) e = hipMemcpy(&hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("flags: ") + hipGetErrorString(e));
+  *flags = hdr.flags;
+  return KDA_OK;
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+const char* kda_version(void) { return "kda-mi355x 0.1.0"; }
+
+}  // extern "C"

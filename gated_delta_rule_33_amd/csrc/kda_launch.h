@@ -1,0 +1,48 @@
+// Host-side launchers of the KDA forward kernels (one per kernel family).
+// Each validates nothing: kda_api.cpp checks every argument before calling.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kda.h"
+#include "kda_common.h"
+
+namespace kda {
+
+enum class InType { F32, BF16 };
+enum class OutType { F32, BF16 };
+
+// Everything the kernels of one call need, resolved on the host.
+struct CallArgs {
+  int64_t B, T, H, K, V;
+  InType in;
+  OutType out;
+  float scale;
+  int l2norm;
+  int n_max;                   // segments per row with packed input (0: fixed rows)
+  int64_t nc_fixed;            // chunks per row without segment_ids: ceil(T / 64)
+  int64_t cmax, smax;          // chunk / segment capacities of the tables and records
+  const void *q, *k, *v, *g, *beta;
+  const float* init;
+  const int32_t* seg_ids;
+  void* o;
+  float* fin;
+  // Workspace carve-up.
+  TableHeader* hdr;
+  SegEntry* segs;
+  ChunkEntry* chunks;
+  char* records;
+  int64_t record_bytes;
+  hipStream_t stream;
+};
+
+int64_t record_bytes(InType in, int64_t K, int64_t V);
+
+hipError_t launch_prep(const CallArgs& a);
+hipError_t launch_intra(const CallArgs& a);
+hipError_t launch_recur(const CallArgs& a);
+hipError_t launch_zero_states(const CallArgs& a);
+
+}  // namespace kda

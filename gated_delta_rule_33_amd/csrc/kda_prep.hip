@@ -1,0 +1,185 @@
+// Segment and chunk tables for packed inputs (integer work only).
+//
+// segment_ids [B,T] are 1-based with 0 = padding (KimiDeltaAttention.__call__,
+// page "feat(kda): integrate KDA attention with tokamax backend and CP
+// support", Public API).  A segment is a maximal run of equal non-zero ids.
+// Each segment is chunked from its own first token (64 tokens per chunk, the
+// last chunk partial), which is the natively packed layout the tokamax packed
+// forward page describes: no chunk straddles a boundary, and the tail rows of
+// a partial chunk are zero.
+//
+// Workgroup 0 builds the tables row by row with block-wide prefix sums; the
+// other workgroups write o = 0 for padding tokens.  Segments past max_segments
+// in a row are not recorded: workgroup 0 zeroes their outputs and raises
+// KDA_FLAG_SEGMENT_OVERFLOW.
+#include "kda_launch.h"
+
+namespace kda {
+namespace {
+
+constexpr int kPrepThreads = 1024;
+
+// Inclusive prefix sum over the 1024 threads of the block; *total gets the sum.
+__device__ int block_scan(int x, int* wave_sums, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int v = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) wave_sums[wv] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < kPrepThreads / 64; ++i) {
+      const int s = wave_sums[i];
+      wave_sums[i] = run;
+      run += s;
+    }
+    wave_sums[kPrepThreads / 64] = run;
+  }
+  __syncthreads();
+  const int res = v + wave_sums[wv];
+  *total = wave_sums[kPrepThreads / 64];
+  __syncthreads();
+  return res;
+}
+
+template <class TO>
+__device__ void zero_token(TO* o, int64_t tok, int64_t HV, int t0, int stride) {
+  for (int64_t e = t0; e < HV; e += stride) o[tok * HV + e] = TO(0);
+}
+
+struct PrepParams {
+  const int32_t* ids;
+  int64_t B, T, H, K, V;
+  int n_max;
+  TableHeader* hdr;
+  SegEntry* segs;
+  ChunkEntry* chunks;
+  void* o;
+  float* fin;
+};
+
+template <class TO>
+__global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
+  const int64_t T = p.T, HV = p.H * p.V;
+  TO* o = static_cast<TO*>(p.o);
+  if (blockIdx.x > 0) {
+    // Padding tokens: one wave per token.
+    const int lane = threadIdx.x & 63;
+    const int64_t wave = (int64_t)(blockIdx.x - 1) * (kPrepThreads / 64) + (threadIdx.x >> 6);
+    const int64_t n_waves = (int64_t)(gridDim.x - 1) * (kPrepThreads / 64);
+    for (int64_t tok = wave; tok < p.B * T; tok += n_waves)
+      if (p.ids[tok] == 0) zero_token(o, tok, HV, lane, 64);
+    return;
+  }
+
+  __shared__ int wave_sums[kPrepThreads / 64 + 1];
+  const int tid = threadIdx.x;
+  int seg_base = 0, chunk_base = 0;
+  uint32_t flags = 0;
+  for (int64_t b = 0; b < p.B; ++b) {
+    const int32_t* row = p.ids + b * T;
+    // Pass 1: segment starts and ends.
+    int row_segs = 0;
+    for (int64_t t0 = 0; t0 < T; t0 += kPrepThreads) {
+      const int64_t t = t0 + tid;
+      const int id = t < T ? row[t] : 0;
+      const int prev = (t > 0 && t < T) ? row[t - 1] : 0;
+      const int next = (t + 1 < T) ? row[t + 1] : 0;
+      const int start = (id != 0) && (t == 0 || id != prev);
+      const int end = (id != 0) && (t == T - 1 || next != id);
+      int total;
+      const int incl = block_scan(start, wave_sums, &total);
+      const int local = row_segs + incl - 1;
+      if (id != 0 && local < p.n_max) {
+        SegEntry* se = p.segs + seg_base + local;
+        if (start) { se->b = (int)b; se->t0 = (int)t; se->local = local; }
+        if (end) se->len = (int)(t + 1);   // end for now; turned into a length below
+      }
+      row_segs += total;
+    }
+    __syncthreads();
+    const int nrec = min(row_segs, p.n_max);
+    if (row_segs > p.n_max) flags |= KDA_FLAG_SEGMENT_OVERFLOW;
+    // Pass 2: lengths, chunk counts and first chunk of each recorded segment.
+    for (int s0 = 0; s0 < nrec; s0 += kPrepThreads) {
+      const int s = s0 + tid;
+      int nch = 0;
+      if (s < nrec) {
+        SegEntry* se = p.segs + seg_base + s;
+        se->len = se->len - se->t0;
+        nch = (se->len + kChunk - 1) / kChunk;
+        se->n_chunks = nch;
+      }
+      int total;
+      const int incl = block_scan(nch, wave_sums, &total);
+      if (s < nrec) p.segs[seg_base + s].chunk_begin = chunk_base + incl - nch;
+      chunk_base += total;
+    }
+    __syncthreads();
+    // Pass 3: chunk entries (one thread per recorded segment).
+    for (int s = tid; s < nrec; s += kPrepThreads) {
+      const SegEntry se = p.segs[seg_base + s];
+      for (int c = 0; c < se.n_chunks; ++c) {
+        ChunkEntry ce;
+        ce.b = (int)b;
+        ce.t0 = se.t0 + c * kChunk;
+        ce.len = min(kChunk, se.len - c * kChunk);
+        ce.seg = seg_base + s;
+        p.chunks[se.chunk_begin + c] = ce;
+      }
+    }
+    // Outputs of unrecorded segments are zero; so are the final states of
+    // slots no segment of this row reaches.
+    if (row_segs > p.n_max) {
+      const SegEntry last = p.segs[seg_base + nrec - 1];
+      for (int64_t t = last.t0 + last.len; t < T; ++t)
+        if (row[t] != 0) zero_token(o, b * T + t, HV, tid, kPrepThreads);
+    }
+    if (p.fin) {
+      const int64_t slot_elems = p.H * p.K * p.V;
+      for (int64_t e = (int64_t)nrec * slot_elems + tid; e < (int64_t)p.n_max * slot_elems; e += kPrepThreads)
+        p.fin[b * p.n_max * slot_elems + e] = 0.f;
+    }
+    seg_base += nrec;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.hdr->n_segments = seg_base;
+    p.hdr->n_chunks = chunk_base;
+    p.hdr->flags = flags;
+  }
+}
+
+__global__ void kda_fill_zero_kernel(float* x, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    x[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_prep(const CallArgs& a) {
+  PrepParams p{a.seg_ids, a.B, a.T, a.H, a.K, a.V, a.n_max, a.hdr, a.segs, a.chunks, a.o, a.fin};
+  const int64_t tokens = a.B * a.T;
+  const int zero_groups = (int)std::min<int64_t>(256, (tokens + 15) / 16);
+  const dim3 grid(1 + zero_groups);
+  if (a.out == OutType::F32)
+    hipLaunchKernelGGL(kda_prep_kernel<float>, grid, dim3(kPrepThreads), 0, a.stream, p);
+  else
+    hipLaunchKernelGGL(kda_prep_kernel<uint16_t>, grid, dim3(kPrepThreads), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+// final_state when no segment can occur (T == 0 without segment_ids).
+hipError_t launch_zero_states(const CallArgs& a) {
+  const int64_t n = a.B * a.H * a.K * a.V;
+  if (n <= 0 || a.fin == nullptr) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>(1024, (n + 255) / 256);
+  hipLaunchKernelGGL(kda_fill_zero_kernel, dim3(grid), dim3(256), 0, a.stream, a.fin, n);
+  return hipGetLastError();
+}
+
+}  // namespace kda

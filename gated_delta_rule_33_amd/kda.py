@@ -1,0 +1,180 @@
+"""Python binding of the KDA forward library (libkda.so, C ABI in include/kda.h).
+
+Argument marshalling only: every step of the forward runs in the HIP kernels.
+PyTorch supplies device memory and the current stream.  The argument list of
+``chunk_kda`` mirrors the chunk_kda entry point of the page "feat(kda):
+integrate KDA attention with tokamax backend and CP support" (Public API).
+There is no CPU or PyTorch fallback: without the built library, or without a
+GPU, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import warnings
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+KDA_FLAG_SEGMENT_OVERFLOW = 0x1
+
+EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_flags", "kda_last_error",
+            "kda_version")
+
+
+class KdaFwdDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("chunk_size", ctypes.c_int32),
+                ("use_qk_l2norm", ctypes.c_int32), ("safe_gate", ctypes.c_int32),
+                ("lower_bound", ctypes.c_float), ("max_segments", ctypes.c_int32)]
+
+
+class KdaError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with gated_delta_rule_33_amd/build.py "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    p, sz = ctypes.c_void_p, ctypes.c_size_t
+    lib.kda_chunk_fwd_workspace_size.argtypes = [ctypes.POINTER(KdaFwdDesc), ctypes.c_int, ctypes.POINTER(sz)]
+    lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_flags.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_uint32)]
+    lib.kda_chunk_fwd_flags.restype = ctypes.c_int
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _raise_for(status: int, what: str):
+    if status == KDA_OK:
+        return
+    msg = f"{what}: {load_library().kda_last_error().decode()}"
+    if status == KDA_ERR_NOT_IMPLEMENTED:
+        raise NotImplementedError(msg)
+    if status == KDA_ERR_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    raise KdaError(msg)
+
+
+def make_desc(B, T, H, K, V, dtype, o_dtype, scale=None, use_qk_l2norm=False, safe_gate=False,
+              lower_bound=None, max_segments=0, chunk_size=64) -> KdaFwdDesc:
+    return KdaFwdDesc(B=B, T=T, H=H, K=K, V=V, dtype=dtype, o_dtype=o_dtype,
+                      scale=float("nan") if scale is None else float(scale), chunk_size=chunk_size,
+                      use_qk_l2norm=int(bool(use_qk_l2norm)), safe_gate=int(bool(safe_gate)),
+                      lower_bound=0.0 if lower_bound is None else float(lower_bound),
+                      max_segments=int(max_segments or 0))
+
+
+def workspace_size(desc: KdaFwdDesc, has_segment_ids: bool) -> int:
+    n = ctypes.c_size_t(0)
+    _raise_for(load_library().kda_chunk_fwd_workspace_size(ctypes.byref(desc), int(has_segment_ids),
+                                                           ctypes.byref(n)), "kda_chunk_fwd_workspace_size")
+    return int(n.value)
+
+
+def _dtype_code(t):
+    import torch
+    if t == torch.float32:
+        return KDA_F32
+    if t == torch.bfloat16:
+        return KDA_BF16
+    raise NotImplementedError(f"dtype {t} is not supported (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=None,
+              output_final_state: bool = False, chunk_size: int = 64, A_log=None, dt_bias=None,
+              use_gate_in_kernel: bool = False, use_qk_l2norm_in_kernel: bool = False,
+              safe_gate: bool = False, lower_bound: Optional[float] = None, segment_ids=None,
+              disable_recompute: bool = False, N_max: Optional[int] = None, cp_context=None,
+              out_dtype=None, workspace=None):
+    """KDA chunked forward on the GPU.
+
+    q, k, g: [B,T,H,K]; v: [B,T,H,V]; beta: [B,T,H]; all float32 or all bfloat16,
+    contiguous, on one HIP device.  initial_state: fp32 [B,H,K,V] ([B,N_max,H,K,V]
+    with segment_ids).  segment_ids: int32 [B,T], 1-based, 0 = padding; needs N_max.
+    out_dtype: dtype of o (default float32: see the precision notes of the
+    library; bfloat16 rounds the result once more).
+    Returns (o, final_state or None).
+    """
+    import torch
+    if A_log is not None or dt_bias is not None or use_gate_in_kernel:
+        raise NotImplementedError("in-kernel gate activation (A_log, dt_bias) is not implemented: pass the "
+                                  "activated log decay as g")
+    if disable_recompute:
+        raise NotImplementedError("disable_recompute concerns the backward pass, which is not implemented")
+    if cp_context is not None:
+        raise NotImplementedError("context parallelism is not implemented (single device)")
+    if lower_bound is not None and not safe_gate:
+        warnings.warn("lower_bound is ignored without safe_gate", stacklevel=2)
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != q.dtype:
+            raise ValueError("q, k, v, g and beta must share one dtype")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:3]) != (B, T, H) or tuple(beta.shape) != (B, T, H):
+        raise ValueError("shape mismatch: q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H]")
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    n_max = 0
+    if segment_ids is not None:
+        if segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != (B, T) or not segment_ids.is_contiguous():
+            raise ValueError("segment_ids must be a contiguous int32 [B, T] tensor")
+        if N_max is None or N_max < 1:
+            raise ValueError("packed input (segment_ids) needs a positive N_max (max segments per row)")
+        n_max = int(N_max)
+    desc = make_desc(B, T, H, K, V, _dtype_code(q.dtype), _dtype_code(out_dtype), scale,
+                     use_qk_l2norm_in_kernel, safe_gate, lower_bound if safe_gate else None, n_max, chunk_size)
+    state_shape = (B, H, K, V) if segment_ids is None else (B, n_max, H, K, V)
+    if initial_state is not None:
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != state_shape \
+                or not initial_state.is_contiguous():
+            raise ValueError(f"initial_state must be a contiguous float32 {state_shape} tensor")
+    ws_bytes = workspace_size(desc, segment_ids is not None)
+    if workspace is None or workspace.numel() < ws_bytes:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    o = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
+    fin = torch.empty(state_shape, dtype=torch.float32, device=q.device) if output_final_state else None
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = load_library().kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(initial_state), _ptr(segment_ids), _ptr(o), _ptr(fin),
+                                      _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                      ctypes.c_void_p(stream))
+    _raise_for(st, "kda_chunk_fwd")
+    return o, fin
+
+
+def read_flags(workspace) -> int:
+    """Synchronise the current stream and read the KDA_FLAG_* word of a workspace."""
+    import torch
+    flags = ctypes.c_uint32(0)
+    stream = torch.cuda.current_stream(workspace.device).cuda_stream
+    _raise_for(load_library().kda_chunk_fwd_flags(_ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                                  ctypes.c_void_p(stream), ctypes.byref(flags)),
+               "kda_chunk_fwd_flags")
+    return int(flags.value)

@@ -1,0 +1,121 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked KDA forward library.
+ *
+ * The operation is the chunked forward of Kimi Delta Attention, the gated
+ * delta rule of the page "feat(kda): integrate KDA attention with tokamax
+ * backend and CP support" (Implementation Details, "Delta Rule
+ * formulation"): per batch row b and head h, token by token,
+ *     S <- diag(exp(g_t)) S                      (decay on the key axis)
+ *     S <- S + beta_t k_t (v_t - k_t^T S)^T      (delta-rule write)
+ *     o_t = scale * q_t^T S                      (read-out after the write)
+ * evaluated in 64-token chunks.  The argument list mirrors the chunk_kda
+ * entry point of that page's Public API section (q, k, v, g, beta, scale,
+ * initial_state, output_final_state, chunk_size, use_qk_l2norm_in_kernel,
+ * safe_gate, lower_bound, segment_ids, N_max).
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is a DEVICE pointer, contiguous, 16-byte aligned.
+ *    The caller owns all memory; the library allocates nothing and keeps no
+ *    state between calls.
+ *  - Layouts are batch-first: q, k, g [B,T,H,K]; v and o [B,T,H,V];
+ *    beta [B,T,H]; segment_ids [B,T] int32; states fp32 [B,H,K,V], or
+ *    [B,N_max,H,K,V] when segment_ids are given (one state per segment, in
+ *    order of appearance within the row).
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  KDA_OK means the arguments were valid and the
+ *    kernels were enqueued.  No exception crosses the ABI.
+ *  - On any other status nothing was enqueued and kda_last_error() returns a
+ *    message for the calling thread.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1,   /* a value or combination the method rejects */
+  KDA_ERR_NOT_IMPLEMENTED = 2,    /* a valid request this library does not cover */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 3,
+  KDA_ERR_HIP = 4                 /* a HIP runtime call failed */
+} kda_status_t;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
+
+/* Flags reported by kda_chunk_fwd_flags(). */
+#define KDA_FLAG_SEGMENT_OVERFLOW 0x1u  /* a row held more than max_segments segments */
+
+typedef struct {
+  int64_t B, T, H;        /* >= 0 each; a zero size makes the call a no-op */
+  int64_t K, V;           /* key / value head dims: 64 or 128 each (else NOT_IMPLEMENTED) */
+  kda_dtype_t dtype;      /* element type of q, k, v, g, beta */
+  kda_dtype_t o_dtype;    /* element type of o (states are always fp32) */
+  float scale;            /* read-out scale; NaN selects 1/sqrt(K); must be finite otherwise */
+  int32_t chunk_size;     /* must be 64 (else NOT_IMPLEMENTED) */
+  int32_t use_qk_l2norm;  /* 0/1: divide q, k by sqrt(sum x^2 + 1e-6) inside the kernel */
+  int32_t safe_gate;      /* 0/1: caller promises lower_bound <= g <= 0 everywhere */
+  float lower_bound;      /* with safe_gate: must lie in [-5, 0) (else INVALID_ARGUMENT);
+                             ignored without safe_gate */
+  int32_t max_segments;   /* N_max: upper bound on segments per row; required >= 1 when
+                             segment_ids are given (else INVALID_ARGUMENT), ignored otherwise */
+} kda_fwd_desc_t;
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for `desc`.  Depends only on
+ * the descriptor (sizes, dtype, max_segments, whether segments are given is
+ * taken from max_segments > 0).  Returns INVALID_ARGUMENT / NOT_IMPLEMENTED
+ * for descriptors kda_chunk_fwd would reject.
+ */
+kda_status_t kda_chunk_fwd_workspace_size(const kda_fwd_desc_t* desc, int has_segment_ids,
+                                          size_t* bytes);
+
+/*
+ * Chunked KDA forward.
+ *   q, k, g       [B,T,H,K] of desc->dtype.  g is the per-key-channel log decay,
+ *                 required to satisfy g <= 0 (and g >= lower_bound under
+ *                 safe_gate); results for g > 0 are unspecified.
+ *   v             [B,T,H,V] of desc->dtype.
+ *   beta          [B,T,H] of desc->dtype.
+ *   initial_state NULL (zero state) or fp32 [B,H,K,V] / [B,N_max,H,K,V].
+ *   segment_ids   NULL (each row is one sequence) or int32 [B,T]: 1-based ids,
+ *                 0 = padding.  A new segment starts at every token whose id
+ *                 is non-zero and differs from the previous token's id.
+ *                 Padding tokens get o = 0 and do not touch any state.
+ *   o             [B,T,H,V] of desc->o_dtype; every element is written.
+ *   final_state   NULL (not requested) or fp32, same shape as initial_state;
+ *                 slots of segments that do not occur are set to zero.
+ *   workspace     device scratch of at least kda_chunk_fwd_workspace_size()
+ *                 bytes; its contents on entry do not matter.
+ * If a row holds more than max_segments segments, the excess segments get
+ * o = 0, their states are not read or written, and KDA_FLAG_SEGMENT_OVERFLOW
+ * is raised in the workspace (read it with kda_chunk_fwd_flags).
+ */
+kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc,
+                           const void* q, const void* k, const void* v,
+                           const void* g, const void* beta,
+                           const float* initial_state, const int32_t* segment_ids,
+                           void* o, float* final_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Waits for `stream`, then reads the KDA_FLAG_* word the last kda_chunk_fwd
+ * call on this workspace left behind (0 when nothing was flagged).
+ */
+kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, void* stream,
+                                 uint32_t* flags);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

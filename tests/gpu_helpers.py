@@ -1,0 +1,76 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, run the
+HIP path through the Python binding, compare with the oracle."""
+import numpy as np
+
+import oracle
+
+TOL_F32 = 1e-4     # max|err| / rms(ref), fp32 inputs
+TOL_BF16 = 2e-2    # max|err| / rms(ref), bf16 inputs
+BF16_HALF_ULP_REL = 2.0 ** -8   # |x - bf16(x)| <= 2^-8 |x| under round-to-nearest-even
+
+
+def to_device(inp: dict, dtype: str, device="cuda"):
+    import torch
+    out = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        if dtype == "bf16":
+            bits = np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)
+            out[name] = torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        else:
+            out[name] = torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).to(device)
+    out["initial_state"] = None if inp["initial_state"] is None else \
+        torch.from_numpy(np.ascontiguousarray(inp["initial_state"], dtype=np.float32)).to(device)
+    out["segment_ids"] = None if inp["segment_ids"] is None else \
+        torch.from_numpy(np.ascontiguousarray(inp["segment_ids"], dtype=np.int32)).to(device)
+    return out
+
+
+def run_gpu(inp: dict, w, out_dtype=None, **over):
+    """Run chunk_kda on the device copy of ``inp``; returns numpy (o, final)."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    d = to_device(inp, w.dtype)
+    kw = dict(scale=inp["scale"], initial_state=d["initial_state"], output_final_state=w.final_state,
+              use_qk_l2norm_in_kernel=w.l2norm_in_kernel, safe_gate=w.safe_gate, lower_bound=w.lower_bound,
+              segment_ids=d["segment_ids"], N_max=inp["max_segments"] if d["segment_ids"] is not None else None,
+              out_dtype=out_dtype)
+    kw.update(over)
+    o, fin = kda.chunk_kda(d["q"], d["k"], d["v"], d["g"], d["beta"], **kw)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    fin = None if fin is None else fin.cpu().numpy().astype(np.float64)
+    return o, fin
+
+
+def check(name, got, ref, tol, bf16_out=False):
+    """Assert max|got - ref| / rms(ref) <= tol; with a bf16 output the final
+    rounding (at most 2^-8 |ref| per element) is added to the allowance."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values"
+    if ref.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    err = np.abs(got - ref)
+    if bf16_out:
+        err = np.maximum(err - BF16_HALF_ULP_REL * (np.abs(ref) + tol * rms), 0.0)
+    rel = float(err.max()) / rms if rms > 0 else float(err.max())
+    assert rel <= tol, f"{name}: max|err|/rms(ref) = {rel:.3e} > {tol:.1e}"
+    return rel
+
+
+def subset_heads(inp: dict, heads):
+    """Inputs restricted to some heads (heads are independent recurrences)."""
+    sub = dict(inp)
+    for n in ("q", "k", "v", "g", "beta"):
+        sub[n] = np.ascontiguousarray(inp[n][:, :, heads])
+    if inp["initial_state"] is not None:
+        ax = 1 if inp["segment_ids"] is None else 2
+        sub["initial_state"] = np.ascontiguousarray(np.take(inp["initial_state"], heads, axis=ax))
+    return sub
+
+
+def oracle_ref(inp: dict, w, heads=None):
+    src = inp if heads is None else subset_heads(inp, heads)
+    return oracle.forward_inputs(src, w, precision="f64")

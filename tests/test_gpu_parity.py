@@ -1,0 +1,280 @@
+"""Parity of the HIP path with the CPU oracle (GPU tests, called through the C ABI).
+
+Bar: max|err| / rms(ref) <= 1e-4 for fp32 inputs and <= 2e-2 for bf16 inputs,
+per output tensor, against the fp64 oracle on the same seeded inputs.
+Workloads follow the forward tests described on the page "feat(kda):
+integrate KDA attention with tokamax backend and CP support" (Test Coverage:
+kernel precision vs the naive recurrence at FP32 and BF16, padding, packed
+sequences, segment_ids fallback, row independence, determinism) and the
+multi-head / multi-row packed cases of the tokamax packed forward page.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from gated_delta_rule_33_amd.inputs import WORKLOADS, Workload, make_inputs, segment_ids_from_lengths
+from tests.gpu_helpers import TOL_BF16, TOL_F32, check, oracle_ref, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _tol(w):
+    return TOL_F32 if w.dtype == "f32" else TOL_BF16
+
+
+@pytest.mark.parametrize("name", ["fp32_b1_h2_t256_k64", "bf16_b1_h8_t1024_fixed", "bf16_b1_h8_t1024_packed4"])
+def test_small_workloads_full_parity(name):
+    w = WORKLOADS[name]
+    _say(f"[parity] {name}")
+    inp = make_inputs(w)
+    o, fin = run_gpu(inp, w)
+    o_ref, fin_ref = oracle_ref(inp, w)
+    e = check(f"{name} o", o, o_ref, _tol(w))
+    _say(f"[parity] {name} o rel err {e:.3e}")
+    if w.final_state:
+        e = check(f"{name} final", fin, fin_ref, _tol(w))
+        _say(f"[parity] {name} final rel err {e:.3e}")
+
+
+@pytest.mark.parametrize("name", ["bf16_b1_h32_t8192_fixed_state", "bf16_b1_h32_t8192_packed25_l2"])
+def test_full_size_workloads_sampled_heads(name):
+    """Full-size launch (the benchmark's configuration); the oracle checks three
+    heads end to end (heads are independent recurrences)."""
+    w = WORKLOADS[name]
+    _say(f"[parity] {name} full size")
+    inp = make_inputs(w)
+    o, fin = run_gpu(inp, w)
+    assert np.all(np.isfinite(o))
+    heads = [0, 13, 31]
+    o_ref, fin_ref = oracle_ref(inp, w, heads)
+    e = check(f"{name} o", o[:, :, heads], o_ref, TOL_BF16)
+    _say(f"[parity] {name} o rel err (heads {heads}) {e:.3e}")
+    if w.final_state:
+        ax = 1 if inp["segment_ids"] is None else 2
+        e = check(f"{name} final", np.take(fin, heads, axis=ax), fin_ref, TOL_BF16)
+        _say(f"[parity] {name} final rel err {e:.3e}")
+
+
+def _custom(name, dtype, B, T, H, K, V, seg_rows=None, seed=11, **kw):
+    w = Workload(name, dtype, B, T, H, K, V, seed=seed, **kw)
+    seg = None if seg_rows is None else segment_ids_from_lengths(seg_rows, T)
+    return w, make_inputs(w, segment_ids=seg)
+
+
+CASES = {
+    # ragged tails, several tiles
+    "ragged_t200": dict(dtype="bf16", B=2, T=200, H=3, K=128, V=128, final_state=True),
+    "tiny_t1": dict(dtype="bf16", B=1, T=1, H=2, K=128, V=128, final_state=True),
+    "short_t37_k64": dict(dtype="bf16", B=1, T=37, H=2, K=64, V=64, final_state=True),
+    "mixed_k64_v128": dict(dtype="bf16", B=1, T=300, H=2, K=64, V=128, final_state=True),
+    "mixed_k128_v64": dict(dtype="bf16", B=1, T=300, H=2, K=128, V=64, final_state=True),
+    "fp32_k128_ragged": dict(dtype="f32", B=1, T=150, H=2, K=128, V=128, final_state=True),
+    "fp32_state_in": dict(dtype="f32", B=2, T=130, H=2, K=64, V=64, initial_state=True, final_state=True),
+    "bf16_state_safe": dict(dtype="bf16", B=2, T=333, H=2, K=128, V=128, initial_state=True, final_state=True,
+                            gate="neg5_sigmoid", safe_gate=True, lower_bound=-5.0),
+    "bf16_l2_in_kernel": dict(dtype="bf16", B=1, T=256, H=2, K=128, V=128, l2norm_in_kernel=True, final_state=True),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_edge_shapes(case):
+    kw = dict(CASES[case])
+    w, inp = _custom(case, **kw)
+    _say(f"[parity] {case}")
+    o, fin = run_gpu(inp, w)
+    o_ref, fin_ref = oracle_ref(inp, w)
+    check(f"{case} o", o, o_ref, _tol(w))
+    if w.final_state:
+        check(f"{case} final", fin, fin_ref, _tol(w))
+
+
+PACKED = {
+    # two rows with different maps, padding between and after, length-1 segments
+    "two_rows_padding": ([[5, 70, 1, 0], [130, 64, 2]], 210),
+    "aligned_64": ([[64, 64, 128]], 256),
+    "many_short": ([[1] * 20 + [3] * 10 + [65]], 150),
+}
+
+
+@pytest.mark.parametrize("case", list(PACKED))
+@pytest.mark.parametrize("with_state", [False, True])
+def test_packed_segments(case, with_state):
+    rows, T = PACKED[case]
+    rows = [[n for n in r if n > 0] for r in rows]
+    seg = segment_ids_from_lengths(rows, T)
+    if case == "two_rows_padding":
+        seg[0, 30:34] = 0          # padding inside row 0 splits its second segment in two
+    B = len(rows)
+    n_max = max(len(r) for r in rows) + 2   # spare slots: their final states must be zero
+    w = Workload(case, "bf16", B, T, 2, 128, 128, seed=21, initial_state=with_state, final_state=True,
+                 max_segments=n_max)
+    inp = make_inputs(w, segment_ids=seg)
+    _say(f"[parity] packed {case} state={with_state}")
+    o, fin = run_gpu(inp, w)
+    o_ref, fin_ref = oracle_ref(inp, w)
+    check(f"{case} o", o, o_ref, TOL_BF16)
+    check(f"{case} final", fin, fin_ref, TOL_BF16)
+    assert np.all(o[seg == 0] == 0.0)
+
+
+def test_segment_ids_all_ones_equals_fixed():
+    w = Workload("ones", "bf16", 2, 190, 2, 128, 128, seed=31, final_state=True, max_segments=1)
+    inp = make_inputs(w)
+    o1, f1 = run_gpu(inp, w)
+    inp2 = dict(inp)
+    inp2["segment_ids"] = np.ones((2, 190), dtype=np.int32)
+    inp2["max_segments"] = 1
+    o2, f2 = run_gpu(inp2, w)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(f1, f2[:, 0])
+
+
+def test_segment_overflow_is_flagged_and_zeroed():
+    import torch
+    from gated_delta_rule_33_amd import kda
+    T = 100
+    seg = segment_ids_from_lengths([[30, 30, 40]], T)
+    w = Workload("overflow", "bf16", 1, T, 2, 128, 128, seed=41, max_segments=2)
+    inp = make_inputs(w, segment_ids=seg)
+    d = to_device(inp, "bf16")
+    ws = torch.empty(kda.workspace_size(kda.make_desc(1, T, 2, 128, 128, kda.KDA_BF16, kda.KDA_F32,
+                                                      max_segments=2), True), dtype=torch.uint8, device="cuda")
+    o, _ = kda.chunk_kda(d["q"], d["k"], d["v"], d["g"], d["beta"], segment_ids=d["segment_ids"], N_max=2,
+                         workspace=ws)
+    assert kda.read_flags(ws) & kda.KDA_FLAG_SEGMENT_OVERFLOW
+    o = o.cpu().numpy()
+    assert np.all(o[0, 60:] == 0.0)
+    # the recorded segments are still right
+    o_ref, _ = oracle.kda_forward(inp["q"][:, :60], inp["k"][:, :60], inp["v"][:, :60], inp["g"][:, :60],
+                                  inp["beta"][:, :60], scale=inp["scale"], segment_ids=seg[:, :60],
+                                  max_segments=2)
+    check("overflow o", o[:, :60], o_ref, TOL_BF16)
+    # and a call within the bound leaves the flag clear
+    kda.chunk_kda(d["q"][:, :60].contiguous(), d["k"][:, :60].contiguous(), d["v"][:, :60].contiguous(),
+                  d["g"][:, :60].contiguous(), d["beta"][:, :60].contiguous(),
+                  segment_ids=d["segment_ids"][:, :60].contiguous(), N_max=2, workspace=ws)
+    assert kda.read_flags(ws) == 0
+
+
+def test_zero_gate_orthonormal_keys_on_gpu():
+    """g = 0, beta = 1, orthonormal keys: causal linear attention (closed form)."""
+    T, H, K, V = 96, 1, 128, 128
+    rng = np.random.default_rng(51)
+    Qm, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    k = np.zeros((1, T, H, K), dtype=np.float32)
+    k[0, :, 0] = Qm[:T]
+    q = rng.standard_normal((1, T, H, K)).astype(np.float32)
+    v = rng.standard_normal((1, T, H, V)).astype(np.float32)
+    inp = dict(q=q, k=k, v=v, g=np.zeros_like(q), beta=np.ones((1, T, H), np.float32), initial_state=None,
+               segment_ids=None, scale=0.125, max_segments=0)
+    w = Workload("zero_gate", "f32", 1, T, H, K, V, final_state=True)
+    o, fin = run_gpu(inp, w)
+    qk = q[0, :, 0].astype(np.float64) @ k[0, :, 0].astype(np.float64).T
+    want = 0.125 * np.tril(qk) @ v[0, :, 0].astype(np.float64)
+    check("zero gate o", o[0, :, 0], want, TOL_F32)
+    check("zero gate final", fin[0, 0], k[0, :, 0].astype(np.float64).T @ v[0, :, 0], TOL_F32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_negative_gate_decays_on_gpu(dtype):
+    """g = -1e4: the state restarts every token; exercises the pair-by-pair
+    diagonal blocks.  o_t = scale beta_t (q_t.k_t) v_t."""
+    w = Workload("neg_gate", dtype, 1, 150, 2, 128, 128, seed=61, initial_state=True, final_state=True)
+    inp = make_inputs(w)
+    g = np.full_like(inp["g"], -1e4)
+    inp["g"] = g
+    if dtype == "bf16":
+        from gated_delta_rule_33_amd.inputs import f32_to_bf16_bits, bf16_bits_to_f32
+        inp["g_bits"] = f32_to_bf16_bits(g)
+        inp["g"] = bf16_bits_to_f32(inp["g_bits"])
+    o, fin = run_gpu(inp, w)
+    o_ref, fin_ref = oracle_ref(inp, w)
+    check("neg gate o", o, o_ref, _tol(w))
+    check("neg gate final", fin, fin_ref, _tol(w))
+
+
+def test_bf16_output():
+    w = WORKLOADS["bf16_b1_h8_t1024_packed4"]
+    inp = make_inputs(w)
+    import torch
+    o, _ = run_gpu(inp, w, out_dtype=torch.bfloat16)
+    o_ref, _ = oracle_ref(inp, w)
+    check("bf16 out", o, o_ref, TOL_BF16, bf16_out=True)
+
+
+def test_deterministic_bitwise():
+    w = WORKLOADS["bf16_b1_h8_t1024_packed4"]
+    inp = make_inputs(w)
+    o1, _ = run_gpu(inp, w)
+    o2, _ = run_gpu(inp, w)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_state_passing_matches_single_run():
+    """run(T) == run(T1) -> final -> run(T - T1, initial = final); bitwise when
+    T1 is a multiple of 64 (the same chunks are formed)."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    w = Workload("pass", "bf16", 1, 320, 2, 128, 128, seed=71, initial_state=True, final_state=True)
+    inp = make_inputs(w)
+    d = to_device(inp, "bf16")
+    o, fin = kda.chunk_kda(d["q"], d["k"], d["v"], d["g"], d["beta"], initial_state=d["initial_state"],
+                           output_final_state=True)
+    for T1 in (128, 100):
+        sl = lambda t, a, b: t[:, a:b].contiguous()
+        oa, fa = kda.chunk_kda(*(sl(d[n], 0, T1) for n in ("q", "k", "v", "g", "beta")),
+                               initial_state=d["initial_state"], output_final_state=True)
+        ob, fb = kda.chunk_kda(*(sl(d[n], T1, 320) for n in ("q", "k", "v", "g", "beta")),
+                               initial_state=fa, output_final_state=True)
+        oc = torch.cat([oa, ob], dim=1)
+        if T1 % 64 == 0:
+            assert torch.equal(oc, o) and torch.equal(fb, fin)
+        else:
+            check("state passing o", oc.cpu().numpy(), o.cpu().numpy(), TOL_BF16)
+            check("state passing final", fb.cpu().numpy(), fin.cpu().numpy(), TOL_BF16)
+
+
+def test_poisoned_output_and_workspace_are_overwritten():
+    """Every element of o is written (NaN-filled buffers come back finite), and
+    stale workspace contents do not leak into the result."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    w = WORKLOADS["bf16_b1_h8_t1024_packed4"]
+    inp = make_inputs(w)
+    seg = inp["segment_ids"].copy()
+    seg[0, 500:520] = 0
+    inp["segment_ids"] = seg
+    d = to_device(inp, "bf16")
+    desc = kda.make_desc(1, 1024, 8, 128, 128, kda.KDA_BF16, kda.KDA_F32, max_segments=4)
+    ws = torch.full((kda.workspace_size(desc, True),), 255, dtype=torch.uint8, device="cuda")
+    o = torch.full((1, 1024, 8, 128), float("nan"), device="cuda")
+    import ctypes
+    lib = kda.load_library()
+    st = lib.kda_chunk_fwd(ctypes.byref(desc), *(ctypes.c_void_p(d[n].data_ptr()) for n in ("q", "k", "v", "g", "beta")),
+                           None, ctypes.c_void_p(d["segment_ids"].data_ptr()), ctypes.c_void_p(o.data_ptr()), None,
+                           ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    torch.cuda.synchronize()
+    on = o.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(on))
+    o_ref, _ = oracle.forward_inputs(inp, w)
+    check("poisoned o", on, o_ref, TOL_BF16)
+    assert np.all(on[0, 500:520] == 0.0)
+
+
+def test_empty_inputs():
+    import torch
+    from gated_delta_rule_33_amd import kda
+    z = torch.zeros((1, 0, 2, 128), dtype=torch.bfloat16, device="cuda")
+    o, fin = kda.chunk_kda(z, z, z, z, torch.zeros((1, 0, 2), dtype=torch.bfloat16, device="cuda"),
+                           output_final_state=True)
+    torch.cuda.synchronize()
+    assert o.shape == (1, 0, 2, 128) and torch.all(fin == 0)
