@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunked forward on one MI355X.
+
+One step = one full forward (every kernel of the path) over the workload's
+synthetic, seeded inputs, already resident in HBM.  Default workload:
+B=1, H=32, T=8192, K=V=128, bf16 inputs, fixed length, fp32 initial state in
+and final state out, g in the safe-gate range [-5, 0) (the representative
+training shape the tokamax packed forward page benchmarks).  The packed N=25
+workload (in-kernel q/k L2 norm) is timed the same way and reported under
+"extra".
+
+Timing follows the pages' method (compile first, then synchronized timed
+iterations, median reported): W untimed warm-up steps, then K timed steps
+between two device synchronizations, with a HIP event on the launch stream
+around every step and around every kernel of every step (through the
+library's launch observer).  Prints ONE JSON line on stdout.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_delta_rule_33_amd.inputs import WORKLOADS, make_inputs, to_device  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak, vendor figure
+METRIC = "KDA fwd ms & tokens/s, B=1 H=32 T=8192 K=V=128 bf16; % MFMA/HBM roofline"
+TPU_V7X_FIXED_MS = 1.870        # pages' fastest H=32/T=8192 fixed forward (context, another machine)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, out_bytes: int):
+    """Algorithmic HBM bytes and matrix flops per kernel launch.
+
+    Bytes: every input read once, every output written once.  Flops (2 per
+    multiply-add, triangles at their true size) per 64-token chunk and head:
+    A 258k + Aqk 266k + solve 44k + W 266k + U 266k MAC in the intra-chunk
+    kernel; Delta 1049k + Qg S 1049k + Aqk Delta 266k + state update 1049k
+    MAC in the recurrence (for K = V = 128)."""
+    es = 2 if w.dtype == "bf16" else 4
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
+    tok = B * T * H
+    n_states = B * H if w.segment_lengths is None else B * w.max_segments * H
+    state_b = n_states * K * V * 4
+    chunks = B * H * (-(-T // 64) if w.segment_lengths is None else sum(-(-n // 64) for n in w.segment_lengths))
+    intra_bytes = tok * (3 * K + V + 1) * es
+    recur_bytes = tok * V * out_bytes + (state_b if w.initial_state else 0) + (state_b if w.final_state else 0)
+    prep_bytes = B * T * 4 if w.segment_lengths is not None else 0
+    scale = (K / 128) * (V / 128)
+    return {
+        "kda_prep": dict(bytes=prep_bytes, flops=0.0),
+        "kda_intra": dict(bytes=intra_bytes, flops=2.0 * chunks * 1.10e6 * scale),
+        "kda_recur": dict(bytes=recur_bytes, flops=2.0 * chunks * 3.413e6 * scale),
+    }
+
+
+def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32"):
+    import torch
+    from gated_delta_rule_33_amd import kda
+
+    inp = make_inputs(w)
+    d = to_device(inp, w.dtype)
+    out_dtype = torch.float32 if out_dtype_name == "f32" else torch.bfloat16
+    call = kda.prepare_call(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=inp["scale"],
+                            initial_state=d["initial_state"], output_final_state=w.final_state,
+                            use_qk_l2norm_in_kernel=w.l2norm_in_kernel, safe_gate=w.safe_gate,
+                            lower_bound=w.lower_bound, segment_ids=d["segment_ids"],
+                            N_max=inp["max_segments"] if d["segment_ids"] is not None else None,
+                            out_dtype=out_dtype)
+    for _ in range(warmup):
+        call.enqueue()
+    torch.cuda.synchronize()
+
+    # Kernel events through the launch observer, step events around each call.
+    pending = {}
+    kernel_events = {}
+
+    def observer(name, stream, phase):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record()
+        if phase == 0:
+            pending[name] = ev
+        else:
+            kernel_events.setdefault(name, []).append((pending.pop(name), ev))
+
+    cb = kda.set_launch_observer(observer)
+    step_events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_events[0].record()
+    for i in range(steps):
+        call.enqueue()
+        step_events[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kda.set_launch_observer(None)
+    del cb
+    step_ms = [step_events[i].elapsed_time(step_events[i + 1]) for i in range(steps)]
+    total_ms = step_events[0].elapsed_time(step_events[-1])
+    kern_ms = {n: [a.elapsed_time(b) for a, b in evs] for n, evs in kernel_events.items()}
+    return dict(inp=inp, call=call, step_ms=step_ms, total_ms=total_ms, wall_s=wall, kernel_ms=kern_ms)
+
+
+def summarize(w, res, out_bytes):
+    steps = len(res["step_ms"])
+    ms = res["total_ms"] / steps
+    alg = algorithmic(w, out_bytes)
+    kern = {}
+    for name, vals in res["kernel_ms"].items():
+        avg = sum(vals) / len(vals)
+        a = alg.get(name, dict(bytes=0, flops=0.0))
+        kern[name] = dict(avg_us=round(avg * 1e3, 2), alg_bytes=a["bytes"], alg_flops=a["flops"],
+                          achieved_gbps=round(a["bytes"] / (avg * 1e-3) / 1e9, 1) if avg > 0 else None,
+                          achieved_tflops=round(a["flops"] / (avg * 1e-3) / 1e12, 2) if avg > 0 else None)
+    dom = max(kern, key=lambda n: kern[n]["avg_us"])
+    path_bytes = sum(a["bytes"] for a in alg.values())
+    path_flops = sum(a["flops"] for a in alg.values())
+    return dict(ms=ms, median_ms=statistics.median(res["step_ms"]), min_ms=min(res["step_ms"]),
+                max_ms=max(res["step_ms"]), tokens_per_s=w.B * w.T / (ms * 1e-3), kernels=kern, dominant=dom,
+                path_gbps=path_bytes / (ms * 1e-3) / 1e9, path_tflops=path_flops / (ms * 1e-3) / 1e12,
+                path_bytes=path_bytes, path_flops=path_flops)
+
+
+def cpu_baseline(w, inp, gpu_out):
+    """The oracle (fp64 build, as it stands) on the host cores, on the whole
+    workload; also the parity of the benchmarked GPU output against it."""
+    import oracle
+    threads = min(oracle.default_threads(), w.B * w.H)
+    t0 = time.perf_counter()
+    o_ref, fin_ref = oracle.forward_inputs(inp, w, precision="f64", num_threads=threads)
+    dt = time.perf_counter() - t0
+    o_gpu, fin_gpu = gpu_out
+    parity = {"o_rel_err": oracle.rel_err(o_gpu, o_ref)}
+    if fin_ref is not None:
+        parity["final_rel_err"] = oracle.rel_err(fin_gpu, fin_ref)
+    cpu = {"value": round(w.B * w.T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"whole workload {w.name} (B*T*H = {w.B * w.T * w.H} head-tokens), fp64 token loop, "
+                     f"{dt:.2f} s on {threads} threads ({os.cpu_count()} CPUs visible)"}
+    return cpu, parity
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bf16_b1_h32_t8192_fixed_state", choices=sorted(WORKLOADS))
+    ap.add_argument("--extra", default="bf16_b1_h32_t8192_packed25_l2",
+                    help="second workload timed and reported under 'extra' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU (the path shards over heads and rows with no "
+              "communication; no multi-GPU figure is produced). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
+    res = time_workload(w, args.steps, args.warmup)
+    s = summarize(w, res, out_bytes=4)
+    log(f"[bench] {w.name}: {s['ms'] * 1e3:.1f} us/step, kernels {s['kernels']}")
+
+    o = res["call"].tensors["o"].float().cpu().numpy()
+    fin = res["call"].tensors["final_state"]
+    fin = None if fin is None else fin.cpu().numpy()
+    cpu, parity = (None, None)
+    if not args.no_cpu_baseline:
+        log("[bench] oracle on the host")
+        cpu, parity = cpu_baseline(w, res["inp"], (o, fin))
+        log(f"[bench] cpu baseline {cpu}, parity {parity}")
+
+    dom = s["kernels"][s["dominant"]]
+    roofline = {"bound": "hbm", "kernel": s["dominant"], "achieved": dom["achieved_gbps"], "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dom["achieved_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                "mfma_tflops": dom["achieved_tflops"],
+                "mfma_frac": round(dom["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+    extra = {"path": {"alg_bytes": s["path_bytes"], "alg_flops": s["path_flops"],
+                      "gbps": round(s["path_gbps"], 1), "hbm_frac": round(s["path_gbps"] / HBM_PEAK_GBPS, 4),
+                      "tflops": round(s["path_tflops"], 2)},
+             "step_ms": {"median": round(s["median_ms"], 4), "min": round(s["min_ms"], 4),
+                         "max": round(s["max_ms"], 4)},
+             "kernels": s["kernels"], "parity_vs_oracle": parity,
+             "tpu_v7x_context_ms": TPU_V7X_FIXED_MS}
+    if args.extra:
+        w2 = WORKLOADS[args.extra]
+        log(f"[bench] {w2.name}")
+        res2 = time_workload(w2, args.steps, args.warmup)
+        s2 = summarize(w2, res2, out_bytes=4)
+        extra[w2.name] = {"ms_per_step": round(s2["ms"], 4), "tokens_per_s": round(s2["tokens_per_s"], 1),
+                          "median_ms": round(s2["median_ms"], 4), "kernels": s2["kernels"],
+                          "path_hbm_frac": round(s2["path_gbps"] / HBM_PEAK_GBPS, 4)}
+        del res2
+    line = {
+        "metric": METRIC, "value": round(s["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(s["ms"], 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": round(s["tokens_per_s"] / (w.B * w.T / (TPU_V7X_FIXED_MS * 1e-3)), 3),
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "K": w.K, "V": w.V,
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "none (1 GPU)",
+                   "inputs": "bf16 q,k,v,g,beta; fp32 initial/final state; fp32 o", "chunk": 64},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

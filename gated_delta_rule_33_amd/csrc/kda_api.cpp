@@ -21,6 +21,17 @@
 namespace {
 
 thread_local std::string g_last_error;
+kda_launch_observer_t g_observer = nullptr;
+void* g_observer_user = nullptr;
+
+// Enqueue one kernel, with the observer (if any) called around it.
+template <class F>
+hipError_t observed(const char* name, hipStream_t s, F&& launch) {
+  if (g_observer) g_observer(name, s, 0, g_observer_user);
+  const hipError_t e = launch();
+  if (g_observer) g_observer(name, s, 1, g_observer_user);
+  return e;
+}
 
 kda_status_t fail(kda_status_t st, const std::string& msg) {
   g_last_error = msg;
@@ -147,16 +158,17 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void
 
   if (d.B == 0 || d.H == 0) return KDA_OK;
   hipError_t e = hipSuccess;
+  const hipStream_t s = a.stream;
   if (has_seg) {
     if (d.T == 0) return KDA_OK;
-    e = kda::launch_prep(a);
+    e = observed("kda_prep", s, [&] { return kda::launch_prep(a); });
   } else if (d.T == 0) {
-    e = kda::launch_zero_states(a);
+    e = observed("kda_zero_states", s, [&] { return kda::launch_zero_states(a); });
     if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
     return KDA_OK;
   }
-  if (e == hipSuccess) e = kda::launch_intra(a);
-  if (e == hipSuccess) e = kda::launch_recur(a);
+  if (e == hipSuccess) e = observed("kda_intra", s, [&] { return kda::launch_intra(a); });
+  if (e == hipSuccess) e = observed("kda_recur", s, [&] { return kda::launch_recur(a); });
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return KDA_OK;
 }
@@ -172,6 +184,11 @@ kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, 
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("flags: ") + hipGetErrorString(e));
   *flags = hdr.flags;
   return KDA_OK;
+}
+
+void kda_set_launch_observer(kda_launch_observer_t fn, void* user) {
+  g_observer = fn;
+  g_observer_user = user;
 }
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }

@@ -36,6 +36,7 @@ __all__ = [
     "bf16_bits_to_f32",
     "segment_ids_from_lengths",
     "balanced_lengths",
+    "to_device",
 ]
 
 
@@ -187,4 +188,22 @@ def make_inputs(w: Workload, segment_ids: Optional[np.ndarray] = None) -> dict:
             out[name] = np.ascontiguousarray(arr, dtype=np.float32)
         else:
             raise ValueError(f"unknown dtype {w.dtype!r}")
+    return out
+
+
+def to_device(inp: dict, dtype: str, device="cuda") -> dict:
+    """Upload the arrays of ``make_inputs`` as torch tensors (bf16 from the
+    exact bit patterns, fp32 as is); states fp32, segment ids int32."""
+    import torch
+    out = {}
+    for name in ("q", "k", "v", "g", "beta"):
+        if dtype == "bf16":
+            bits = np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)
+            out[name] = torch.from_numpy(bits).to(device).view(torch.bfloat16)
+        else:
+            out[name] = torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).to(device)
+    out["initial_state"] = None if inp["initial_state"] is None else \
+        torch.from_numpy(np.ascontiguousarray(inp["initial_state"], dtype=np.float32)).to(device)
+    out["segment_ids"] = None if inp["segment_ids"] is None else \
+        torch.from_numpy(np.ascontiguousarray(inp["segment_ids"], dtype=np.int32)).to(device)
     return out

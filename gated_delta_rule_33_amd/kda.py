@@ -10,7 +10,6 @@ GPU, every call raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 import warnings
 from typing import Optional
@@ -22,8 +21,11 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 
-EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_flags", "kda_last_error",
-            "kda_version")
+EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer",
+            "kda_last_error", "kda_version")
+
+# void (*)(const char* kernel_name, void* stream, int phase, void* user)
+LAUNCH_OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p)
 
 
 class KdaFwdDesc(ctypes.Structure):
@@ -58,6 +60,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_flags.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_uint32)]
     lib.kda_chunk_fwd_flags.restype = ctypes.c_int
+    lib.kda_set_launch_observer.argtypes = [LAUNCH_OBSERVER, ctypes.c_void_p]
+    lib.kda_set_launch_observer.restype = None
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.restype = ctypes.c_char_p
     _lib = lib
@@ -167,6 +171,55 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
                                       ctypes.c_void_p(stream))
     _raise_for(st, "kda_chunk_fwd")
     return o, fin
+
+
+def set_launch_observer(fn):
+    """Install fn(kernel_name: str, stream: int, phase: int) around every kernel
+    launch (None removes it).  Returns the ctypes callback, which the caller
+    must keep alive while it is installed."""
+    lib = load_library()
+    if fn is None:
+        lib.kda_set_launch_observer(LAUNCH_OBSERVER(), None)
+        return None
+    cb = LAUNCH_OBSERVER(lambda name, stream, phase, user: fn(name.decode(), stream, phase))
+    lib.kda_set_launch_observer(cb, None)
+    return cb
+
+
+class PreparedCall:
+    """kda_chunk_fwd with every argument marshalled once: ``enqueue()`` only
+    crosses the C ABI (for timing loops).  Holds references to its tensors."""
+
+    def __init__(self, desc: KdaFwdDesc, tensors: dict, workspace, stream: int):
+        self.desc, self.tensors, self.workspace = desc, tensors, workspace
+        names = ("q", "k", "v", "g", "beta", "initial_state", "segment_ids", "o", "final_state")
+        self.args = [ctypes.byref(desc)] + [_ptr(tensors.get(n)) for n in names] + \
+            [_ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)]
+        self.fn = load_library().kda_chunk_fwd
+
+    def enqueue(self):
+        _raise_for(self.fn(*self.args), "kda_chunk_fwd")
+
+
+def prepare_call(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
+                 use_qk_l2norm_in_kernel=False, safe_gate=False, lower_bound=None, segment_ids=None,
+                 N_max=None, out_dtype=None) -> PreparedCall:
+    """Allocate o, final state and workspace for one shape and return a
+    PreparedCall that enqueues the forward on the current stream."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    n_max = int(N_max) if segment_ids is not None else 0
+    desc = make_desc(B, T, H, K, V, _dtype_code(q.dtype), _dtype_code(out_dtype), scale, use_qk_l2norm_in_kernel,
+                     safe_gate, lower_bound if safe_gate else None, n_max)
+    ws = torch.empty(max(workspace_size(desc, segment_ids is not None), 1), dtype=torch.uint8, device=q.device)
+    state_shape = (B, H, K, V) if segment_ids is None else (B, n_max, H, K, V)
+    t = dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state, segment_ids=segment_ids,
+             o=torch.empty((B, T, H, V), dtype=out_dtype, device=q.device),
+             final_state=torch.empty(state_shape, dtype=torch.float32, device=q.device) if output_final_state
+             else None)
+    return PreparedCall(desc, t, ws, torch.cuda.current_stream(q.device).cuda_stream)
 
 
 def read_flags(workspace) -> int:

@@ -16,7 +16,7 @@
  * Conventions shared by every entry point:
  *  - Every tensor pointer is a DEVICE pointer, contiguous, 16-byte aligned.
  *    The caller owns all memory; the library allocates nothing and keeps no
- *    state between calls.
+ *    state between calls (the optional launch observer aside).
  *  - Layouts are batch-first: q, k, g [B,T,H,K]; v and o [B,T,H,V];
  *    beta [B,T,H]; segment_ids [B,T] int32; states fp32 [B,H,K,V], or
  *    [B,N_max,H,K,V] when segment_ids are given (one state per segment, in
@@ -108,6 +108,16 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc,
  */
 kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, void* stream,
                                  uint32_t* flags);
+
+/*
+ * Launch observer, for measurement tools: when set, kda_chunk_fwd calls
+ * fn(kernel_name, stream, phase, user) on the calling thread right before
+ * (phase 0) and right after (phase 1) it enqueues each kernel, so a caller
+ * can record timing events on `stream` around every kernel.  NULL removes
+ * it.  Process-wide; set it while no other thread is inside kda_chunk_fwd.
+ */
+typedef void (*kda_launch_observer_t)(const char* kernel_name, void* stream, int phase, void* user);
+void kda_set_launch_observer(kda_launch_observer_t fn, void* user);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* kda_last_error(void);

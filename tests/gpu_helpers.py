@@ -3,26 +3,11 @@ HIP path through the Python binding, compare with the oracle."""
 import numpy as np
 
 import oracle
+from gated_delta_rule_33_amd.inputs import to_device  # noqa: F401 (re-exported for tests)
 
 TOL_F32 = 1e-4     # max|err| / rms(ref), fp32 inputs
 TOL_BF16 = 2e-2    # max|err| / rms(ref), bf16 inputs
 BF16_HALF_ULP_REL = 2.0 ** -8   # |x - bf16(x)| <= 2^-8 |x| under round-to-nearest-even
-
-
-def to_device(inp: dict, dtype: str, device="cuda"):
-    import torch
-    out = {}
-    for name in ("q", "k", "v", "g", "beta"):
-        if dtype == "bf16":
-            bits = np.ascontiguousarray(inp[name + "_bits"]).view(np.int16)
-            out[name] = torch.from_numpy(bits).to(device).view(torch.bfloat16)
-        else:
-            out[name] = torch.from_numpy(np.ascontiguousarray(inp[name], dtype=np.float32)).to(device)
-    out["initial_state"] = None if inp["initial_state"] is None else \
-        torch.from_numpy(np.ascontiguousarray(inp["initial_state"], dtype=np.float32)).to(device)
-    out["segment_ids"] = None if inp["segment_ids"] is None else \
-        torch.from_numpy(np.ascontiguousarray(inp["segment_ids"], dtype=np.int32)).to(device)
-    return out
 
 
 def run_gpu(inp: dict, w, out_dtype=None, **over):
