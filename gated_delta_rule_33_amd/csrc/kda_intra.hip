@@ -31,37 +31,39 @@ namespace {
 
 constexpr float kSpanMax = 64.f;
 
+// LDS of one workgroup.  q and v are not staged whole: q is read in operand
+// layout straight from global memory, v is written into the k region once k
+// is no longer needed.  About 72 KB for bf16 K = V = 128, so two workgroups
+// share a CU and one's loads overlap the other's arithmetic.
 template <class TI, int K, int V>
 struct IntraSmem {
-  static constexpr int kQP = K + 8;   // row pitch (elements) of q, k
-  static constexpr int kVP = V + 8;   // row pitch of v
-  static constexpr int kGP = K + 4;   // row pitch (floats) of G / exp(G)
-  static constexpr int kMP = 68;      // row pitch of M (T below the diagonal, A^T above)
-  TI q[kChunk * kQP];
-  TI k[kChunk * kQP];
-  TI v[kChunk * kVP];
+  static constexpr int kKP = (K > V ? K : V) + 8;   // row pitch (elements) of k, later v
+  static constexpr int kGP = K + 4;                 // row pitch (floats) of G, later exp(G)
+  static constexpr int kMP = 68;                    // row pitch of M (T below the diagonal, A^T above)
+  TI kv[kChunk * kKP];
   float G[kChunk * kGP];
   float M[kChunk * kMP];
   float beta[kChunk];
-  float nq[kChunk], nk[kChunk];
-  float part[512];
-  int span_bits[4];
+  float nk[kChunk];
+  float part[kThreads];
 };
 
-__device__ __forceinline__ float ldf(const float* p, int i) { return p[i]; }
-__device__ __forceinline__ float ldf(const uint16_t* p, int i) { return bits_to_f32(p[i]); }
+// Four consecutive elements as floats.
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 ld4(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+               __uint_as_float(v.y & 0xffff0000u)};
+}
+__device__ __forceinline__ float ld1(const float* p) { return *p; }
+__device__ __forceinline__ float ld1(const uint16_t* p) { return bits_to_f32(*p); }
 
-// 16B vector copy of input rows into LDS; rows >= len are zero.
-template <class TI, int W_, int PITCH>
-__device__ __forceinline__ void load_rows(TI* dst, const TI* src, int64_t row_stride, int len, int tid) {
-  constexpr int E = 16 / sizeof(TI);
-  constexpr int PER_ROW = W_ / E;
-  for (int idx = tid; idx < kChunk * PER_ROW; idx += kThreads) {
-    const int r = idx / PER_ROW, cv = idx % PER_ROW;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (r < len) val = *reinterpret_cast<const uint4*>(src + r * row_stride + cv * E);
-    *reinterpret_cast<uint4*>(dst + r * PITCH + cv * E) = val;
-  }
+// The eight elements of row `row` at the fragment k-order of k-tile kb.
+template <class TI>
+__device__ __forceinline__ void row8(const TI* rowp, int kb, int g, float x[8]) {
+  const f32x4 a = ld4(rowp + 32 * kb + 4 * g), b = ld4(rowp + 32 * kb + 16 + 4 * g);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
 
 // 16-deep fp32 product on the matrix cores: element s of lane group g holds k = 4g + s.
@@ -84,7 +86,7 @@ struct IntraParams {
 };
 
 template <class TI, int K, int V>
-__global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
+__global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
   using S = IntraSmem<TI, K, V>;
   using PA = typename Prec<TI>::A;
   using PT = typename Prec<TI>::T;
@@ -94,6 +96,9 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
   using PK = typename Prec<TI>::Kt;
   using PQ = typename Prec<TI>::Q;
   using L = RecordLayout<TI, K, V>;
+  constexpr int E = 16 / sizeof(TI);             // elements per 16-byte load
+  constexpr int NKL = kChunk * K / E / kThreads;  // 16-byte loads per thread for k and g
+  constexpr int NVL = kChunk * V / E / kThreads;  // ... and for v
   extern __shared__ __align__(16) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
@@ -122,22 +127,37 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
     }
     char* rec = p.records + item * p.record_bytes;
     const int64_t tok0 = b * p.T + t0;
+    const TI* qrow0 = gq_ + (tok0 * H + h) * K;   // row r at qrow0 + r * H * K
 
-    // ---- load the chunk (rows >= len are zero: they then contribute nothing)
-    load_rows<TI, K, S::kQP>(sm.q, gq_ + (tok0 * H + h) * K, H * K, len, tid);
-    load_rows<TI, K, S::kQP>(sm.k, gk_ + (tok0 * H + h) * K, H * K, len, tid);
-    load_rows<TI, V, S::kVP>(sm.v, gv_ + (tok0 * H + h) * V, H * V, len, tid);
+    // ---- all loads of the chunk issued at once (rows >= len read as zero)
+    uint4 kreg[NKL], greg[NKL];
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+      const int idx = tid + u * kThreads, r = idx / (K / E), cv = idx % (K / E);
+      kreg[u] = greg[u] = make_uint4(0, 0, 0, 0);
+      if (r < len) {
+        kreg[u] = *reinterpret_cast<const uint4*>(gk_ + ((tok0 + r) * H + h) * K + cv * E);
+        greg[u] = *reinterpret_cast<const uint4*>(gg_ + ((tok0 + r) * H + h) * K + cv * E);
+      }
+    }
     if (tid < kChunk) sm.beta[tid] = tid < len ? load_in(gb_, (tok0 + tid) * H + h) : 0.f;
-    if (tid < 4) sm.span_bits[tid] = 0;
+#pragma unroll
+    for (int u = 0; u < NKL; ++u) {
+      const int idx = tid + u * kThreads, r = idx / (K / E), cv = idx % (K / E);
+      *reinterpret_cast<uint4*>(sm.kv + r * S::kKP + cv * E) = kreg[u];
+      const TI* ge = reinterpret_cast<const TI*>(&greg[u]);
+#pragma unroll
+      for (int e = 0; e < E; ++e) sm.G[r * S::kGP + cv * E + e] = ld1(ge + e);
+    }
+    __syncthreads();
 
     // ---- running sum of g over the chunk, per channel
     {
-      constexpr int RP = kChunk / (kThreads / K);   // rows per thread
+      constexpr int PARTS = kThreads / K, RP = kChunk / PARTS;
       const int c = tid % K, part = tid / K, r0 = part * RP;
       float run = 0.f;
       for (int r = r0; r < r0 + RP; ++r) {
-        const float gv = r < len ? load_in(gg_, ((tok0 + r) * H + h) * K + c) : 0.f;
-        run += gv;
+        run += sm.G[r * S::kGP + c];
         sm.G[r * S::kGP + c] = run;
       }
       sm.part[part * K + c] = run;
@@ -147,50 +167,60 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
       if (part > 0)
         for (int r = r0; r < r0 + RP; ++r) sm.G[r * S::kGP + c] += off;
     }
-    __syncthreads();
 
-    // ---- q/k normalisation factors and the diagonal-block spans
-    {
-      const int r = tid >> 2, qtr = tid & 3;
+    // ---- this wave's rows: q in operand layout, norms, its block's span
+    const int R = w, f = 16 * R, r_own = f + m;
+    auto q_row8 = [&](int kb, float x[8]) {
+      if (r_own < len) {
+        row8(qrow0 + (int64_t)r_own * H * K, kb, gq, x);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = 0.f;
+      }
+    };
+    float nqr = 1.f, nkr = 1.f;
+    if (p.l2norm) {
       float sq = 0.f, sk = 0.f;
-      if (p.l2norm) {
-        for (int c = qtr * (K / 4); c < (qtr + 1) * (K / 4); ++c) {
-          const float a = ldf(sm.q, r * S::kQP + c), bb = ldf(sm.k, r * S::kQP + c);
-          sq += a * a;
-          sk += bb * bb;
-        }
-        sq += __shfl_xor(sq, 1); sq += __shfl_xor(sq, 2);
-        sk += __shfl_xor(sk, 1); sk += __shfl_xor(sk, 2);
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        float kx[8], qx[8];
+        q_row8(kb, qx);
+        row8(sm.kv + r_own * S::kKP, kb, gq, kx);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { sq += qx[j] * qx[j]; sk += kx[j] * kx[j]; }
       }
-      if (qtr == 0) {
-        sm.nq[r] = p.l2norm ? 1.f / sqrtf(sq + 1e-6f) : 1.f;
-        sm.nk[r] = p.l2norm ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
-      }
-      for (int e = tid; e < 4 * K; e += kThreads) {
-        const int blk = e / K, c = e % K;
-        const float span = sm.G[(16 * blk) * S::kGP + c] - sm.G[(16 * blk + 15) * S::kGP + c];
-        atomicMax(&sm.span_bits[blk], __float_as_int(fmaxf(span, 0.f)));
-      }
+      sq += __shfl_xor(sq, 16); sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 16); sk += __shfl_xor(sk, 32);
+      nqr = 1.f / sqrtf(sq + 1e-6f);
+      nkr = 1.f / sqrtf(sk + 1e-6f);
     }
-    __syncthreads();
+    if (gq == 0) sm.nk[r_own] = nkr;
+    __syncthreads();   // G complete, nk visible
+    float span = 0.f;
+#pragma unroll
+    for (int c = lane; c < K; c += kWave) span = fmaxf(span, sm.G[f * S::kGP + c] - sm.G[(f + 15) * S::kGP + c]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
+    const bool diag_split = span <= kSpanMax;
 
-    // ---- A and Aqk for row block R = w: tiles (I, R) with D[i][r], I <= R
-    const int R = w, f = 16 * R;
+    // ---- A and Aqk for row block R = w: tiles (I, R) hold D[i][r], I <= R
     f32x4 accKK[4], accQK[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) { accKK[I] = f32x4{0, 0, 0, 0}; accQK[I] = f32x4{0, 0, 0, 0}; }
-    const bool diag_split = __int_as_float(sm.span_bits[R]) <= kSpanMax;
     {
-      const int r = f + m;
-      const float nqr = sm.nq[r], nkr = sm.nk[r];
+      const int r = r_own;
+#pragma unroll 1
       for (int kb = 0; kb < K / 32; ++kb) {
-        float xk[8], xq[8];
+        float gr[8], gf[8], kx[8], xk[8], xq[8], qx[8];
+        q_row8(kb, qx);
+        row8(sm.G + r * S::kGP, kb, gq, gr);
+        row8(sm.G + f * S::kGP, kb, gq, gf);
+        row8(sm.kv + r * S::kKP, kb, gq, kx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const int c = 32 * kb + kperm(gq, j);
-          const float e = __expf(sm.G[r * S::kGP + c] - sm.G[f * S::kGP + c]);
-          xk[j] = ldf(sm.k, r * S::kQP + c) * nkr * e;
-          xq[j] = ldf(sm.q, r * S::kQP + c) * nqr * e;
+          const float e = __expf(gr[j] - gf[j]);
+          xk[j] = kx[j] * nkr * e;
+          xq[j] = qx[j] * nqr * e;
         }
         PA fkr, fqr;
         fkr.set(xk);
@@ -200,12 +230,11 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
           if (I > R || (I == R && !diag_split)) continue;
           const int i = 16 * I + m;
           const float nki = sm.nk[i];
-          float xc[8];
+          float gi[8], ki[8], xc[8];
+          row8(sm.G + i * S::kGP, kb, gq, gi);
+          row8(sm.kv + i * S::kKP, kb, gq, ki);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int c = 32 * kb + kperm(gq, j);
-            xc[j] = ldf(sm.k, i * S::kQP + c) * nki * __expf(sm.G[f * S::kGP + c] - sm.G[i * S::kGP + c]);
-          }
+          for (int j = 0; j < 8; ++j) xc[j] = ki[j] * nki * __expf(gf[j] - gi[j]);
           PA fkc;
           fkc.set(xc);
           mma(accKK[I], fkc, fkr);
@@ -222,9 +251,9 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
             const float nki = sm.nk[i];
             for (int c = 0; c < K; ++c) {
               const float e = __expf(sm.G[r * S::kGP + c] - sm.G[i * S::kGP + c]);
-              const float kk = ldf(sm.k, i * S::kQP + c) * nki * e;
-              sk_ += ldf(sm.k, r * S::kQP + c) * nkr * kk;
-              sq_ += ldf(sm.q, r * S::kQP + c) * nqr * kk;
+              const float kk = ld1(sm.kv + i * S::kKP + c) * nki * e;
+              sk_ += ld1(sm.kv + r * S::kKP + c) * nkr * kk;
+              sq_ += ld1(qrow0 + (int64_t)r * H * K + c) * nqr * kk;
             }
           }
 #pragma unroll
@@ -245,6 +274,20 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
         }
       }
     }
+    // ---- scale * Aqk, rows of block w: the D[i][r] tiles (I, w) are the operand layout
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float x[8];
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        x[ii] = (2 * kb <= R) ? accQK[2 * kb][ii] : 0.f;
+        x[4 + ii] = (2 * kb + 1 <= R) ? accQK[2 * kb + 1][ii] : 0.f;
+      }
+      PQ af;
+      af.set(x);
+      af.store(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<PQ>(), lane);
+    }
+
     __syncthreads();
 
     // ---- T = (I + A)^-1: invert the four 16x16 diagonal blocks (wave w: block w)
@@ -252,12 +295,12 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
       const int j = lane;
       float t[16], acc[16];
 #pragma unroll
-      for (int s = 0; s < 16; ++s) acc[s] = 0.f;
+      for (int s2 = 0; s2 < 16; ++s2) acc[s2] = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         t[r] = (r == j) ? 1.f : (r < j ? 0.f : -acc[r]);
 #pragma unroll
-        for (int s = r + 1; s < 16; ++s) acc[s] += sm.M[(f + r) * S::kMP + f + s] * t[r];   // A[f+s][f+r]
+        for (int s2 = r + 1; s2 < 16; ++s2) acc[s2] += sm.M[(f + r) * S::kMP + f + s2] * t[r];   // A[f+s2][f+r]
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -272,18 +315,18 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
         for (int J = II; J < RR; ++J) {
           float a[4], bb[4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            a[s] = sm.M[(16 * J + 4 * gq + s) * S::kMP + 16 * RR + m];   // A[16RR+m][16J+4gq+s]
-            // T[16J+4gq+s][16II+m]; above the diagonal of a diagonal block M holds A^T, T is 0
-            bb[s] = (J > II || 4 * gq + s >= m) ? sm.M[(16 * J + 4 * gq + s) * S::kMP + 16 * II + m] : 0.f;
+          for (int s2 = 0; s2 < 4; ++s2) {
+            a[s2] = sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * RR + m];   // A[16RR+m][16J+4gq+s2]
+            // T[16J+4gq+s2][16II+m]; above the diagonal of a diagonal block M holds A^T, T is 0
+            bb[s2] = (J > II || 4 * gq + s2 >= m) ? sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * II + m] : 0.f;
           }
           mma16_f32(mm, a, bb);
         }
         float a[4], bb[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          a[s] = (m >= 4 * gq + s) ? sm.M[(16 * RR + m) * S::kMP + 16 * RR + 4 * gq + s] : 0.f;  // T_RR[m][4gq+s]
-          bb[s] = mm[s];
+        for (int s2 = 0; s2 < 4; ++s2) {
+          a[s2] = (m >= 4 * gq + s2) ? sm.M[(16 * RR + m) * S::kMP + 16 * RR + 4 * gq + s2] : 0.f;  // T_RR[m][4gq+s2]
+          bb[s2] = mm[s2];
         }
         f32x4 res = {0, 0, 0, 0};
         mma16_f32(res, a, bb);
@@ -301,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 32 * kb + kperm(gq, j);
-        x[j] = ldf(sm.k, r * S::kQP + c) * sm.nk[r] * __expf(gc - sm.G[r * S::kGP + c]);
+        x[j] = ld1(sm.kv + r * S::kKP + c) * sm.nk[r] * __expf(gc - sm.G[r * S::kGP + c]);
       }
       PK fr;
       fr.set(x);
@@ -309,102 +352,122 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(IntraParams p) {
     }
     __syncthreads();
     // exp(G) in place of G from here on.
-    for (int e = tid; e < kChunk * K; e += kThreads) {
-      const int r = e / K, c = e % K;
-      sm.G[r * S::kGP + c] = __expf(sm.G[r * S::kGP + c]);
+    for (int e4 = tid; e4 < kChunk * K / 4; e4 += kThreads) {
+      const int r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
+      f32x4 x = ld4(sm.G + r * S::kGP + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __expf(x[i]);
+      *reinterpret_cast<f32x4*>(sm.G + r * S::kGP + c) = x;
     }
     __syncthreads();
     if (tid < K) reinterpret_cast<float*>(rec + L::kGc)[tid] = sm.G[(kChunk - 1) * S::kGP + tid];
 
-    // ---- -W = -(T diag(beta) (K * exp(G))), computed as W^T tiles D[c][r] for rows r of block w
-    {
-      const int r = 16 * w + m;
-      PT tf[2];
-      PT tb[2];
+    // ---- T fragments (row r of block rb, k = i): T and T diag(beta); T[r][i] = 0 for i > r
+    auto t_frag = [&](int rb, int kb, bool with_beta) {
+      const int r = 16 * rb + m;
+      float x[8];
+      const f32x4 a = ld4(sm.M + r * S::kMP + 32 * kb + 4 * gq), c4 = ld4(sm.M + r * S::kMP + 32 * kb + 16 + 4 * gq);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float xt[8], xtb[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 32 * kb + kperm(gq, j);
-          const float tv = (i <= r) ? sm.M[r * S::kMP + i] : 0.f;
-          xt[j] = tv;
-          xtb[j] = tv * sm.beta[i];
-        }
-        tf[kb].set(xt);
-        tb[kb].set(xtb);
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * kb + kperm(gq, j);
+        const float tv = j < 4 ? a[j] : c4[j - 4];
+        x[j] = (i <= r) ? (with_beta ? tv * sm.beta[i] : tv) : 0.f;
       }
-      const int nkb = w / 2 + 1;   // T[r][i] = 0 for i > r
-      for (int kb2 = 0; kb2 < K / 32; ++kb2) {
-        f32x4 acc2[2];
+      PT fr;
+      fr.set(x);
+      return fr;
+    };
+
+    // ---- -W: W^T tiles D[c][r] for the key-channel blocks cb = 2w, 2w+1 and every row block
+    if (2 * w < K / 16) {
+      PX xf[2][2];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int cb = 2 * kb2 + hh, c = 16 * cb + m;
-          acc2[hh] = f32x4{0, 0, 0, 0};
+      for (int hh = 0; hh < 2; ++hh) {
+        const int c = 16 * (2 * w + hh) + m;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            if (kb >= nkb) continue;
-            float x[8];
+        for (int kb = 0; kb < 2; ++kb) {
+          float x[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const int i = 32 * kb + kperm(gq, j);
-              x[j] = sm.beta[i] * ldf(sm.k, i * S::kQP + c) * sm.nk[i] * sm.G[i * S::kGP + c];
-            }
-            PX xf;
-            xf.set(x);
-            mma(acc2[hh], xf, tf[kb]);
+          for (int j = 0; j < 8; ++j) {
+            const int i = 32 * kb + kperm(gq, j);
+            x[j] = sm.beta[i] * ld1(sm.kv + i * S::kKP + c) * sm.nk[i] * sm.G[i * S::kGP + c];
           }
+          xf[hh][kb].set(x);
+        }
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 acc2[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb > rb / 2) continue;
+          const PT tf = t_frag(rb, kb, false);
+          mma(acc2[0], xf[0][kb], tf);
+          mma(acc2[1], xf[1][kb], tf);
         }
         float wv[8];
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) { wv[ii] = -acc2[0][ii]; wv[4 + ii] = -acc2[1][ii]; }
         PW wf;
         wf.set(wv);
-        wf.store(rec + L::kWn + (int64_t)(w * (K / 32) + kb2) * tile_bytes<PW>(), lane);
+        wf.store(rec + L::kWn + (int64_t)(rb * (K / 32) + w) * tile_bytes<PW>(), lane);
       }
-      // ---- U = T diag(beta) V, rows of block w, output-tile layout
-      for (int vb = 0; vb < V / 16; ++vb) {
-        f32x4 acc = {0, 0, 0, 0};
+    }
+
+    // ---- scale * q * exp(G), rows of block w
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      float gr[8], x[8], qx[8];
+      q_row8(kb, qx);
+      row8(sm.G + r_own * S::kGP, kb, gq, gr);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = p.scale * qx[j] * nqr * gr[j];
+      PQ qf;
+      qf.set(x);
+      qf.store(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<PQ>(), lane);
+    }
+    // ---- U = T diag(beta) V: v staged into the k region, value blocks vb = 2w, 2w+1
+    {
+      uint4 vreg[NVL];
+#pragma unroll
+      for (int u = 0; u < NVL; ++u) {
+        const int idx = tid + u * kThreads, r = idx / (V / E), cv = idx % (V / E);
+        vreg[u] = make_uint4(0, 0, 0, 0);
+        if (r < len) vreg[u] = *reinterpret_cast<const uint4*>(gv_ + ((tok0 + r) * H + h) * V + cv * E);
+      }
+      __syncthreads();   // k no longer read
+#pragma unroll
+      for (int u = 0; u < NVL; ++u) {
+        const int idx = tid + u * kThreads, r = idx / (V / E), cv = idx % (V / E);
+        *reinterpret_cast<uint4*>(sm.kv + r * S::kKP + cv * E) = vreg[u];
+      }
+    }
+    __syncthreads();
+    if (2 * w < V / 16) {
+      PV vf[2][2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          if (kb >= nkb) continue;
           float x[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 32 * kb + kperm(gq, j);
-            x[j] = ldf(sm.v, i * S::kVP + 16 * vb + m);
-          }
-          PV vf;
-          vf.set(x);
-          mma(acc, tb[kb], vf);
+          for (int j = 0; j < 8; ++j) x[j] = ld1(sm.kv + (32 * kb + kperm(gq, j)) * S::kKP + 16 * (2 * w + hh) + m);
+          vf[hh][kb].set(x);
         }
-        reinterpret_cast<f32x4*>(rec + L::kU)[(w * (V / 16) + vb) * kWave + lane] = acc;
       }
-      // ---- scale * q * exp(G), rows of block w
-      const float nqr = sm.nq[r];
-      for (int kb = 0; kb < K / 32; ++kb) {
-        float x[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = 32 * kb + kperm(gq, j);
-          x[j] = p.scale * ldf(sm.q, r * S::kQP + c) * nqr * sm.G[r * S::kGP + c];
+      for (int rb = 0; rb < 4; ++rb) {
+        f32x4 acc2[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb > rb / 2) continue;
+          const PT tb = t_frag(rb, kb, true);
+          mma(acc2[0], tb, vf[0][kb]);
+          mma(acc2[1], tb, vf[1][kb]);
         }
-        PQ qf;
-        qf.set(x);
-        qf.store(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<PQ>(), lane);
-      }
-      // ---- scale * Aqk, rows of block w: D[i][r] tiles (I, w) are the operand layout
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float x[8];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          x[ii] = (2 * kb <= R) ? accQK[2 * kb][ii] : 0.f;
-          x[4 + ii] = (2 * kb + 1 <= R) ? accQK[2 * kb + 1][ii] : 0.f;
-        }
-        PQ af;
-        af.set(x);
-        af.store(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<PQ>(), lane);
+        for (int hh = 0; hh < 2; ++hh)
+          reinterpret_cast<f32x4*>(rec + L::kU)[(rb * (V / 16) + 2 * w + hh) * kWave + lane] = acc2[hh];
       }
     }
     __syncthreads();   // LDS is reused by the next item

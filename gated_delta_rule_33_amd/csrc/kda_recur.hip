@@ -81,6 +81,40 @@ __device__ __forceinline__ void store_out(uint16_t* o, int64_t i, float x) {
   o[i] = *reinterpret_cast<const uint16_t*>(&h);
 }
 
+// Every operand one wave reads from a chunk record, held in registers so
+// that the next chunk's loads are in flight while this chunk computes.
+template <class TI, int K, int V>
+struct ChunkOps {
+  using P = Prec<TI>;
+  static constexpr int NCB = K / 16 / 4;
+  f32x4 u;
+  typename P::W wn[K / 32];
+  typename P::Kt kt[NCB][2];
+  typename P::Q qg[K / 32];
+  typename P::Q aqk[2];
+  f32x4 gc[NCB];
+  __device__ __forceinline__ void load(const char* rec, int w, int j, int lane, int gq) {
+    using L = RecordLayout<TI, K, V>;
+    u = reinterpret_cast<const f32x4*>(rec + L::kU)[(w * (V / 16) + j) * kWave + lane];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) {
+      wn[kb].load(rec + L::kWn + (int64_t)(w * (K / 32) + kb) * tile_bytes<typename P::W>(), lane);
+      qg[kb].load(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<typename P::Q>(), lane);
+    }
+#pragma unroll
+    for (int u_ = 0; u_ < NCB; ++u_) {
+      const int cb = w * NCB + u_;
+      gc[u_] = *reinterpret_cast<const f32x4*>(rec + L::kGc + 4 * (16 * cb + 4 * gq));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kt[u_][kb].load(rec + L::kKt + (int64_t)(cb * 2 + kb) * tile_bytes<typename P::Kt>(), lane);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= w / 2) aqk[kb].load(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<typename P::Q>(), lane);
+  }
+};
+
 struct RecurParams {
   int64_t B, T, H;
   int64_t nc_fixed;
@@ -100,10 +134,6 @@ template <class TI, class TO, int K, int V>
 __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
   using PS = typename Prec<TI>::S;
   using PD = typename Prec<TI>::D;
-  using PW = typename Prec<TI>::W;
-  using PK = typename Prec<TI>::Kt;
-  using PQ = typename Prec<TI>::Q;
-  using L = RecordLayout<TI, K, V>;
   constexpr int NV = V / kVT;
   constexpr int SP = K + 8;        // LDS row pitch of the state operand
   constexpr int DP = kChunk + 8;   // LDS row pitch of the Delta operand
@@ -155,10 +185,8 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
   }
   __syncthreads();
 
-  int cur = 0;
-  for (int64_t n = 0; n < n_chunks; ++n) {
-    int64_t rec_idx, t0;
-    int len;
+  // Chunk n's record index, first token and length.
+  auto chunk_info = [&](int64_t n, int64_t& rec_idx, int64_t& t0, int& len) {
     if (p.packed) {
       const ChunkEntry ce = p.chunks[chunk0 + n];
       rec_idx = (chunk0 + n) * H + h;
@@ -169,16 +197,33 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
       t0 = n * kChunk;
       len = (int)min<int64_t>(kChunk, p.T - t0);
     }
-    const char* rec = p.records + rec_idx * p.record_bytes;
+  };
+
+  // The operands of chunk n + 1 (clamped to the last chunk) are loaded while
+  // chunk n computes; `cur` is loop-carried, so those loads cannot sink.
+  ChunkOps<TI, K, V> cur;
+  int64_t t0 = 0, t0n = 0;
+  int len = 0, lenn = 0;
+  int buf = 0;
+  if (n_chunks > 0) {
+    int64_t rec_idx;
+    chunk_info(0, rec_idx, t0, len);
+    cur.load(p.records + rec_idx * p.record_bytes, w, j, lane, gq);
+  }
+  for (int64_t n = 0; n < n_chunks; ++n) {
+    ChunkOps<TI, K, V> nxt;
+    {
+      int64_t rec_idx;
+      chunk_info(n + 1 < n_chunks ? n + 1 : n, rec_idx, t0n, lenn);
+      nxt.load(p.records + rec_idx * p.record_bytes, w, j, lane, gq);
+    }
 
     // Delta = U - W S for tokens 16w..16w+15
-    f32x4 d = reinterpret_cast<const f32x4*>(rec + L::kU)[(w * NV + j) * kWave + lane];
+    f32x4 d = cur.u;
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
-      PW a;
-      a.load(rec + L::kWn + (int64_t)(w * (K / 32) + kb) * tile_bytes<PW>(), lane);
-      const PS s = LdsPlane<PS>::template read<kVT, SP>(s_state[cur], m, kb, gq);
-      mma(d, a, s);
+      const PS s = LdsPlane<PS>::template read<kVT, SP>(s_state[buf], m, kb, gq);
+      mma(d, cur.wn[kb], s);
     }
     {
       float x[4] = {d[0], d[1], d[2], d[3]};
@@ -190,34 +235,29 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
 #pragma unroll
     for (int u = 0; u < NCB; ++u) {
       const int cb = w * NCB + u, c0 = 16 * cb + 4 * gq;
-      const f32x4 gc = *reinterpret_cast<const f32x4*>(rec + L::kGc + 4 * c0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[u][i] *= gc[i];
+      for (int i = 0; i < 4; ++i) st[u][i] *= cur.gc[u][i];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        PK a;
-        a.load(rec + L::kKt + (int64_t)(cb * 2 + kb) * tile_bytes<PK>(), lane);
         const PD dd = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
-        mma(st[u], a, dd);
+        mma(st[u], cur.kt[u][kb], dd);
       }
       float x[4] = {st[u][0], st[u][1], st[u][2], st[u][3]};
-      LdsPlane<PS>::template write4<kVT, SP>(s_state[cur ^ 1], m, c0, x);
+      LdsPlane<PS>::template write4<kVT, SP>(s_state[buf ^ 1], m, c0, x);
     }
 
     // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
     f32x4 ov = {0, 0, 0, 0};
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
-      PQ a;
-      a.load(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<PQ>(), lane);
-      const PS s = LdsPlane<PS>::template read<kVT, SP>(s_state[cur], m, kb, gq);
-      mma(ov, a, s);
+      const PS s = LdsPlane<PS>::template read<kVT, SP>(s_state[buf], m, kb, gq);
+      mma(ov, cur.qg[kb], s);
     }
-    for (int kb = 0; kb <= w / 2; ++kb) {
-      PQ a;
-      a.load(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<PQ>(), lane);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (kb > w / 2) continue;
       const PD dd = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
-      mma(ov, a, dd);
+      mma(ov, cur.aqk[kb], dd);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -225,7 +265,10 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
       if (r < len) store_out(out, ((b * p.T + t0 + r) * H + h) * V + v0 + m, ov[i]);
     }
     __syncthreads();
-    cur ^= 1;
+    buf ^= 1;
+    cur = nxt;
+    t0 = t0n;
+    len = lenn;
   }
 
   if (p.fin) {
