@@ -1,11 +1,12 @@
 """Pins of the CPU oracle against facts fixed by the pages and by mathematics.
 
-Each test names what it pins.  Sources: the "Delta Rule formulation" and the
-Test Coverage "Properties" row (zero gate accumulates, large negative gate
-decays) of the page "feat(kda): integrate KDA attention with tokamax backend
-and CP support"; the same page's forward tests (packed sequences, segment_ids
-fallback, row independence, CP equivalence); the review commit on the second
-copy of that page (within-row packed-segment isolation, l2-norm unit norm).
+Each test names what it pins.  Sources: the Delta Rule formulation and the
+Properties row of the Test Coverage table (a zero gate keeps accumulating, a
+very negative gate empties the state) on the page "feat(kda): integrate KDA
+attention with tokamax backend and CP support"; that page's forward tests
+(packed sequences, the missing-segment-ids fallback, row independence, CP
+equivalence); the review commits on the second copy of that page (segments in
+one row stay isolated, normalised vectors have unit norm).
 None of these tests re-types the oracle's loop: each compares it with a
 closed form, a different algorithm, or an invariant.
 """
@@ -35,7 +36,7 @@ def _orthonormal(n, seed):
 # ---------------------------------------------------------------- closed forms
 
 def test_zero_gate_orthonormal_keys_is_causal_linear_attention():
-    """g = 0 accumulates (Properties: zero-gate accumulates).  With orthonormal
+    """g = 0 keeps accumulating (Test Coverage, Properties).  With orthonormal
     keys each residual is the full value, so o_t = scale sum_{i<=t} beta_i (q_t.k_i) v_i
     and the final state is sum_i beta_i k_i v_i^T."""
     B, T, H, K, V = 1, 6, 2, 8, 5
@@ -87,7 +88,7 @@ def test_distinct_channel_keys_decay_on_key_axis():
 
 
 def test_large_negative_gate_decays_state_to_zero():
-    """Properties: large-negative-gate decays.  exp(-1e4) is exactly 0, so each
+    """A very negative gate empties the state (Test Coverage, Properties).  exp(-1e4) is exactly 0, so each
     step starts from an empty state: S_t = beta_t k_t v_t^T and
     o_t = scale beta_t (q_t.k_t) v_t (the read-out sees token t's own write)."""
     B, T, H, K, V = 2, 7, 3, 8, 4
@@ -235,7 +236,7 @@ def _segments(row):
 
 @pytest.mark.parametrize("with_state", [False, True])
 def test_packed_equals_independent_segment_runs(with_state):
-    """Within-row packed-segment isolation: every segment restarts the recurrence
+    """Segments packed in one row stay isolated: every segment restarts the recurrence
     (from its own initial state), padding (id 0) gets o = 0 and leaves the state
     alone, and a segment's output is exactly that of a run on the segment alone."""
     q, k, v, g, beta, seg = _packed_case()
