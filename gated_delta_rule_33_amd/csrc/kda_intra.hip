@@ -1,5 +1,5 @@
 // Intra-chunk kernel of the KDA forward: everything that does not depend on
-// the recurrent state, for one (chunk, head) per workgroup.
+// the recurrent state, per (chunk, head) item.
 //
 // Notation (rows r, i = tokens of the chunk, c = key channel):
 //   G_r   = sum_{j<=r} g_j, the running log decay inside the chunk
@@ -31,19 +31,36 @@ namespace {
 
 constexpr float kSpanMax = 64.f;
 
-// LDS of one workgroup.  q and v are not staged whole: q is read in operand
-// layout straight from global memory, v is written into the k region once k
-// is no longer needed.  About 72 KB for bf16 K = V = 128, so two workgroups
-// share a CU and one's loads overlap the other's arithmetic.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) const void glob_void_t;
+
+// Rows of W elements kept in LDS with their 16-byte chunks XOR-swizzled by the
+// row index, so that 16 lanes reading one chunk of 16 different rows hit 16
+// different bank groups.  Direct-to-LDS loads write 64 consecutive 16-byte
+// slots per instruction; each lane picks the global chunk that belongs in its
+// slot, which is how the swizzle is applied on the way in.
+template <class TI, int W>
+struct SwzRows {
+  static constexpr int E = 16 / (int)sizeof(TI);   // elements per chunk
+  static constexpr int NCH = W / E;                  // chunks per row
+  __device__ static __forceinline__ int idx(int r, int c) {
+    return r * W + (((c / E) ^ (r % NCH)) * E) + (c % E);
+  }
+};
+
 template <class TI, int K, int V>
 struct IntraSmem {
-  static constexpr int kKP = (K > V ? K : V) + 8;   // row pitch (elements) of k, later v
-  static constexpr int kGP = K + 4;                 // row pitch (floats) of G, later exp(G)
-  static constexpr int kMP = 68;                    // row pitch of M (T below the diagonal, A^T above)
-  TI kv[kChunk * kKP];
+  static constexpr bool kDB = sizeof(TI) == 2;   // k and g/v double-buffered (fits LDS for bf16)
+  static constexpr int NB = kDB ? 2 : 1;
+  static constexpr int kGVW = K > V ? K : V;      // g (width K) and later v (width V) share a buffer
+  static constexpr int kGP = K + 4;               // row pitch (floats) of G, later exp(G)
+  static constexpr int kMP = 68;                  // row pitch of M (T below the diagonal, A^T above)
+  TI q[kChunk * K];
+  TI k[NB][kChunk * K];
+  TI gv[NB][kChunk * kGVW];
   float G[kChunk * kGP];
-  float M[kChunk * kMP];
   float beta[kChunk];
+  float M[kChunk * kMP];
   float nk[kChunk];
   float part[kThreads];
 };
@@ -58,13 +75,40 @@ __device__ __forceinline__ f32x4 ld4(const uint16_t* p) {
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 __device__ __forceinline__ float ld1(const uint16_t* p) { return bits_to_f32(*p); }
 
-// The eight elements of row `row` at the fragment k-order of k-tile kb.
-template <class TI>
-__device__ __forceinline__ void row8(const TI* rowp, int kb, int g, float x[8]) {
+// The eight elements of a swizzled row at the fragment k-order of k-tile kb.
+template <class TI, int W>
+__device__ __forceinline__ void row8(const TI* base, int r, int kb, int g, float x[8]) {
+  using S = SwzRows<TI, W>;
+  const f32x4 a = ld4(base + S::idx(r, 32 * kb + 4 * g)), b = ld4(base + S::idx(r, 32 * kb + 16 + 4 * g));
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+// The same for an fp32 row with a padded pitch.
+__device__ __forceinline__ void row8f(const float* rowp, int kb, int g, float x[8]) {
   const f32x4 a = ld4(rowp + 32 * kb + 4 * g), b = ld4(rowp + 32 * kb + 16 + 4 * g);
   x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
   x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
+
+// This wave's share of the direct-to-LDS loads of a 64 x W tile whose row r
+// starts at src + r * row_stride.  Rows >= len are not loaded (their LDS rows
+// are zeroed after the wait).  Asynchronous: completion is awaited with
+// wait_loads() before the data is read.
+template <class TI, int W>
+__device__ __forceinline__ void issue_rows(TI* lds, const TI* src, int64_t row_stride, int len, int w, int lane) {
+  using S = SwzRows<TI, W>;
+  constexpr int BLOCKS = kChunk * S::NCH / kWave;   // 1 KB blocks
+#pragma unroll
+  for (int bi = w; bi < BLOCKS; bi += kThreads / kWave) {
+    const int L = bi * kWave + lane, r = L / S::NCH, pch = L % S::NCH, cv = pch ^ (r % S::NCH);
+    if (r < len)
+      __builtin_amdgcn_global_load_lds((glob_void_t*)(src + r * row_stride + cv * S::E),
+                                       (lds_void_t*)(lds + bi * kWave * S::E), 16, 0, 0);
+  }
+}
+
+// Wait for every outstanding vector memory operation of this wave.
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
 
 // 16-deep fp32 product on the matrix cores: element s of lane group g holds k = 4g + s.
 __device__ __forceinline__ void mma16_f32(f32x4& c, const float a[4], const float b[4]) {
@@ -85,9 +129,37 @@ struct IntraParams {
   int64_t record_bytes;
 };
 
+struct ItemInfo {
+  int64_t h, tok0;   // head, first token's row index b * T + t0
+  int len;
+};
+
+__device__ __forceinline__ ItemInfo item_info(const IntraParams& p, int64_t item) {
+  ItemInfo it;
+  it.h = item % p.H;
+  const int64_t chunk = item / p.H;
+  if (p.packed) {
+    const ChunkEntry ce = p.chunks[chunk];
+    it.tok0 = (int64_t)ce.b * p.T + ce.t0;
+    it.len = ce.len;
+  } else {
+    const int64_t b = chunk / p.nc_fixed, t0 = (chunk % p.nc_fixed) * kChunk;
+    it.tok0 = b * p.T + t0;
+    it.len = (int)min<int64_t>(kChunk, p.T - t0);
+  }
+  return it;
+}
+
+// One workgroup per CU, looping over (chunk, head) items.  The inputs of the
+// next item are loaded into LDS (direct-to-LDS, asynchronous) while the
+// current item computes: k, g and beta at the start of the item (second
+// buffers), q once the current q is dead (after the A products), v into the g
+// buffer once g has been summed.
 template <class TI, int K, int V>
-__global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
+__global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
   using S = IntraSmem<TI, K, V>;
+  using SK = SwzRows<TI, K>;
+  using SV = SwzRows<TI, V>;
   using PA = typename Prec<TI>::A;
   using PT = typename Prec<TI>::T;
   using PX = typename Prec<TI>::X;
@@ -96,9 +168,6 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
   using PK = typename Prec<TI>::Kt;
   using PQ = typename Prec<TI>::Q;
   using L = RecordLayout<TI, K, V>;
-  constexpr int E = 16 / sizeof(TI);             // elements per 16-byte load
-  constexpr int NKL = kChunk * K / E / kThreads;  // 16-byte loads per thread for k and g
-  constexpr int NVL = kChunk * V / E / kThreads;  // ... and for v
   extern __shared__ __align__(16) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
@@ -112,42 +181,50 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
   const int64_t H = p.H;
   const int64_t n_items = p.packed ? (int64_t)p.hdr->n_chunks * H : p.B * p.nc_fixed * H;
   if (!p.packed && blockIdx.x == 0 && tid == 0) p.hdr->flags = 0;   // no tables without segments
+  if ((int64_t)blockIdx.x >= n_items) return;
 
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x) {
-    const int64_t h = item % H, chunk = item / H;
-    int64_t b, t0;
-    int len;
-    if (p.packed) {
-      const ChunkEntry ce = p.chunks[chunk];
-      b = ce.b; t0 = ce.t0; len = ce.len;
-    } else {
-      b = chunk / p.nc_fixed;
-      t0 = (chunk % p.nc_fixed) * kChunk;
-      len = (int)min<int64_t>(kChunk, p.T - t0);
-    }
+  // beta of the next item travels in one register per lane of wave 0.
+  float beta_next = 0.f;
+  auto issue_kgb = [&](const ItemInfo& it, int buf) {
+    issue_rows<TI, K>(sm.k[buf], gk_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
+    issue_rows<TI, K>(sm.gv[buf], gg_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
+    beta_next = (w == 0 && lane < it.len) ? load_in(gb_, (it.tok0 + lane) * H + it.h) : 0.f;
+  };
+  auto issue_q = [&](const ItemInfo& it) {
+    issue_rows<TI, K>(sm.q, gq_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
+  };
+
+  {
+    const ItemInfo first = item_info(p, blockIdx.x);
+    issue_kgb(first, 0);
+    issue_q(first);
+  }
+
+  int it_no = 0;
+  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x, ++it_no) {
+    const int cb = S::kDB ? (it_no & 1) : 0;
+    const ItemInfo cur = item_info(p, item);
+    const int len = cur.len;
+    const int64_t h = cur.h;
+    const int64_t nxt_item = item + gridDim.x;
+    const bool has_next = nxt_item < n_items;
+    const ItemInfo nxt = has_next ? item_info(p, nxt_item) : cur;
     char* rec = p.records + item * p.record_bytes;
-    const int64_t tok0 = b * p.T + t0;
-    const TI* qrow0 = gq_ + (tok0 * H + h) * K;   // row r at qrow0 + r * H * K
+    TI* kbuf = sm.k[cb];
+    TI* gvbuf = sm.gv[cb];
 
-    // ---- all loads of the chunk issued at once (rows >= len read as zero)
-    uint4 kreg[NKL], greg[NKL];
-#pragma unroll
-    for (int u = 0; u < NKL; ++u) {
-      const int idx = tid + u * kThreads, r = idx / (K / E), cv = idx % (K / E);
-      kreg[u] = greg[u] = make_uint4(0, 0, 0, 0);
-      if (r < len) {
-        kreg[u] = *reinterpret_cast<const uint4*>(gk_ + ((tok0 + r) * H + h) * K + cv * E);
-        greg[u] = *reinterpret_cast<const uint4*>(gg_ + ((tok0 + r) * H + h) * K + cv * E);
+    // ---- this item's q, k, g, beta have landed; zero the rows past the chunk
+    wait_loads();
+    __syncthreads();
+    if (w == 0) sm.beta[lane] = beta_next;   // zero past the chunk
+    if (S::kDB && has_next) issue_kgb(nxt, cb ^ 1);
+    if (len < kChunk) {
+      for (int e = tid; e < (kChunk - len) * K; e += kThreads) {
+        const int r = len + e / K, c = e % K;
+        sm.q[SK::idx(r, c)] = TI(0);
+        kbuf[SK::idx(r, c)] = TI(0);
+        gvbuf[SK::idx(r, c)] = TI(0);
       }
-    }
-    if (tid < kChunk) sm.beta[tid] = tid < len ? load_in(gb_, (tok0 + tid) * H + h) : 0.f;
-#pragma unroll
-    for (int u = 0; u < NKL; ++u) {
-      const int idx = tid + u * kThreads, r = idx / (K / E), cv = idx % (K / E);
-      *reinterpret_cast<uint4*>(sm.kv + r * S::kKP + cv * E) = kreg[u];
-      const TI* ge = reinterpret_cast<const TI*>(&greg[u]);
-#pragma unroll
-      for (int e = 0; e < E; ++e) sm.G[r * S::kGP + cv * E + e] = ld1(ge + e);
     }
     __syncthreads();
 
@@ -155,37 +232,31 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
     {
       constexpr int PARTS = kThreads / K, RP = kChunk / PARTS;
       const int c = tid % K, part = tid / K, r0 = part * RP;
-      float run = 0.f;
-      for (int r = r0; r < r0 + RP; ++r) {
-        run += sm.G[r * S::kGP + c];
-        sm.G[r * S::kGP + c] = run;
-      }
-      sm.part[part * K + c] = run;
+      float gcol[RP];
+#pragma unroll
+      for (int i = 0; i < RP; ++i) gcol[i] = ld1(gvbuf + SK::idx(r0 + i, c));   // all reads in flight
+#pragma unroll
+      for (int i = 1; i < RP; ++i) gcol[i] += gcol[i - 1];
+      sm.part[part * K + c] = gcol[RP - 1];
       __syncthreads();
       float off = 0.f;
       for (int pp = 0; pp < part; ++pp) off += sm.part[pp * K + c];
-      if (part > 0)
-        for (int r = r0; r < r0 + RP; ++r) sm.G[r * S::kGP + c] += off;
-    }
-
-    // ---- this wave's rows: q in operand layout, norms, its block's span
-    const int R = w, f = 16 * R, r_own = f + m;
-    auto q_row8 = [&](int kb, float x[8]) {
-      if (r_own < len) {
-        row8(qrow0 + (int64_t)r_own * H * K, kb, gq, x);
-      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = 0.f;
-      }
-    };
+      for (int i = 0; i < RP; ++i) sm.G[(r0 + i) * S::kGP + c] = gcol[i] + off;
+    }
+    __syncthreads();   // g consumed: the buffer now receives v
+    issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
+
+    // ---- this wave's rows: norms and its block's span
+    const int R = w, f = 16 * R, r_own = f + m;
     float nqr = 1.f, nkr = 1.f;
     if (p.l2norm) {
       float sq = 0.f, sk = 0.f;
 #pragma unroll
       for (int kb = 0; kb < K / 32; ++kb) {
         float kx[8], qx[8];
-        q_row8(kb, qx);
-        row8(sm.kv + r_own * S::kKP, kb, gq, kx);
+        row8<TI, K>(sm.q, r_own, kb, gq, qx);
+        row8<TI, K>(kbuf, r_own, kb, gq, kx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) { sq += qx[j] * qx[j]; sk += kx[j] * kx[j]; }
       }
@@ -195,13 +266,12 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
       nkr = 1.f / sqrtf(sk + 1e-6f);
     }
     if (gq == 0) sm.nk[r_own] = nkr;
-    __syncthreads();   // G complete, nk visible
     float span = 0.f;
-#pragma unroll
     for (int c = lane; c < K; c += kWave) span = fmaxf(span, sm.G[f * S::kGP + c] - sm.G[(f + 15) * S::kGP + c]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
     const bool diag_split = span <= kSpanMax;
+    __syncthreads();   // nk visible
 
     // ---- A and Aqk for row block R = w: tiles (I, R) hold D[i][r], I <= R
     f32x4 accKK[4], accQK[4];
@@ -209,13 +279,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
     for (int I = 0; I < 4; ++I) { accKK[I] = f32x4{0, 0, 0, 0}; accQK[I] = f32x4{0, 0, 0, 0}; }
     {
       const int r = r_own;
-#pragma unroll 1
+#pragma unroll 2
       for (int kb = 0; kb < K / 32; ++kb) {
-        float gr[8], gf[8], kx[8], xk[8], xq[8], qx[8];
-        q_row8(kb, qx);
-        row8(sm.G + r * S::kGP, kb, gq, gr);
-        row8(sm.G + f * S::kGP, kb, gq, gf);
-        row8(sm.kv + r * S::kKP, kb, gq, kx);
+        float gr[8], gf[8], kx[8], qx[8], xk[8], xq[8];
+        row8f(sm.G + r * S::kGP, kb, gq, gr);
+        row8f(sm.G + f * S::kGP, kb, gq, gf);
+        row8<TI, K>(kbuf, r, kb, gq, kx);
+        row8<TI, K>(sm.q, r, kb, gq, qx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float e = __expf(gr[j] - gf[j]);
@@ -225,14 +295,22 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
         PA fkr, fqr;
         fkr.set(xk);
         fqr.set(xq);
+        {   // scale * q * exp(G) for this wave's rows: the output's inter-chunk operand
+          float xg[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) xg[j] = p.scale * qx[j] * nqr * __expf(gr[j]);
+          PQ qf;
+          qf.set(xg);
+          qf.store(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<PQ>(), lane);
+        }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (I > R || (I == R && !diag_split)) continue;
           const int i = 16 * I + m;
           const float nki = sm.nk[i];
           float gi[8], ki[8], xc[8];
-          row8(sm.G + i * S::kGP, kb, gq, gi);
-          row8(sm.kv + i * S::kKP, kb, gq, ki);
+          row8f(sm.G + i * S::kGP, kb, gq, gi);
+          row8<TI, K>(kbuf, i, kb, gq, ki);
 #pragma unroll
           for (int j = 0; j < 8; ++j) xc[j] = ki[j] * nki * __expf(gf[j] - gi[j]);
           PA fkc;
@@ -251,9 +329,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
             const float nki = sm.nk[i];
             for (int c = 0; c < K; ++c) {
               const float e = __expf(sm.G[r * S::kGP + c] - sm.G[i * S::kGP + c]);
-              const float kk = ld1(sm.kv + i * S::kKP + c) * nki * e;
-              sk_ += ld1(sm.kv + r * S::kKP + c) * nkr * kk;
-              sq_ += ld1(qrow0 + (int64_t)r * H * K + c) * nqr * kk;
+              const float kk = ld1(kbuf + SK::idx(i, c)) * nki * e;
+              sk_ += ld1(kbuf + SK::idx(r, c)) * nkr * kk;
+              sq_ += ld1(sm.q + SK::idx(r, c)) * nqr * kk;
             }
           }
 #pragma unroll
@@ -287,10 +365,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
       af.set(x);
       af.store(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<PQ>(), lane);
     }
+    __syncthreads();   // q is dead: the next item's q streams in
+    if (has_next) issue_q(nxt);
 
-    __syncthreads();
-
-    // ---- T = (I + A)^-1: invert the four 16x16 diagonal blocks (wave w: block w)
+    // ---- T = (I + A)^-1, diagonal 16x16 blocks first (wave w: block w)
     if (lane < 16) {
       const int j = lane;
       float t[16], acc[16];
@@ -307,48 +385,63 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
         if (r >= j) sm.M[(f + r) * S::kMP + f + j] = t[r];
     }
     __syncthreads();
-    // ---- off-diagonal blocks by distance: T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI
-    for (int d = 1; d < 4; ++d) {
-      const int RR = w + d, II = w;
-      if (RR < 4) {
+    // ---- off-diagonal blocks, one block column per wave, kept in registers:
+    //      T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI for R = I+1 .. 3, I = w
+    {
+      const int I = w;
+      f32x4 tcol[4];   // T_JI for J > I, accumulator layout (= operand layout with k = rows)
+#pragma unroll
+      for (int RR = 1; RR < 4; ++RR) {
+        if (RR <= I) continue;
         f32x4 mm = {0, 0, 0, 0};
-        for (int J = II; J < RR; ++J) {
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+          if (J < I || J >= RR) continue;
           float a[4], bb[4];
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) {
             a[s2] = sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * RR + m];   // A[16RR+m][16J+4gq+s2]
-            // T[16J+4gq+s2][16II+m]; above the diagonal of a diagonal block M holds A^T, T is 0
-            bb[s2] = (J > II || 4 * gq + s2 >= m) ? sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * II + m] : 0.f;
+            if (J == I)   // T_II: lower part of the diagonal block
+              bb[s2] = (4 * gq + s2 >= m) ? sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * I + m] : 0.f;
+            else
+              bb[s2] = tcol[J][s2];
           }
           mma16_f32(mm, a, bb);
         }
-        float a[4], bb[4];
+        float a[4];
+        const f32x4 trr = ld4(sm.M + (16 * RR + m) * S::kMP + 16 * RR + 4 * gq);
 #pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          a[s2] = (m >= 4 * gq + s2) ? sm.M[(16 * RR + m) * S::kMP + 16 * RR + 4 * gq + s2] : 0.f;  // T_RR[m][4gq+s2]
-          bb[s2] = mm[s2];
-        }
+        for (int s2 = 0; s2 < 4; ++s2) a[s2] = (m >= 4 * gq + s2) ? trr[s2] : 0.f;   // T_RR[m][4gq+s2]
+        float bb[4] = {mm[0], mm[1], mm[2], mm[3]};
         f32x4 res = {0, 0, 0, 0};
         mma16_f32(res, a, bb);
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) sm.M[(16 * RR + 4 * gq + ii) * S::kMP + 16 * II + m] = -res[ii];
+        for (int ii = 0; ii < 4; ++ii) {
+          res[ii] = -res[ii];
+          sm.M[(16 * RR + 4 * gq + ii) * S::kMP + 16 * I + m] = res[ii];
+        }
+        tcol[RR] = res;
       }
-      __syncthreads();
     }
+    __syncthreads();
 
     // ---- Kt = (k * exp(G_C - G))^T as operand tiles [c-block][token k-tile]
     for (int t = w; t < (K / 16) * 2; t += 4) {
-      const int cb = t >> 1, kb = t & 1, c = 16 * cb + m;
+      const int cbk = t >> 1, kb = t & 1, c = 16 * cbk + m;
       const float gc = sm.G[(kChunk - 1) * S::kGP + c];
-      float x[8];
+      float x[8], kv8[8], g8[8], n8[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < 8; ++j) {   // all reads first
         const int r = 32 * kb + kperm(gq, j);
-        x[j] = ld1(sm.kv + r * S::kKP + c) * sm.nk[r] * __expf(gc - sm.G[r * S::kGP + c]);
+        kv8[j] = ld1(kbuf + SK::idx(r, c));
+        g8[j] = sm.G[r * S::kGP + c];
+        n8[j] = sm.nk[r];
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = kv8[j] * n8[j] * __expf(gc - g8[j]);
       PK fr;
       fr.set(x);
-      fr.store(rec + L::kKt + (int64_t)(cb * 2 + kb) * tile_bytes<PK>(), lane);
+      fr.store(rec + L::kKt + (int64_t)(cbk * 2 + kb) * tile_bytes<PK>(), lane);
     }
     __syncthreads();
     // exp(G) in place of G from here on.
@@ -390,7 +483,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 32 * kb + kperm(gq, j);
-            x[j] = sm.beta[i] * ld1(sm.kv + i * S::kKP + c) * sm.nk[i] * sm.G[i * S::kGP + c];
+            x[j] = sm.beta[i] * ld1(kbuf + SK::idx(i, c)) * sm.nk[i] * sm.G[i * S::kGP + c];
           }
           xf[hh][kb].set(x);
         }
@@ -414,34 +507,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
       }
     }
 
-    // ---- scale * q * exp(G), rows of block w
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      float gr[8], x[8], qx[8];
-      q_row8(kb, qx);
-      row8(sm.G + r_own * S::kGP, kb, gq, gr);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = p.scale * qx[j] * nqr * gr[j];
-      PQ qf;
-      qf.set(x);
-      qf.store(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<PQ>(), lane);
-    }
-    // ---- U = T diag(beta) V: v staged into the k region, value blocks vb = 2w, 2w+1
-    {
-      uint4 vreg[NVL];
-#pragma unroll
-      for (int u = 0; u < NVL; ++u) {
-        const int idx = tid + u * kThreads, r = idx / (V / E), cv = idx % (V / E);
-        vreg[u] = make_uint4(0, 0, 0, 0);
-        if (r < len) vreg[u] = *reinterpret_cast<const uint4*>(gv_ + ((tok0 + r) * H + h) * V + cv * E);
-      }
-      __syncthreads();   // k no longer read
-#pragma unroll
-      for (int u = 0; u < NVL; ++u) {
-        const int idx = tid + u * kThreads, r = idx / (V / E), cv = idx % (V / E);
-        *reinterpret_cast<uint4*>(sm.kv + r * S::kKP + cv * E) = vreg[u];
-      }
-    }
+    // ---- U = T diag(beta) V for value blocks vb = 2w, 2w+1: v has landed in the g buffer
+    wait_loads();
+    __syncthreads();
+    if (len < kChunk)
+      for (int e = tid; e < (kChunk - len) * V; e += kThreads) gvbuf[SV::idx(len + e / V, e % V)] = TI(0);
     __syncthreads();
     if (2 * w < V / 16) {
       PV vf[2][2];
@@ -451,7 +521,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
         for (int kb = 0; kb < 2; ++kb) {
           float x[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = ld1(sm.kv + (32 * kb + kperm(gq, j)) * S::kKP + 16 * (2 * w + hh) + m);
+          for (int j = 0; j < 8; ++j) x[j] = ld1(gvbuf + SV::idx(32 * kb + kperm(gq, j), 16 * (2 * w + hh) + m));
           vf[hh][kb].set(x);
         }
       }
@@ -470,8 +540,22 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(IntraParams p) {
           reinterpret_cast<f32x4*>(rec + L::kU)[(rb * (V / 16) + 2 * w + hh) * kWave + lane] = acc2[hh];
       }
     }
-    __syncthreads();   // LDS is reused by the next item
+    __syncthreads();   // k and the g/v buffer are free
+    if (!S::kDB && has_next) issue_kgb(nxt, 0);
   }
+}
+
+// Compute units of the current device (one persistent workgroup each).
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 template <class TI, int K, int V>
@@ -485,7 +569,7 @@ hipError_t launch_intra_t(const CallArgs& a) {
   if (e != hipSuccess) return e;
   const int64_t items = (a.n_max > 0 ? a.cmax : a.B * a.nc_fixed) * a.H;
   if (items <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)std::min<int64_t>(items, 1 << 20);
+  const unsigned grid = (unsigned)std::min<int64_t>(items, cu_count());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, a.stream, p);
   return hipGetLastError();
 }
