@@ -30,6 +30,55 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Direct-to-LDS loads.  One instruction moves 16 bytes per lane from each
+// lane's global address to LDS at (M0 = wave-uniform LDS base) + 16 * lane,
+// i.e. 1 KB per wave.  It is issued from inline assembly so that the compiler
+// does not treat every later LDS read as dependent on it (it cannot tell the
+// LDS blocks apart and would drain all such loads before any LDS read); the
+// issuing code waits for the data itself with vm_wait before reading it.  The
+// compiler's own waits for its register loads only become longer by it: it
+// does not count these loads, so it never assumes fewer are outstanding.
+// s_nop covers the M0-write-to-LDS-DMA hazard.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ void dma16(void* lds_base, const void* lane_src) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds_base);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(lane_src), "{m0}"(m0) : "memory");
+}
+// Copy BYTES (a multiple of 1 KB) from src to the LDS block at dst, one wave.
+template <int BYTES>
+__device__ __forceinline__ void dma_copy(char* dst, const char* src, int lane) {
+  static_assert(BYTES % 1024 == 0, "whole 1 KB blocks");
+#pragma unroll
+  for (int i = 0; i < BYTES / 1024; ++i) dma16(dst + 1024 * i, src + 1024 * i + 16 * lane);
+}
+// Wait until at most N vector memory operations of this wave are outstanding
+// (s_waitcnt vmcnt(N), expcnt and lgkmcnt left open).  The asm statement keeps
+// the compiler from moving LDS reads above the wait.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+// Wait for every outstanding LDS operation of this wave (lgkmcnt(0)).
+__device__ __forceinline__ void lds_wait() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier for data exchanged through LDS: this wave's LDS reads and
+// writes complete, then all waves meet.  __syncthreads() would also wait for
+// every outstanding global load of the wave (its workgroup-scope fence counts
+// the LDS side of direct-to-LDS loads), which would drain the prefetches that
+// are meant to stay in flight across the barrier; those are awaited with
+// vm_wait by the code that reads their data.
+__device__ __forceinline__ void block_sync() {
+  lds_wait();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // k index (0..31) held in element j of lane group g.
 __device__ __forceinline__ int kperm(int g, int j) { return (j < 4) ? 4 * g + j : 12 + 4 * g + j; }
 

@@ -31,9 +31,6 @@ namespace {
 
 constexpr float kSpanMax = 64.f;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void glob_void_t;
-
 // Rows of W elements kept in LDS with their 16-byte chunks XOR-swizzled by the
 // row index, so that 16 lanes reading one chunk of 16 different rows hit 16
 // different bank groups.  Direct-to-LDS loads write 64 consecutive 16-byte
@@ -102,13 +99,12 @@ __device__ __forceinline__ void issue_rows(TI* lds, const TI* src, int64_t row_s
   for (int bi = w; bi < BLOCKS; bi += kThreads / kWave) {
     const int L = bi * kWave + lane, r = L / S::NCH, pch = L % S::NCH, cv = pch ^ (r % S::NCH);
     if (r < len)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(src + r * row_stride + cv * S::E),
-                                       (lds_void_t*)(lds + bi * kWave * S::E), 16, 0, 0);
+      dma16(lds + bi * kWave * S::E, src + r * row_stride + cv * S::E);
   }
 }
 
 // Wait for every outstanding vector memory operation of this wave.
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x3f70); }
+__device__ __forceinline__ void wait_loads() { vm_wait<0>(); }
 
 // 16-deep fp32 product on the matrix cores: element s of lane group g holds k = 4g + s.
 __device__ __forceinline__ void mma16_f32(f32x4& c, const float a[4], const float b[4]) {
@@ -183,12 +179,16 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
   if (!p.packed && blockIdx.x == 0 && tid == 0) p.hdr->flags = 0;   // no tables without segments
   if ((int64_t)blockIdx.x >= n_items) return;
 
-  // beta of the next item travels in one register per lane of wave 0.
-  float beta_next = 0.f;
+  // beta of the next item travels as raw input bits in one register per lane
+  // (lane = token), loaded unconditionally from a clamped token and widened
+  // only after the wait for the item's loads: a load whose value is used at
+  // once would make the compiler wait for every load in flight, the
+  // direct-to-LDS prefetches included.
+  TI beta_next = TI(0);
   auto issue_kgb = [&](const ItemInfo& it, int buf) {
     issue_rows<TI, K>(sm.k[buf], gk_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
     issue_rows<TI, K>(sm.gv[buf], gg_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
-    beta_next = (w == 0 && lane < it.len) ? load_in(gb_, (it.tok0 + lane) * H + it.h) : 0.f;
+    beta_next = gb_[(it.tok0 + min(lane, it.len - 1)) * H + it.h];
   };
   auto issue_q = [&](const ItemInfo& it) {
     issue_rows<TI, K>(sm.q, gq_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
@@ -215,8 +215,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
 
     // ---- this item's q, k, g, beta have landed; zero the rows past the chunk
     wait_loads();
-    __syncthreads();
-    if (w == 0) sm.beta[lane] = beta_next;   // zero past the chunk
+    block_sync();
+    if (w == 0) sm.beta[lane] = lane < len ? ld1(&beta_next) : 0.f;   // zero past the chunk
     if (S::kDB && has_next) issue_kgb(nxt, cb ^ 1);
     if (len < kChunk) {
       for (int e = tid; e < (kChunk - len) * K; e += kThreads) {
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
         gvbuf[SK::idx(r, c)] = TI(0);
       }
     }
-    __syncthreads();
+    block_sync();
 
     // ---- running sum of g over the chunk, per channel
     {
@@ -238,13 +238,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
 #pragma unroll
       for (int i = 1; i < RP; ++i) gcol[i] += gcol[i - 1];
       sm.part[part * K + c] = gcol[RP - 1];
-      __syncthreads();
+      block_sync();
       float off = 0.f;
       for (int pp = 0; pp < part; ++pp) off += sm.part[pp * K + c];
 #pragma unroll
       for (int i = 0; i < RP; ++i) sm.G[(r0 + i) * S::kGP + c] = gcol[i] + off;
     }
-    __syncthreads();   // g consumed: the buffer now receives v
+    block_sync();   // g consumed: the buffer now receives v
     issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
 
     // ---- this wave's rows: norms and its block's span
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
     const bool diag_split = span <= kSpanMax;
-    __syncthreads();   // nk visible
+    block_sync();   // nk visible
 
     // ---- A and Aqk for row block R = w: tiles (I, R) hold D[i][r], I <= R
     f32x4 accKK[4], accQK[4];
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
       af.set(x);
       af.store(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<PQ>(), lane);
     }
-    __syncthreads();   // q is dead: the next item's q streams in
+    block_sync();   // q is dead: the next item's q streams in
     if (has_next) issue_q(nxt);
 
     // ---- T = (I + A)^-1, diagonal 16x16 blocks first (wave w: block w)
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
       for (int r = 0; r < 16; ++r)
         if (r >= j) sm.M[(f + r) * S::kMP + f + j] = t[r];
     }
-    __syncthreads();
+    block_sync();
     // ---- off-diagonal blocks, one block column per wave, kept in registers:
     //      T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI for R = I+1 .. 3, I = w
     {
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
         tcol[RR] = res;
       }
     }
-    __syncthreads();
+    block_sync();
 
     // ---- Kt = (k * exp(G_C - G))^T as operand tiles [c-block][token k-tile]
     for (int t = w; t < (K / 16) * 2; t += 4) {
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
       fr.set(x);
       fr.store(rec + L::kKt + (int64_t)(cbk * 2 + kb) * tile_bytes<PK>(), lane);
     }
-    __syncthreads();
+    block_sync();
     // exp(G) in place of G from here on.
     for (int e4 = tid; e4 < kChunk * K / 4; e4 += kThreads) {
       const int r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
       for (int i = 0; i < 4; ++i) x[i] = __expf(x[i]);
       *reinterpret_cast<f32x4*>(sm.G + r * S::kGP + c) = x;
     }
-    __syncthreads();
+    block_sync();
     if (tid < K) reinterpret_cast<float*>(rec + L::kGc)[tid] = sm.G[(kChunk - 1) * S::kGP + tid];
 
     // ---- T fragments (row r of block rb, k = i): T and T diag(beta); T[r][i] = 0 for i > r
@@ -509,10 +509,10 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
 
     // ---- U = T diag(beta) V for value blocks vb = 2w, 2w+1: v has landed in the g buffer
     wait_loads();
-    __syncthreads();
+    block_sync();
     if (len < kChunk)
       for (int e = tid; e < (kChunk - len) * V; e += kThreads) gvbuf[SV::idx(len + e / V, e % V)] = TI(0);
-    __syncthreads();
+    block_sync();
     if (2 * w < V / 16) {
       PV vf[2][2];
 #pragma unroll
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
           reinterpret_cast<f32x4*>(rec + L::kU)[(rb * (V / 16) + 2 * w + hh) * kWave + lane] = acc2[hh];
       }
     }
-    __syncthreads();   // k and the g/v buffer are free
+    block_sync();   // k and the g/v buffer are free
     if (!S::kDB && has_next) issue_kgb(nxt, 0);
   }
 }

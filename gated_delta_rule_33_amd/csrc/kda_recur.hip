@@ -11,14 +11,34 @@
 // following the chunk form of the "Delta Rule formulation" on the page
 // "feat(kda): integrate KDA attention with tokamax backend and CP support"
 // (Implementation Details).  The S and Delta operands are exchanged between
-// the four waves through LDS; all other operands come from the per-chunk
-// records the intra-chunk kernel wrote.
+// the four compute waves through LDS; all other operands come from the
+// per-chunk records the intra-chunk kernel wrote, staged into LDS by
+// producer waves.
+//
+// Wave roles.  A wave that issues direct-to-LDS loads moves about 10 bytes
+// per clock: the rate is per issuing wave (per SIMD), so a compute wave that
+// loads its own operands spends most of a step stalled on issue.  Here
+// producer wave 4 + i fills the stage of compute wave i (waves are spread
+// round-robin over the SIMDs, so each SIMD hosts one of each), and wave 8
+// pulls records a few chunks ahead into L2.  Three barriers per chunk:
+//   B1 after the Delta phase, B15 after the state update, B2 after the
+//   output phase.
+// A stage group is refilled as soon as the barrier after its last reader
+// has passed, and the producer waits for it before the barrier that opens
+// its next reader: Wn/U (read before B1) refill after B1 and land by B2;
+// Kt/Gc (read between B1 and B15) refill after B15 and land by the next B1;
+// Qg/Aqk (read between B15 and B2) refill after B2 and land by the next B15.
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
 constexpr int kVT = 16;   // value channels per workgroup
+constexpr int kComputeWaves = 4;
+constexpr int kProducer0 = kComputeWaves;          // producer of compute wave i: kProducer0 + i
+constexpr int kPrefetchWave = 2 * kComputeWaves;
+constexpr int kRecurThreads = (kPrefetchWave + 1) * kWave;
+constexpr int kPrefetchAhead = 4;   // chunks between the L2 prefetch and the use of a record
 
 // An operand kept in LDS as rows n (value channel) of k-contiguous values.
 template <class F> struct LdsPlane;
@@ -81,37 +101,51 @@ __device__ __forceinline__ void store_out(uint16_t* o, int64_t i, float x) {
   o[i] = *reinterpret_cast<const uint16_t*>(&h);
 }
 
-// Every operand one wave reads from a chunk record, held in registers so
-// that the next chunk's loads are in flight while this chunk computes.
+// The record operands compute wave w uses in one chunk, staged in its own LDS
+// block by its producer wave with direct-to-LDS loads.
+//   Wn  : -W rows 16w..16w+15, all K          (K/32 tiles)
+//   U   : U rows 16w..16w+15, this value tile  (1 KB)
+//   Kt  : key-channel blocks cb = w*NCB+u      (NCB x 2 tiles)
+//   Qg  : Qg rows 16w..16w+15, all K          (K/32 tiles)
+//   Aqk : Aqk row block w, token blocks <= w/2 (1 or 2 tiles)
+//   Gc  : exp(G_C) for this wave's key-channel blocks (16 NCB floats)
 template <class TI, int K, int V>
-struct ChunkOps {
+struct Stage {
   using P = Prec<TI>;
-  static constexpr int NCB = K / 16 / 4;
-  f32x4 u;
-  typename P::W wn[K / 32];
-  typename P::Kt kt[NCB][2];
-  typename P::Q qg[K / 32];
-  typename P::Q aqk[2];
-  f32x4 gc[NCB];
-  __device__ __forceinline__ void load(const char* rec, int w, int j, int lane, int gq) {
-    using L = RecordLayout<TI, K, V>;
-    u = reinterpret_cast<const f32x4*>(rec + L::kU)[(w * (V / 16) + j) * kWave + lane];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      wn[kb].load(rec + L::kWn + (int64_t)(w * (K / 32) + kb) * tile_bytes<typename P::W>(), lane);
-      qg[kb].load(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<typename P::Q>(), lane);
-    }
-#pragma unroll
-    for (int u_ = 0; u_ < NCB; ++u_) {
-      const int cb = w * NCB + u_;
-      gc[u_] = *reinterpret_cast<const f32x4*>(rec + L::kGc + 4 * (16 * cb + 4 * gq));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        kt[u_][kb].load(rec + L::kKt + (int64_t)(cb * 2 + kb) * tile_bytes<typename P::Kt>(), lane);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) aqk[kb].load(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<typename P::Q>(), lane);
+  using L = RecordLayout<TI, K, V>;
+  static constexpr int NCB = K / 64;
+  static constexpr int kWnBytes = (K / 32) * tile_bytes<typename P::W>();
+  static constexpr int kKtBytes = NCB * 2 * tile_bytes<typename P::Kt>();
+  static constexpr int kQgBytes = (K / 32) * tile_bytes<typename P::Q>();
+  static constexpr int kAqkTile = tile_bytes<typename P::Q>();
+  static constexpr int oWn = 0;
+  static constexpr int oU = oWn + kWnBytes;
+  static constexpr int oKt = oU + 1024;
+  static constexpr int oQg = oKt + kKtBytes;
+  static constexpr int oAqk = oQg + kQgBytes;
+  static constexpr int oGc = oAqk + 2 * kAqkTile;
+  static constexpr int kBytes = oGc + 64 * NCB;
+  // Load instructions (1 KB each) per group.
+  static constexpr int nW = kWnBytes / 1024 + 1;   // Wn and U
+  static constexpr int nKt = kKtBytes / 1024 + 1;   // Kt and Gc
+  static constexpr int nQ1 = (kQgBytes + kAqkTile) / 1024;       // Qg and Aqk, waves 0 and 1
+  static constexpr int nQ2 = (kQgBytes + 2 * kAqkTile) / 1024;   // waves 2 and 3
+
+  __device__ static void issue_w(char* stg, const char* rec, int w, int j, int lane) {
+    dma_copy<kWnBytes>(stg + oWn, rec + L::kWn + (int64_t)w * kWnBytes, lane);
+    dma_copy<1024>(stg + oU, rec + L::kU + (int64_t)(w * (V / 16) + j) * 1024, lane);
+  }
+  __device__ static void issue_kt(char* stg, const char* rec, int w, int lane) {
+    dma_copy<kKtBytes>(stg + oKt, rec + L::kKt + (int64_t)w * kKtBytes, lane);
+    if (lane < 4 * NCB) dma16(stg + oGc, rec + L::kGc + 64 * (w * NCB) + 16 * lane);
+  }
+  __device__ static void issue_q(char* stg, const char* rec, int w, int lane) {
+    dma_copy<kQgBytes>(stg + oQg, rec + L::kQg + (int64_t)w * kQgBytes, lane);
+    const char* a = rec + L::kAqk + (int64_t)(2 * w) * kAqkTile;
+    if (w >= 2)
+      dma_copy<2 * kAqkTile>(stg + oAqk, a, lane);
+    else
+      dma_copy<kAqkTile>(stg + oAqk, a, lane);
   }
 };
 
@@ -122,7 +156,6 @@ struct RecurParams {
   int64_t n_seq_heads_fixed;   // B * H when not packed
   const TableHeader* hdr;
   const SegEntry* segs;
-  const ChunkEntry* chunks;
   const char* records;
   int64_t record_bytes;
   const float* init;
@@ -131,18 +164,22 @@ struct RecurParams {
 };
 
 template <class TI, class TO, int K, int V>
-__global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
-  using PS = typename Prec<TI>::S;
-  using PD = typename Prec<TI>::D;
+__global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p) {
+  using P = Prec<TI>;
+  using PS = typename P::S;
+  using PD = typename P::D;
+  using SG = Stage<TI, K, V>;
   constexpr int NV = V / kVT;
   constexpr int SP = K + 8;        // LDS row pitch of the state operand
   constexpr int DP = kChunk + 8;   // LDS row pitch of the Delta operand
-  constexpr int S_BYTES = LdsPlane<PS>::template bytes<kVT, SP>();
-  constexpr int NCB = K / 16 / 4;  // key-channel blocks of the state per wave
-  __shared__ __align__(16) char s_state[2][S_BYTES];
+  constexpr int NCB = SG::NCB;     // key-channel blocks of the state per wave
+  __shared__ __align__(16) char s_stage[kComputeWaves][SG::kBytes];
+  __shared__ __align__(16) char s_state[LdsPlane<PS>::template bytes<kVT, SP>()];
   __shared__ __align__(16) char s_delta[LdsPlane<PD>::template bytes<kVT, DP>()];
+  __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, gq = lane >> 4;
   const int64_t H = p.H;
 
@@ -156,18 +193,102 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
   if (seq_head >= n_seq_heads) return;
   const int64_t h = seq_head % H, sq = seq_head / H;
 
-  int64_t b, slot, n_chunks, chunk0 = 0;
+  // Chunk n of a sequence starts at token t_begin + 64 n; its record is
+  // (first_chunk + n) * H + h.
+  int64_t b, slot, n_chunks, first_chunk, t_begin, seq_len;
   if (p.packed) {
     const SegEntry se = p.segs[sq];
     b = se.b;
     slot = ((int64_t)se.b * p.n_max + se.local) * H + h;
     n_chunks = se.n_chunks;
-    chunk0 = se.chunk_begin;
+    first_chunk = se.chunk_begin;
+    t_begin = se.t0;
+    seq_len = se.len;
   } else {
     b = sq;
     slot = b * H + h;
     n_chunks = p.nc_fixed;
+    first_chunk = b * p.nc_fixed;
+    t_begin = 0;
+    seq_len = p.T;
   }
+  auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
+
+  // ---- L2 prefetch wave: walks kPrefetchAhead chunks ahead and touches this
+  // workgroup's 1/NV share of each record (every 64-byte segment once), so
+  // the record is in this XCD's L2 when the producers of all NV workgroups
+  // stage it.
+  if (wave == kPrefetchWave) {
+    using L = RecordLayout<TI, K, V>;
+    constexpr int SEGS = (int)(L::kBytes / 64);
+    constexpr int SHARE = (SEGS + NV - 1) / NV;
+    auto prefetch = [&](int64_t n) {
+      const char* r = record(n);
+#pragma unroll
+      for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
+        const int e = i * kWave + lane, seg = j * SHARE + e;
+        if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
+      }
+    };
+    for (int64_t n = 1; n <= kPrefetchAhead && n < n_chunks; ++n) prefetch(n);
+    block_sync();
+    for (int64_t n = 0; n < n_chunks; ++n) {
+      if (n + kPrefetchAhead + 1 < n_chunks) prefetch(n + kPrefetchAhead + 1);
+      block_sync();
+      block_sync();
+      block_sync();
+    }
+    vm_wait<0>();
+    return;
+  }
+
+  // ---- producer waves.  Waits: direct-to-LDS loads of one wave complete in
+  // issue order, so a group has landed once no more than the number of loads
+  // issued after it are outstanding.
+  if (wave >= kProducer0) {
+    const int w = wave - kProducer0;
+    char* stg = s_stage[w];
+    const bool two_aqk = w >= 2;
+    if (n_chunks > 0) {
+      const char* r0 = record(0);
+      SG::issue_w(stg, r0, w, j, lane);
+      SG::issue_kt(stg, r0, w, lane);
+      SG::issue_q(stg, r0, w, lane);
+      vm_wait<0>();
+    }
+    block_sync();
+    for (int64_t n = 0; n < n_chunks; ++n) {
+      const bool more = n + 1 < n_chunks;
+      const char* rn = record(n);
+      const char* rn1 = more ? record(n + 1) : rn;
+      // Delta phase reads Wn/U(n).  Qg/Aqk(n) go out; Kt/Gc(n) must land.
+      if (n > 0) {
+        SG::issue_q(stg, rn, w, lane);
+        if (two_aqk) vm_wait<SG::nQ2>(); else vm_wait<SG::nQ1>();
+      }
+      block_sync();   // B1
+      // State update reads Kt/Gc(n).  Wn/U(n+1) go out; Qg/Aqk(n) must land.
+      if (more) {
+        SG::issue_w(stg, rn1, w, j, lane);
+        vm_wait<SG::nW>();
+      } else {
+        vm_wait<0>();
+      }
+      block_sync();   // B15
+      // Output phase reads Qg/Aqk(n).  Kt/Gc(n+1) go out; Wn/U(n+1) must land.
+      if (more) {
+        SG::issue_kt(stg, rn1, w, lane);
+        vm_wait<SG::nKt>();
+      }
+      block_sync();   // B2
+    }
+    vm_wait<0>();
+    return;
+  }
+
+  // ---- compute waves
+  const int w = wave;
+  const char* stg = s_stage[w];
   TO* out = static_cast<TO*>(p.o);
   const int v0 = kVT * j;
 
@@ -181,94 +302,72 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
     for (int i = 0; i < 4; ++i)
       st[u][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
     float x[4] = {st[u][0], st[u][1], st[u][2], st[u][3]};
-    LdsPlane<PS>::template write4<kVT, SP>(s_state[0], m, c0, x);
+    LdsPlane<PS>::template write4<kVT, SP>(s_state, m, c0, x);
   }
-  __syncthreads();
+  block_sync();
 
-  // Chunk n's record index, first token and length.
-  auto chunk_info = [&](int64_t n, int64_t& rec_idx, int64_t& t0, int& len) {
-    if (p.packed) {
-      const ChunkEntry ce = p.chunks[chunk0 + n];
-      rec_idx = (chunk0 + n) * H + h;
-      t0 = ce.t0;
-      len = ce.len;
-    } else {
-      rec_idx = (b * p.nc_fixed + n) * H + h;
-      t0 = n * kChunk;
-      len = (int)min<int64_t>(kChunk, p.T - t0);
-    }
-  };
-
-  // The operands of chunk n + 1 (clamped to the last chunk) are loaded while
-  // chunk n computes; `cur` is loop-carried, so those loads cannot sink.
-  ChunkOps<TI, K, V> cur;
-  int64_t t0 = 0, t0n = 0;
-  int len = 0, lenn = 0;
-  int buf = 0;
-  if (n_chunks > 0) {
-    int64_t rec_idx;
-    chunk_info(0, rec_idx, t0, len);
-    cur.load(p.records + rec_idx * p.record_bytes, w, j, lane, gq);
-  }
   for (int64_t n = 0; n < n_chunks; ++n) {
-    ChunkOps<TI, K, V> nxt;
-    {
-      int64_t rec_idx;
-      chunk_info(n + 1 < n_chunks ? n + 1 : n, rec_idx, t0n, lenn);
-      nxt.load(p.records + rec_idx * p.record_bytes, w, j, lane, gq);
-    }
+    const int64_t t0 = t_begin + n * kChunk;
+    const int len = (int)min<int64_t>(kChunk, seq_len - n * kChunk);
 
-    // Delta = U - W S for tokens 16w..16w+15
-    f32x4 d = cur.u;
+    // Delta = U - W S for tokens 16w..16w+15; the S operand stays in
+    // registers for the output phase.
+    PS sf[K / 32];
+    typename P::W wn[K / 32];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) {
-      const PS s = LdsPlane<PS>::template read<kVT, SP>(s_state[buf], m, kb, gq);
-      mma(d, cur.wn[kb], s);
+      wn[kb].load(stg + SG::oWn + kb * tile_bytes<typename P::W>(), lane);
+      sf[kb] = LdsPlane<PS>::template read<kVT, SP>(s_state, m, kb, gq);
     }
+    f32x4 d = reinterpret_cast<const f32x4*>(stg + SG::oU)[lane];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) mma(d, wn[kb], sf[kb]);
     {
       float x[4] = {d[0], d[1], d[2], d[3]};
       LdsPlane<PD>::template write4<kVT, DP>(s_delta, m, 16 * w + 4 * gq, x);
     }
-    __syncthreads();
+    block_sync();   // B1
 
-    // S <- diag(exp(G_C)) S + Kt^T Delta
+    // S <- diag(exp(G_C)) S + Kt^T Delta; the Delta operand stays in
+    // registers for the output phase.
+    PD dd[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dd[kb] = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
 #pragma unroll
     for (int u = 0; u < NCB; ++u) {
       const int cb = w * NCB + u, c0 = 16 * cb + 4 * gq;
+      const f32x4 gc = reinterpret_cast<const f32x4*>(stg + SG::oGc)[4 * u + gq];
+      typename P::Kt kt[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st[u][i] *= cur.gc[u][i];
+      for (int kb = 0; kb < 2; ++kb) kt[kb].load(stg + SG::oKt + (u * 2 + kb) * tile_bytes<typename P::Kt>(), lane);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const PD dd = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
-        mma(st[u], cur.kt[u][kb], dd);
-      }
+      for (int i = 0; i < 4; ++i) st[u][i] *= gc[i];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) mma(st[u], kt[kb], dd[kb]);
       float x[4] = {st[u][0], st[u][1], st[u][2], st[u][3]};
-      LdsPlane<PS>::template write4<kVT, SP>(s_state[buf ^ 1], m, c0, x);
+      LdsPlane<PS>::template write4<kVT, SP>(s_state, m, c0, x);
     }
+    block_sync();   // B15
 
     // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
+    typename P::Q qg[K / 32], aq[2];
+#pragma unroll
+    for (int kb = 0; kb < K / 32; ++kb) qg[kb].load(stg + SG::oQg + kb * tile_bytes<typename P::Q>(), lane);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= w / 2) aq[kb].load(stg + SG::oAqk + kb * SG::kAqkTile, lane);
     f32x4 ov = {0, 0, 0, 0};
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) {
-      const PS s = LdsPlane<PS>::template read<kVT, SP>(s_state[buf], m, kb, gq);
-      mma(ov, cur.qg[kb], s);
-    }
+    for (int kb = 0; kb < K / 32; ++kb) mma(ov, qg[kb], sf[kb]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb > w / 2) continue;
-      const PD dd = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
-      mma(ov, cur.aqk[kb], dd);
-    }
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= w / 2) mma(ov, aq[kb], dd[kb]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * gq + i;
       if (r < len) store_out(out, ((b * p.T + t0 + r) * H + h) * V + v0 + m, ov[i]);
     }
-    __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    t0 = t0n;
-    len = lenn;
+    block_sync();   // B2
   }
 
   if (p.fin) {
@@ -284,13 +383,13 @@ __global__ __launch_bounds__(kThreads) void kda_recur_kernel(RecurParams p) {
 template <class TI, class TO, int K, int V>
 hipError_t launch_recur_t(const CallArgs& a) {
   constexpr int NV = V / kVT;
-  RecurParams p{a.B, a.T, a.H, a.nc_fixed, a.n_max > 0, a.n_max, a.B * a.H, a.hdr, a.segs, a.chunks,
+  RecurParams p{a.B, a.T, a.H, a.nc_fixed, a.n_max > 0, a.n_max, a.B * a.H, a.hdr, a.segs,
                 a.records, a.record_bytes, a.init, a.fin, a.o};
   const int64_t seq_heads = (a.n_max > 0 ? a.smax : a.B) * a.H;
   if (seq_heads <= 0) return hipSuccess;
   const int64_t groups = (seq_heads + 7) / 8;
   const int64_t grid = groups * 8 * NV;
-  hipLaunchKernelGGL((kda_recur_kernel<TI, TO, K, V>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream, p);
+  hipLaunchKernelGGL((kda_recur_kernel<TI, TO, K, V>), dim3((unsigned)grid), dim3(kRecurThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 
