@@ -18,8 +18,10 @@ library's launch observer).  Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -37,8 +39,51 @@ METRIC = "KDA fwd ms & tokens/s, B=1 H=32 T=8192 K=V=128 bf16; % MFMA/HBM roofli
 TPU_V7X_FIXED_MS = 1.870        # pages' fastest H=32/T=8192 fixed forward (context, another machine)
 
 
+KERNEL_SOURCES = {   # sources a kernel's code depends on (its traffic figures go stale when they change)
+    "kda_intra": ["kda_intra.hip", "kda_common.h", "kda_launch.h"],
+    "kda_recur": ["kda_recur.hip", "kda_common.h", "kda_launch.h"],
+    "kda_prep": ["kda_prep.hip", "kda_common.h", "kda_launch.h"],
+}
+COPY_CALIBRATION_MIB = 512
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "gated_delta_rule_33_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this kernel
+    and workload, if it was taken on the current source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    src = re.search(r"^source_sha256: *(\S+)", text, re.M)
+    tot = re.search(r"^hbm_bytes_per_launch: *([0-9.eE+]+)", text, re.M)
+    if not src or not tot or src.group(1) != kernel_source_hash(kernel):
+        return None
+    return float(tot.group(1))
+
+
+def copy_calibration():
+    """One plain device copy of known size (read and write COPY_CALIBRATION_MIB
+    each), for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiled run."""
+    import torch
+    n = COPY_CALIBRATION_MIB * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)   # reads 4n bytes, writes 4n bytes
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def algorithmic(w, out_bytes: int):
@@ -160,6 +205,8 @@ def main():
     ap.add_argument("--extra", default="bf16_b1_h32_t8192_packed25_l2",
                     help="second workload timed and reported under 'extra' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help=f"run one {COPY_CALIBRATION_MIB} MiB elementwise copy first (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -172,6 +219,9 @@ def main():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
     w = WORKLOADS[args.workload]
+    if args.calibrate_copy:
+        log(f"[bench] calibration copy of {COPY_CALIBRATION_MIB} MiB")
+        copy_calibration()
     log(f"[bench] {w.name}: warmup {args.warmup}, steps {args.steps}")
     res = time_workload(w, args.steps, args.warmup)
     s = summarize(w, res, out_bytes=4)
@@ -188,7 +238,8 @@ def main():
 
     dom = s["kernels"][s["dominant"]]
     roofline = {"bound": "hbm", "kernel": s["dominant"], "achieved": dom["achieved_gbps"], "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(dom["achieved_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(dom["achieved_gbps"] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(s["dominant"], w.name), "alg_bytes": dom["alg_bytes"],
                 "mfma_tflops": dom["achieved_tflops"],
                 "mfma_frac": round(dom["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
     extra = {"path": {"alg_bytes": s["path_bytes"], "alg_flops": s["path_flops"],
