@@ -112,6 +112,14 @@ struct FragB {
   __device__ __forceinline__ void store(void* tile, int lane) const {
     reinterpret_cast<bf16x8*>(tile)[lane] = v;
   }
+  // Elements 4 half .. 4 half + 3 of this lane's fragment in a tile (the
+  // other half is written by whoever holds it).
+  __device__ static __forceinline__ void store_half(void* tile, int lane, int half, const float x[4]) {
+    bf16x4 h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) h[j] = to_bf16(x[j]);
+    reinterpret_cast<bf16x4*>(tile)[2 * lane + half] = h;
+  }
 };
 
 struct FragP {
@@ -154,6 +162,9 @@ struct FragF {
     f32x4* t = reinterpret_cast<f32x4*>(tile);
     t[2 * lane] = a;
     t[2 * lane + 1] = b;
+  }
+  __device__ static __forceinline__ void store_half(void* tile, int lane, int half, const float x[4]) {
+    reinterpret_cast<f32x4*>(tile)[2 * lane + half] = f32x4{x[0], x[1], x[2], x[3]};
   }
 };
 

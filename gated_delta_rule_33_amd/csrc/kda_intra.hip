@@ -30,6 +30,8 @@ namespace kda {
 namespace {
 
 constexpr float kSpanMax = 64.f;
+constexpr int kIntraWaves = 8;                       // two per SIMD
+constexpr int kIntraThreads = kIntraWaves * kWave;
 
 // Rows of W elements kept in LDS with their 16-byte chunks XOR-swizzled by the
 // row index, so that 16 lanes reading one chunk of 16 different rows hit 16
@@ -59,7 +61,14 @@ struct IntraSmem {
   float beta[kChunk];
   float M[kChunk * kMP];
   float nk[kChunk];
-  float part[kThreads];
+  float part[kIntraThreads];
+  // Partial A / Aqk tiles of the upper key-channel half: 10 (row block, column
+  // block) tiles x {A, Aqk} x 64 lanes x 4.  They reuse the q buffer (dead by
+  // then) when it is large enough (fp32 inputs with K = 128), else their own.
+  static constexpr int kRedFloats = 10 * 2 * kWave * 4;
+  static constexpr bool kRedInQ = sizeof(TI) * kChunk * K >= sizeof(float) * kRedFloats;
+  float red[kRedInQ ? 1 : kRedFloats];
+  __device__ float* red_buf() { return kRedInQ ? reinterpret_cast<float*>(q) : red; }
 };
 
 // Four consecutive elements as floats.
@@ -96,7 +105,7 @@ __device__ __forceinline__ void issue_rows(TI* lds, const TI* src, int64_t row_s
   using S = SwzRows<TI, W>;
   constexpr int BLOCKS = kChunk * S::NCH / kWave;   // 1 KB blocks
 #pragma unroll
-  for (int bi = w; bi < BLOCKS; bi += kThreads / kWave) {
+  for (int bi = w; bi < BLOCKS; bi += kIntraWaves) {
     const int L = bi * kWave + lane, r = L / S::NCH, pch = L % S::NCH, cv = pch ^ (r % S::NCH);
     if (r < len)
       dma16(lds + bi * kWave * S::E, src + r * row_stride + cv * S::E);
@@ -105,6 +114,15 @@ __device__ __forceinline__ void issue_rows(TI* lds, const TI* src, int64_t row_s
 
 // Wait for every outstanding vector memory operation of this wave.
 __device__ __forceinline__ void wait_loads() { vm_wait<0>(); }
+
+// A copy of x the compiler cannot see through.  Per-lane LDS addresses derived
+// from it inside the item loop are recomputed per item instead of being
+// hoisted out of the loop, where they would all stay live and spill.
+__device__ __forceinline__ int opaque(int x) {
+  int y;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
+  return y;
+}
 
 // 16-deep fp32 product on the matrix cores: element s of lane group g holds k = 4g + s.
 __device__ __forceinline__ void mma16_f32(f32x4& c, const float a[4], const float b[4]) {
@@ -152,7 +170,7 @@ __device__ __forceinline__ ItemInfo item_info(const IntraParams& p, int64_t item
 // buffers), q once the current q is dead (after the A products), v into the g
 // buffer once g has been summed.
 template <class TI, int K, int V>
-__global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
+__global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams p) {
   using S = IntraSmem<TI, K, V>;
   using SK = SwzRows<TI, K>;
   using SV = SwzRows<TI, V>;
@@ -167,8 +185,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
   extern __shared__ __align__(16) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int m = lane & 15, gq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Row block of the intra-chunk products and half of the key channels this
+  // wave takes: waves s and s + 4 share SIMD s and get row blocks s and 3 - s,
+  // so every SIMD carries the same share of the triangle.
+  const int R = w < 4 ? w : 7 - w, chalf = w / 4;
   const TI* gq_ = static_cast<const TI*>(p.q);
   const TI* gk_ = static_cast<const TI*>(p.k);
   const TI* gv_ = static_cast<const TI*>(p.v);
@@ -212,6 +234,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
     char* rec = p.records + item * p.record_bytes;
     TI* kbuf = sm.k[cb];
     TI* gvbuf = sm.gv[cb];
+    const int tid = opaque(threadIdx.x), lane = tid & 63;
+    const int m = lane & 15, gq = lane >> 4;
 
     // ---- this item's q, k, g, beta have landed; zero the rows past the chunk
     wait_loads();
@@ -219,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
     if (w == 0) sm.beta[lane] = lane < len ? ld1(&beta_next) : 0.f;   // zero past the chunk
     if (S::kDB && has_next) issue_kgb(nxt, cb ^ 1);
     if (len < kChunk) {
-      for (int e = tid; e < (kChunk - len) * K; e += kThreads) {
+      for (int e = tid; e < (kChunk - len) * K; e += kIntraThreads) {
         const int r = len + e / K, c = e % K;
         sm.q[SK::idx(r, c)] = TI(0);
         kbuf[SK::idx(r, c)] = TI(0);
@@ -230,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
 
     // ---- running sum of g over the chunk, per channel
     {
-      constexpr int PARTS = kThreads / K, RP = kChunk / PARTS;
+      constexpr int PARTS = kIntraThreads / K, RP = kChunk / PARTS;
       const int c = tid % K, part = tid / K, r0 = part * RP;
       float gcol[RP];
 #pragma unroll
@@ -247,8 +271,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
     block_sync();   // g consumed: the buffer now receives v
     issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
 
-    // ---- this wave's rows: norms and its block's span
-    const int R = w, f = 16 * R, r_own = f + m;
+    // ---- this wave's rows: norms and its block's span (both waves of a row block)
+    const int f = 16 * R, r_own = f + m;
     float nqr = 1.f, nkr = 1.f;
     if (p.l2norm) {
       float sq = 0.f, sk = 0.f;
@@ -265,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
       nqr = 1.f / sqrtf(sq + 1e-6f);
       nkr = 1.f / sqrtf(sk + 1e-6f);
     }
-    if (gq == 0) sm.nk[r_own] = nkr;
+    if (gq == 0 && chalf == 0) sm.nk[r_own] = nkr;
     float span = 0.f;
     for (int c = lane; c < K; c += kWave) span = fmaxf(span, sm.G[f * S::kGP + c] - sm.G[(f + 15) * S::kGP + c]);
 #pragma unroll
@@ -273,14 +297,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
     const bool diag_split = span <= kSpanMax;
     block_sync();   // nk visible
 
-    // ---- A and Aqk for row block R = w: tiles (I, R) hold D[i][r], I <= R
+    // ---- A and Aqk for row block R over key-channel half chalf: tiles (I, R)
+    //      hold D[i][r], I <= R; the two halves are summed through LDS below
     f32x4 accKK[4], accQK[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) { accKK[I] = f32x4{0, 0, 0, 0}; accQK[I] = f32x4{0, 0, 0, 0}; }
     {
       const int r = r_own;
-#pragma unroll 2
-      for (int kb = 0; kb < K / 32; ++kb) {
+      constexpr int KBH = K / 64;   // 32-channel slabs per half
+#pragma unroll
+      for (int kbi = 0; kbi < KBH; ++kbi) {
+        const int kb = chalf * KBH + kbi;
         float gr[8], gf[8], kx[8], qx[8], xk[8], xq[8];
         row8f(sm.G + r * S::kGP, kb, gq, gr);
         row8f(sm.G + f * S::kGP, kb, gq, gf);
@@ -301,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
           for (int j = 0; j < 8; ++j) xg[j] = p.scale * qx[j] * nqr * __expf(gr[j]);
           PQ qf;
           qf.set(xg);
-          qf.store(rec + L::kQg + (int64_t)(w * (K / 32) + kb) * tile_bytes<PQ>(), lane);
+          qf.store(rec + L::kQg + (int64_t)(R * (K / 32) + kb) * tile_bytes<PQ>(), lane);
         }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
@@ -327,7 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
           float sk_ = 0.f, sq_ = 0.f;
           if (i <= r) {
             const float nki = sm.nk[i];
-            for (int c = 0; c < K; ++c) {
+            for (int c = chalf * (K / 2); c < (chalf + 1) * (K / 2); ++c) {
               const float e = __expf(sm.G[r * S::kGP + c] - sm.G[i * S::kGP + c]);
               const float kk = ld1(kbuf + SK::idx(i, c)) * nki * e;
               sk_ += ld1(kbuf + SK::idx(r, c)) * nkr * kk;
@@ -339,37 +366,82 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
             if (I == R) { accKK[I][ii] = sk_; accQK[I][ii] = sq_; }
         }
       }
-      // A[r][i] = beta_r * D[i][r] (i < r), stored transposed above the diagonal of M.
-      const float br = sm.beta[r];
+    }
+    // ---- the upper channel half hands its partial tiles to the lower half
+    {
+      float* red = sm.red_buf();
+      const int slot0 = R * (R + 1) / 2;   // tiles (R, 0..R)
+      block_sync();   // everyone is done with q (fp32 inputs reuse it here)
+      if (chalf == 1) {
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        if (I > R) continue;
+        for (int I = 0; I < 4; ++I) {
+          if (I > R) continue;
+          reinterpret_cast<f32x4*>(red)[((slot0 + I) * 2 + 0) * kWave + lane] = accKK[I];
+          reinterpret_cast<f32x4*>(red)[((slot0 + I) * 2 + 1) * kWave + lane] = accQK[I];
+        }
+      }
+      block_sync();
+      if (chalf == 0) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int i = 16 * I + 4 * gq + ii;
-          if (i < r) sm.M[i * S::kMP + r] = br * accKK[I][ii];
-          accQK[I][ii] = (i <= r) ? p.scale * accQK[I][ii] : 0.f;
+        for (int I = 0; I < 4; ++I) {
+          if (I > R) continue;
+          accKK[I] += reinterpret_cast<const f32x4*>(red)[((slot0 + I) * 2 + 0) * kWave + lane];
+          accQK[I] += reinterpret_cast<const f32x4*>(red)[((slot0 + I) * 2 + 1) * kWave + lane];
+        }
+        // A[r][i] = beta_r * D[i][r] (i < r), stored transposed above the diagonal of M.
+        const int r = r_own;
+        const float br = sm.beta[r];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (I > R) continue;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 16 * I + 4 * gq + ii;
+            if (i < r) sm.M[i * S::kMP + r] = br * accKK[I][ii];
+            accQK[I][ii] = (i <= r) ? p.scale * accQK[I][ii] : 0.f;
+          }
+        }
+        // scale * Aqk, rows of block R: the D[i][r] tiles (I, R) are the operand layout
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          float x[8];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            x[ii] = (2 * kb <= R) ? accQK[2 * kb][ii] : 0.f;
+            x[4 + ii] = (2 * kb + 1 <= R) ? accQK[2 * kb + 1][ii] : 0.f;
+          }
+          PQ af;
+          af.set(x);
+          af.store(rec + L::kAqk + (int64_t)(R * 2 + kb) * tile_bytes<PQ>(), lane);
         }
       }
     }
-    // ---- scale * Aqk, rows of block w: the D[i][r] tiles (I, w) are the operand layout
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      float x[8];
-#pragma unroll
-      for (int ii = 0; ii < 4; ++ii) {
-        x[ii] = (2 * kb <= R) ? accQK[2 * kb][ii] : 0.f;
-        x[4 + ii] = (2 * kb + 1 <= R) ? accQK[2 * kb + 1][ii] : 0.f;
-      }
-      PQ af;
-      af.set(x);
-      af.store(rec + L::kAqk + (int64_t)(w * 2 + kb) * tile_bytes<PQ>(), lane);
-    }
-    block_sync();   // q is dead: the next item's q streams in
+    block_sync();   // q and the partial tiles are dead: the next item's q streams in
     if (has_next) issue_q(nxt);
 
-    // ---- T = (I + A)^-1, diagonal 16x16 blocks first (wave w: block w)
-    if (lane < 16) {
+    // ---- Kt = (k * exp(G_C - G))^T as operand tiles [c-block][token k-tile];
+    //      independent of T, so waves 4-7 build them while waves 0-3 solve
+    constexpr int NKT = (K / 16) * 2;
+    auto kt_tile = [&](int t) {
+      const int cbk = t >> 1, kb = t & 1, c = 16 * cbk + m;
+      const float gc = sm.G[(kChunk - 1) * S::kGP + c];
+      float x[8], kv8[8], g8[8], n8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {   // all reads first
+        const int r = 32 * kb + kperm(gq, j);
+        kv8[j] = ld1(kbuf + SK::idx(r, c));
+        g8[j] = sm.G[r * S::kGP + c];
+        n8[j] = sm.nk[r];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = kv8[j] * n8[j] * __expf(gc - g8[j]);
+      PK fr;
+      fr.set(x);
+      fr.store(rec + L::kKt + (int64_t)(cbk * 2 + kb) * tile_bytes<PK>(), lane);
+    };
+
+    // ---- T = (I + A)^-1, diagonal 16x16 blocks first (wave w < 4: block w)
+    if (w < 4 && lane < 16) {
       const int j = lane;
       float t[16], acc[16];
 #pragma unroll
@@ -383,11 +455,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         if (r >= j) sm.M[(f + r) * S::kMP + f + j] = t[r];
+    } else if (w >= 4) {
+      for (int t = w - 4; t < NKT / 2; t += 4) kt_tile(t);
     }
     block_sync();
     // ---- off-diagonal blocks, one block column per wave, kept in registers:
     //      T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI for R = I+1 .. 3, I = w
-    {
+    if (w < 4) {
       const int I = w;
       f32x4 tcol[4];   // T_JI for J > I, accumulator layout (= operand layout with k = rows)
 #pragma unroll
@@ -422,30 +496,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
         }
         tcol[RR] = res;
       }
+    } else {
+      for (int t = NKT / 2 + w - 4; t < NKT; t += 4) kt_tile(t);
     }
     block_sync();
 
-    // ---- Kt = (k * exp(G_C - G))^T as operand tiles [c-block][token k-tile]
-    for (int t = w; t < (K / 16) * 2; t += 4) {
-      const int cbk = t >> 1, kb = t & 1, c = 16 * cbk + m;
-      const float gc = sm.G[(kChunk - 1) * S::kGP + c];
-      float x[8], kv8[8], g8[8], n8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {   // all reads first
-        const int r = 32 * kb + kperm(gq, j);
-        kv8[j] = ld1(kbuf + SK::idx(r, c));
-        g8[j] = sm.G[r * S::kGP + c];
-        n8[j] = sm.nk[r];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = kv8[j] * n8[j] * __expf(gc - g8[j]);
-      PK fr;
-      fr.set(x);
-      fr.store(rec + L::kKt + (int64_t)(cbk * 2 + kb) * tile_bytes<PK>(), lane);
-    }
-    block_sync();
     // exp(G) in place of G from here on.
-    for (int e4 = tid; e4 < kChunk * K / 4; e4 += kThreads) {
+    for (int e4 = tid; e4 < kChunk * K / 4; e4 += kIntraThreads) {
       const int r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
       f32x4 x = ld4(sm.G + r * S::kGP + c);
 #pragma unroll
@@ -471,73 +528,59 @@ __global__ __launch_bounds__(kThreads, 1) void kda_intra_kernel(IntraParams p) {
       return fr;
     };
 
-    // ---- -W: W^T tiles D[c][r] for the key-channel blocks cb = 2w, 2w+1 and every row block
-    if (2 * w < K / 16) {
-      PX xf[2][2];
+    // ---- -W: W^T tiles D[c][r] for key-channel block cb = w and every row
+    //      block; a W operand tile spans two channel blocks, so each wave
+    //      writes its half of every lane's fragment
+    if (w < K / 16) {
+      PX xf[2];
+      const int c = 16 * w + m;
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int c = 16 * (2 * w + hh) + m;
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 32 * kb + kperm(gq, j);
-            x[j] = sm.beta[i] * ld1(kbuf + SK::idx(i, c)) * sm.nk[i] * sm.G[i * S::kGP + c];
-          }
-          xf[hh][kb].set(x);
+        for (int j = 0; j < 8; ++j) {
+          const int i = 32 * kb + kperm(gq, j);
+          x[j] = sm.beta[i] * ld1(kbuf + SK::idx(i, c)) * sm.nk[i] * sm.G[i * S::kGP + c];
         }
+        xf[kb].set(x);
       }
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        f32x4 acc2[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > rb / 2) continue;
-          const PT tf = t_frag(rb, kb, false);
-          mma(acc2[0], xf[0][kb], tf);
-          mma(acc2[1], xf[1][kb], tf);
+          mma(acc, xf[kb], t_frag(rb, kb, false));
         }
-        float wv[8];
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) { wv[ii] = -acc2[0][ii]; wv[4 + ii] = -acc2[1][ii]; }
-        PW wf;
-        wf.set(wv);
-        wf.store(rec + L::kWn + (int64_t)(rb * (K / 32) + w) * tile_bytes<PW>(), lane);
+        const float wv[4] = {-acc[0], -acc[1], -acc[2], -acc[3]};
+        PW::store_half(rec + L::kWn + (int64_t)(rb * (K / 32) + w / 2) * tile_bytes<PW>(), lane, w & 1, wv);
       }
     }
 
-    // ---- U = T diag(beta) V for value blocks vb = 2w, 2w+1: v has landed in the g buffer
+    // ---- U = T diag(beta) V for value block vb = w: v has landed in the g buffer
     wait_loads();
     block_sync();
     if (len < kChunk)
-      for (int e = tid; e < (kChunk - len) * V; e += kThreads) gvbuf[SV::idx(len + e / V, e % V)] = TI(0);
+      for (int e = tid; e < (kChunk - len) * V; e += kIntraThreads) gvbuf[SV::idx(len + e / V, e % V)] = TI(0);
     block_sync();
-    if (2 * w < V / 16) {
-      PV vf[2][2];
+    if (w < V / 16) {
+      PV vf[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+      for (int kb = 0; kb < 2; ++kb) {
+        float x[8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = ld1(gvbuf + SV::idx(32 * kb + kperm(gq, j), 16 * (2 * w + hh) + m));
-          vf[hh][kb].set(x);
-        }
+        for (int j = 0; j < 8; ++j) x[j] = ld1(gvbuf + SV::idx(32 * kb + kperm(gq, j), 16 * w + m));
+        vf[kb].set(x);
       }
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) {
-        f32x4 acc2[2] = {f32x4{0, 0, 0, 0}, f32x4{0, 0, 0, 0}};
+        f32x4 acc = {0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > rb / 2) continue;
-          const PT tb = t_frag(rb, kb, true);
-          mma(acc2[0], tb, vf[0][kb]);
-          mma(acc2[1], tb, vf[1][kb]);
+          mma(acc, t_frag(rb, kb, true), vf[kb]);
         }
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          reinterpret_cast<f32x4*>(rec + L::kU)[(rb * (V / 16) + 2 * w + hh) * kWave + lane] = acc2[hh];
+        reinterpret_cast<f32x4*>(rec + L::kU)[(rb * (V / 16) + w) * kWave + lane] = acc;
       }
     }
     block_sync();   // k and the g/v buffer are free
@@ -570,7 +613,7 @@ hipError_t launch_intra_t(const CallArgs& a) {
   const int64_t items = (a.n_max > 0 ? a.cmax : a.B * a.nc_fixed) * a.H;
   if (items <= 0) return hipSuccess;
   const unsigned grid = (unsigned)std::min<int64_t>(items, cu_count());
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), smem, a.stream, p);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kIntraThreads), smem, a.stream, p);
   return hipGetLastError();
 }
 
