@@ -60,8 +60,8 @@ struct IntraSmem {
   float G[kChunk * kGP];
   float beta[kChunk];
   float M[kChunk * kMP];
-  float nk[kChunk];
-  float part[kIntraThreads];
+  alignas(16) float nk[kChunk];
+  float part[2 * kIntraThreads];
   // Partial A / Aqk tiles of the upper key-channel half: 10 (row block, column
   // block) tiles x {A, Aqk} x 64 lanes x 4.  They reuse the q buffer (dead by
   // then) when it is large enough (fp32 inputs with K = 128), else their own.
@@ -79,6 +79,17 @@ __device__ __forceinline__ f32x4 ld4(const uint16_t* p) {
                __uint_as_float(v.y & 0xffff0000u)};
 }
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
+// Two consecutive elements (even offset) as floats.
+__device__ __forceinline__ void ld2(const float* p, float& a, float& b) {
+  const float2 v = *reinterpret_cast<const float2*>(p);
+  a = v.x;
+  b = v.y;
+}
+__device__ __forceinline__ void ld2(const uint16_t* p, float& a, float& b) {
+  const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
+  a = __uint_as_float(v << 16);
+  b = __uint_as_float(v & 0xffff0000u);
+}
 __device__ __forceinline__ float ld1(const uint16_t* p) { return bits_to_f32(*p); }
 
 // The eight elements of a swizzled row at the fragment k-order of k-tile kb.
@@ -253,20 +264,28 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     block_sync();
 
     // ---- running sum of g over the chunk, per channel
-    {
-      constexpr int PARTS = kIntraThreads / K, RP = kChunk / PARTS;
-      const int c = tid % K, part = tid / K, r0 = part * RP;
-      float gcol[RP];
+    {   // two channels per thread, rows in PARTS parts of RP
+      constexpr int PAIRS = K / 2, PARTS = kIntraThreads / PAIRS, RP = kChunk / PARTS;
+      const int c = 2 * (tid % PAIRS), part = tid / PAIRS, r0 = part * RP;
+      float g0[RP], g1[RP];
 #pragma unroll
-      for (int i = 0; i < RP; ++i) gcol[i] = ld1(gvbuf + SK::idx(r0 + i, c));   // all reads in flight
+      for (int i = 0; i < RP; ++i) ld2(gvbuf + SK::idx(r0 + i, c), g0[i], g1[i]);   // all reads in flight
 #pragma unroll
-      for (int i = 1; i < RP; ++i) gcol[i] += gcol[i - 1];
-      sm.part[part * K + c] = gcol[RP - 1];
+      for (int i = 1; i < RP; ++i) {
+        g0[i] += g0[i - 1];
+        g1[i] += g1[i - 1];
+      }
+      *reinterpret_cast<float2*>(&sm.part[part * K + c]) = float2{g0[RP - 1], g1[RP - 1]};
       block_sync();
-      float off = 0.f;
-      for (int pp = 0; pp < part; ++pp) off += sm.part[pp * K + c];
+      float o0 = 0.f, o1 = 0.f;
+      for (int pp = 0; pp < part; ++pp) {
+        const float2 v = *reinterpret_cast<const float2*>(&sm.part[pp * K + c]);
+        o0 += v.x;
+        o1 += v.y;
+      }
 #pragma unroll
-      for (int i = 0; i < RP; ++i) sm.G[(r0 + i) * S::kGP + c] = gcol[i] + off;
+      for (int i = 0; i < RP; ++i)
+        *reinterpret_cast<float2*>(&sm.G[(r0 + i) * S::kGP + c]) = float2{g0[i] + o0, g1[i] + o1};
     }
     block_sync();   // g consumed: the buffer now receives v
     issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
@@ -298,12 +317,15 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     block_sync();   // nk visible
 
     // ---- A and Aqk for row block R over key-channel half chalf: tiles (I, R)
-    //      hold D[i][r], I <= R; the two halves are summed through LDS below
+    //      hold D[i][r], I <= R; the two halves are summed through LDS below.
+    //      The per-row L2-norm factors multiply the 16x16 results, not the
+    //      operands.
     f32x4 accKK[4], accQK[4];
 #pragma unroll
     for (int I = 0; I < 4; ++I) { accKK[I] = f32x4{0, 0, 0, 0}; accQK[I] = f32x4{0, 0, 0, 0}; }
     {
       const int r = r_own;
+      const float sqr = p.scale * nqr;
       constexpr int KBH = K / 64;   // 32-channel slabs per half
 #pragma unroll
       for (int kbi = 0; kbi < KBH; ++kbi) {
@@ -316,8 +338,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float e = __expf(gr[j] - gf[j]);
-          xk[j] = kx[j] * nkr * e;
-          xq[j] = qx[j] * nqr * e;
+          xk[j] = kx[j] * e;
+          xq[j] = qx[j] * e;
         }
         PA fkr, fqr;
         fkr.set(xk);
@@ -325,7 +347,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
         {   // scale * q * exp(G) for this wave's rows: the output's inter-chunk operand
           float xg[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) xg[j] = p.scale * qx[j] * nqr * __expf(gr[j]);
+          for (int j = 0; j < 8; ++j) xg[j] = sqr * qx[j] * __expf(gr[j]);
           PQ qf;
           qf.set(xg);
           qf.store(rec + L::kQg + (int64_t)(R * (K / 32) + kb) * tile_bytes<PQ>(), lane);
@@ -334,16 +356,27 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
         for (int I = 0; I < 4; ++I) {
           if (I > R || (I == R && !diag_split)) continue;
           const int i = 16 * I + m;
-          const float nki = sm.nk[i];
           float gi[8], ki[8], xc[8];
           row8f(sm.G + i * S::kGP, kb, gq, gi);
           row8<TI, K>(kbuf, i, kb, gq, ki);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) xc[j] = ki[j] * nki * __expf(gf[j] - gi[j]);
+          for (int j = 0; j < 8; ++j) xc[j] = ki[j] * __expf(gf[j] - gi[j]);
           PA fkc;
           fkc.set(xc);
           mma(accKK[I], fkc, fkr);
           mma(accQK[I], fkc, fqr);
+        }
+      }
+      if (p.l2norm) {   // D[i][r] * nk_i * (nk_r | nq_r); lane: column r, rows i = 16I + 4gq + ii
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (I > R) continue;
+          const f32x4 nki = ld4(sm.nk + 16 * I + 4 * gq);
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            accKK[I][ii] *= nki[ii] * nkr;
+            accQK[I][ii] *= nki[ii] * nqr;
+          }
         }
       }
       if (!diag_split) {
@@ -501,17 +534,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     }
     block_sync();
 
-    // exp(G) in place of G from here on.
-    for (int e4 = tid; e4 < kChunk * K / 4; e4 += kIntraThreads) {
-      const int r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
-      f32x4 x = ld4(sm.G + r * S::kGP + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = __expf(x[i]);
-      *reinterpret_cast<f32x4*>(sm.G + r * S::kGP + c) = x;
-    }
-    block_sync();
-    if (tid < K) reinterpret_cast<float*>(rec + L::kGc)[tid] = sm.G[(kChunk - 1) * S::kGP + tid];
-
     // ---- T fragments (row r of block rb, k = i): T and T diag(beta); T[r][i] = 0 for i > r
     auto t_frag = [&](int rb, int kb, bool with_beta) {
       const int r = 16 * rb + m;
@@ -527,6 +549,38 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       fr.set(x);
       return fr;
     };
+    // With bf16 inputs the twelve fragments W and U use ((rb, kb) with
+    // kb <= rb / 2, without and with beta) are built once, into the dead
+    // partial-tile buffer, instead of by every wave.
+    constexpr bool kTShared = !S::kRedInQ && 12 * tile_bytes<PT>() <= S::kRedFloats * 4;
+    char* tfr = reinterpret_cast<char*>(sm.red_buf());
+    auto t_index = [](int rb, int kb, bool with_beta) { return (with_beta ? 6 : 0) + (rb < 2 ? rb : 2 * rb - 2) + kb; };
+    auto t_get = [&](int rb, int kb, bool with_beta) {
+      if constexpr (kTShared) {
+        PT f;
+        f.load(tfr + t_index(rb, kb, with_beta) * tile_bytes<PT>(), lane);
+        return f;
+      } else {
+        return t_frag(rb, kb, with_beta);
+      }
+    };
+
+    // exp(G) in place of G from here on; the shared T fragments alongside.
+    for (int e4 = tid; e4 < kChunk * K / 4; e4 += kIntraThreads) {
+      const int r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
+      f32x4 x = ld4(sm.G + r * S::kGP + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = __expf(x[i]);
+      *reinterpret_cast<f32x4*>(sm.G + r * S::kGP + c) = x;
+    }
+    if constexpr (kTShared) {
+      for (int tt = w; tt < 12; tt += kIntraWaves) {
+        const int pr = tt % 6, rb = pr < 2 ? pr : (pr + 2) / 2, kb = pr < 2 ? 0 : pr & 1;
+        t_frag(rb, kb, tt >= 6).store(tfr + tt * tile_bytes<PT>(), lane);
+      }
+    }
+    block_sync();
+    if (tid < K) reinterpret_cast<float*>(rec + L::kGc)[tid] = sm.G[(kChunk - 1) * S::kGP + tid];
 
     // ---- -W: W^T tiles D[c][r] for key-channel block cb = w and every row
     //      block; a W operand tile spans two channel blocks, so each wave
@@ -550,7 +604,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > rb / 2) continue;
-          mma(acc, xf[kb], t_frag(rb, kb, false));
+          mma(acc, xf[kb], t_get(rb, kb, false));
         }
         const float wv[4] = {-acc[0], -acc[1], -acc[2], -acc[3]};
         PW::store_half(rec + L::kWn + (int64_t)(rb * (K / 32) + w / 2) * tile_bytes<PW>(), lane, w & 1, wv);
@@ -578,7 +632,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           if (kb > rb / 2) continue;
-          mma(acc, t_frag(rb, kb, true), vf[kb]);
+          mma(acc, t_get(rb, kb, true), vf[kb]);
         }
         reinterpret_cast<f32x4*>(rec + L::kU)[(rb * (V / 16) + w) * kWave + lane] = acc;
       }
