@@ -400,41 +400,48 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
         }
       }
     }
-    // ---- the upper channel half hands its partial tiles to the lower half
+    // ---- the two channel halves exchange partial tiles: the upper half
+    //      completes A (into M), the lower half completes Aqk (into the record)
     {
       float* red = sm.red_buf();
       const int slot0 = R * (R + 1) / 2;   // tiles (R, 0..R)
       block_sync();   // everyone is done with q (fp32 inputs reuse it here)
-      if (chalf == 1) {
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          if (I > R) continue;
+      for (int I = 0; I < 4; ++I) {
+        if (I > R) continue;
+        if (chalf == 1)
           reinterpret_cast<f32x4*>(red)[((slot0 + I) * 2 + 0) * kWave + lane] = accKK[I];
+        else
           reinterpret_cast<f32x4*>(red)[((slot0 + I) * 2 + 1) * kWave + lane] = accQK[I];
-        }
       }
       block_sync();
+      const int r = r_own;
       if (chalf == 0) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          if (I > R) continue;
-          accKK[I] += reinterpret_cast<const f32x4*>(red)[((slot0 + I) * 2 + 0) * kWave + lane];
-          accQK[I] += reinterpret_cast<const f32x4*>(red)[((slot0 + I) * 2 + 1) * kWave + lane];
-        }
         // A[r][i] = beta_r * D[i][r] (i < r), stored transposed above the diagonal of M.
-        const int r = r_own;
         const float br = sm.beta[r];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (I > R) continue;
+          const f32x4 part = reinterpret_cast<const f32x4*>(red)[((slot0 + I) * 2 + 0) * kWave + lane];
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
             const int i = 16 * I + 4 * gq + ii;
-            if (i < r) sm.M[i * S::kMP + r] = br * accKK[I][ii];
-            accQK[I][ii] = (i <= r) ? p.scale * accQK[I][ii] : 0.f;
+            const float a = br * (accKK[I][ii] + part[ii]);
+            if (I < R || i < r) sm.M[i * S::kMP + r] = a;
           }
         }
+      } else {
         // scale * Aqk, rows of block R: the D[i][r] tiles (I, R) are the operand layout
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          if (I > R) continue;
+          const f32x4 part = reinterpret_cast<const f32x4*>(red)[((slot0 + I) * 2 + 1) * kWave + lane];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 16 * I + 4 * gq + ii;
+            accQK[I][ii] = (I < R || i <= r) ? p.scale * (accQK[I][ii] + part[ii]) : 0.f;
+          }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           float x[8];
