@@ -177,9 +177,9 @@ __device__ __forceinline__ ItemInfo item_info(const IntraParams& p, int64_t item
 
 // One workgroup per CU, looping over (chunk, head) items.  The inputs of the
 // next item are loaded into LDS (direct-to-LDS, asynchronous) while the
-// current item computes: k, g and beta at the start of the item (second
-// buffers), q once the current q is dead (after the A products), v into the g
-// buffer once g has been summed.
+// current item computes: k, g and beta after the A products (second buffers),
+// q once the current q is dead (after the A products), v into the g buffer
+// once g has been summed (issued after the A products too).
 template <class TI, int K, int V>
 __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams p) {
   using S = IntraSmem<TI, K, V>;
@@ -252,7 +252,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     wait_loads();
     block_sync();
     if (w == 0) sm.beta[lane] = lane < len ? ld1(&beta_next) : 0.f;   // zero past the chunk
-    if (S::kDB && has_next) issue_kgb(nxt, cb ^ 1);
     if (len < kChunk) {
       for (int e = tid; e < (kChunk - len) * K; e += kIntraThreads) {
         const int r = len + e / K, c = e % K;
@@ -287,8 +286,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       for (int i = 0; i < RP; ++i)
         *reinterpret_cast<float2*>(&sm.G[(r0 + i) * S::kGP + c]) = float2{g0[i] + o0, g1[i] + o1};
     }
-    block_sync();   // g consumed: the buffer now receives v
-    issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
+    block_sync();   // g consumed: the buffer may receive v
 
     // ---- this wave's rows: norms and its block's span (both waves of a row block)
     const int f = 16 * R, r_own = f + m;
@@ -400,6 +398,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
         }
       }
     }
+    // This item's v and the next item's k, g and beta go out here, where the
+    // other wave of each SIMD has VALU work to fill the issue stalls.
+    issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
+    if (S::kDB && has_next) issue_kgb(nxt, cb ^ 1);
+
     // ---- the two channel halves exchange partial tiles: the upper half
     //      completes A (into M), the lower half completes Aqk (into the record)
     {
