@@ -44,5 +44,6 @@ hipError_t launch_prep(const CallArgs& a);
 hipError_t launch_intra(const CallArgs& a);
 hipError_t launch_recur(const CallArgs& a);
 hipError_t launch_zero_states(const CallArgs& a);
+int cu_count();
 
 }  // namespace kda

@@ -17,10 +17,16 @@
 //
 // Wave roles.  A wave that issues direct-to-LDS loads moves about 10 bytes
 // per clock: the rate is per issuing wave (per SIMD), so a compute wave that
-// loads its own operands spends most of a step stalled on issue.  Here
-// producer wave 4 + i fills the stage of compute wave i (waves are spread
-// round-robin over the SIMDs, so each SIMD hosts one of each), and wave 8
-// pulls records a few chunks ahead into L2.  Three barriers per chunk:
+// loads its own operands spends most of a step stalled on issue.  Here a
+// workgroup carries TPW value tiles of one (sequence, head): compute waves
+// 4t .. 4t+3 run tile t, producer wave 4 TPW + i fills stage i (the record
+// operands of token block / key-channel group i, shared by the tiles; only U
+// differs per tile) and the last wave pulls records a few chunks ahead into
+// L2.  Waves are spread round-robin over the SIMDs, so SIMD i hosts compute
+// wave i of every tile and producer i.  Two tiles per workgroup halve the
+// staged bytes per tile and let the two compute groups hide each other's
+// latencies; that pays when there are many (sequence, head) pairs, while one
+// tile per workgroup spreads few of them over all CUs.  Three barriers per chunk:
 //   B1 after the Delta phase, B15 after the state update, B2 after the
 //   output phase.
 // A stage group is refilled as soon as the barrier after its last reader
@@ -34,10 +40,13 @@ namespace kda {
 namespace {
 
 constexpr int kVT = 16;   // value channels per workgroup
-constexpr int kComputeWaves = 4;
-constexpr int kProducer0 = kComputeWaves;          // producer of compute wave i: kProducer0 + i
-constexpr int kPrefetchWave = 2 * kComputeWaves;
-constexpr int kRecurThreads = (kPrefetchWave + 1) * kWave;
+constexpr int kComputeWaves = 4;   // per value tile
+template <int TPW>
+struct Roles {
+  static constexpr int kProducer0 = kComputeWaves * TPW;   // producer of stage i: kProducer0 + i
+  static constexpr int kPrefetchWave = kProducer0 + kComputeWaves;
+  static constexpr int kThreads = (kPrefetchWave + 1) * kWave;
+};
 constexpr int kPrefetchAhead = 4;   // chunks between the L2 prefetch and the use of a record
 
 // An operand kept in LDS as rows n (value channel) of k-contiguous values.
@@ -104,12 +113,12 @@ __device__ __forceinline__ void store_out(uint16_t* o, int64_t i, float x) {
 // The record operands compute wave w uses in one chunk, staged in its own LDS
 // block by its producer wave with direct-to-LDS loads.
 //   Wn  : -W rows 16w..16w+15, all K          (K/32 tiles)
-//   U   : U rows 16w..16w+15, this value tile  (1 KB)
+//   U   : U rows 16w..16w+15, per value tile   (TPW x 1 KB)
 //   Kt  : key-channel blocks cb = w*NCB+u      (NCB x 2 tiles)
 //   Qg  : Qg rows 16w..16w+15, all K          (K/32 tiles)
 //   Aqk : Aqk row block w, token blocks <= w/2 (1 or 2 tiles)
 //   Gc  : exp(G_C) for this wave's key-channel blocks (16 NCB floats)
-template <class TI, int K, int V>
+template <class TI, int K, int V, int TPW>
 struct Stage {
   using P = Prec<TI>;
   using L = RecordLayout<TI, K, V>;
@@ -120,20 +129,22 @@ struct Stage {
   static constexpr int kAqkTile = tile_bytes<typename P::Q>();
   static constexpr int oWn = 0;
   static constexpr int oU = oWn + kWnBytes;
-  static constexpr int oKt = oU + 1024;
+  static constexpr int oKt = oU + TPW * 1024;
   static constexpr int oQg = oKt + kKtBytes;
   static constexpr int oAqk = oQg + kQgBytes;
   static constexpr int oGc = oAqk + 2 * kAqkTile;
   static constexpr int kBytes = oGc + 64 * NCB;
   // Load instructions (1 KB each) per group.
-  static constexpr int nW = kWnBytes / 1024 + 1;   // Wn and U
+  static constexpr int nW = kWnBytes / 1024 + TPW;   // Wn and U
   static constexpr int nKt = kKtBytes / 1024 + 1;   // Kt and Gc
   static constexpr int nQ1 = (kQgBytes + kAqkTile) / 1024;       // Qg and Aqk, waves 0 and 1
   static constexpr int nQ2 = (kQgBytes + 2 * kAqkTile) / 1024;   // waves 2 and 3
 
-  __device__ static void issue_w(char* stg, const char* rec, int w, int j, int lane) {
+  __device__ static void issue_w(char* stg, const char* rec, int w, int j0, int lane) {
     dma_copy<kWnBytes>(stg + oWn, rec + L::kWn + (int64_t)w * kWnBytes, lane);
-    dma_copy<1024>(stg + oU, rec + L::kU + (int64_t)(w * (V / 16) + j) * 1024, lane);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      dma_copy<1024>(stg + oU + 1024 * t, rec + L::kU + (int64_t)(w * (V / 16) + j0 + t) * 1024, lane);
   }
   __device__ static void issue_kt(char* stg, const char* rec, int w, int lane) {
     dma_copy<kKtBytes>(stg + oKt, rec + L::kKt + (int64_t)w * kKtBytes, lane);
@@ -163,19 +174,22 @@ struct RecurParams {
   void* o;
 };
 
-template <class TI, class TO, int K, int V>
-__global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p) {
+template <class TI, class TO, int K, int V, int TPW>
+__global__ __launch_bounds__(Roles<TPW>::kThreads) void kda_recur_kernel(RecurParams p) {
   using P = Prec<TI>;
   using PS = typename P::S;
   using PD = typename P::D;
-  using SG = Stage<TI, K, V>;
+  using SG = Stage<TI, K, V, TPW>;
+  constexpr int kProducer0 = Roles<TPW>::kProducer0;
+  constexpr int kPrefetchWave = Roles<TPW>::kPrefetchWave;
   constexpr int NV = V / kVT;
+  constexpr int NVW = NV / TPW;     // workgroups per (sequence, head)
   constexpr int SP = K + 8;        // LDS row pitch of the state operand
   constexpr int DP = kChunk + 8;   // LDS row pitch of the Delta operand
   constexpr int NCB = SG::NCB;     // key-channel blocks of the state per wave
   __shared__ __align__(16) char s_stage[kComputeWaves][SG::kBytes];
-  __shared__ __align__(16) char s_state[LdsPlane<PS>::template bytes<kVT, SP>()];
-  __shared__ __align__(16) char s_delta[LdsPlane<PD>::template bytes<kVT, DP>()];
+  __shared__ __align__(16) char s_state_t[TPW][LdsPlane<PS>::template bytes<kVT, SP>()];
+  __shared__ __align__(16) char s_delta_t[TPW][LdsPlane<PD>::template bytes<kVT, DP>()];
   __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -183,12 +197,13 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
   const int m = lane & 15, gq = lane >> 4;
   const int64_t H = p.H;
 
-  // XCD-aware decode: the NV value tiles of one (sequence, head) sit on
+  // XCD-aware decode: the NVW workgroups of one (sequence, head) sit on
   // workgroup ids with equal id % 8, which the dispatcher places on one XCD,
-  // so they share that XCD's L2 copy of the chunk records.
+  // so they share that XCD's L2 copy of the chunk records.  Workgroup jw
+  // carries value tiles j0 = TPW jw .. j0 + TPW - 1.
   const int64_t id = blockIdx.x;
-  const int64_t seq_head = (id / (8 * NV)) * 8 + id % 8;
-  const int j = (int)((id / 8) % NV);
+  const int64_t seq_head = (id / (8 * NVW)) * 8 + id % 8;
+  const int jw = (int)((id / 8) % NVW), j0 = TPW * jw;
   const int64_t n_seq_heads = p.packed ? (int64_t)p.hdr->n_segments * H : p.n_seq_heads_fixed;
   if (seq_head >= n_seq_heads) return;
   const int64_t h = seq_head % H, sq = seq_head / H;
@@ -215,18 +230,18 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
   auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
 
   // ---- L2 prefetch wave: walks kPrefetchAhead chunks ahead and touches this
-  // workgroup's 1/NV share of each record (every 64-byte segment once), so
-  // the record is in this XCD's L2 when the producers of all NV workgroups
+  // workgroup's 1/NVW share of each record (every 64-byte segment once), so
+  // the record is in this XCD's L2 when the producers of all NVW workgroups
   // stage it.
   if (wave == kPrefetchWave) {
     using L = RecordLayout<TI, K, V>;
     constexpr int SEGS = (int)(L::kBytes / 64);
-    constexpr int SHARE = (SEGS + NV - 1) / NV;
+    constexpr int SHARE = (SEGS + NVW - 1) / NVW;
     auto prefetch = [&](int64_t n) {
       const char* r = record(n);
 #pragma unroll
       for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
-        const int e = i * kWave + lane, seg = j * SHARE + e;
+        const int e = i * kWave + lane, seg = jw * SHARE + e;
         if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
       }
     };
@@ -251,7 +266,7 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
     const bool two_aqk = w >= 2;
     if (n_chunks > 0) {
       const char* r0 = record(0);
-      SG::issue_w(stg, r0, w, j, lane);
+      SG::issue_w(stg, r0, w, j0, lane);
       SG::issue_kt(stg, r0, w, lane);
       SG::issue_q(stg, r0, w, lane);
       vm_wait<0>();
@@ -269,7 +284,7 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
       block_sync();   // B1
       // State update reads Kt/Gc(n).  Wn/U(n+1) go out; Qg/Aqk(n) must land.
       if (more) {
-        SG::issue_w(stg, rn1, w, j, lane);
+        SG::issue_w(stg, rn1, w, j0, lane);
         vm_wait<SG::nW>();
       } else {
         vm_wait<0>();
@@ -286,11 +301,13 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
     return;
   }
 
-  // ---- compute waves
-  const int w = wave;
+  // ---- compute waves of tile tl
+  const int tl = wave / kComputeWaves, w = wave % kComputeWaves;
   const char* stg = s_stage[w];
   TO* out = static_cast<TO*>(p.o);
-  const int v0 = kVT * j;
+  const int v0 = kVT * (j0 + tl);
+  char* s_state = s_state_t[tl];
+  char* s_delta = s_delta_t[tl];
 
   // State slice: wave w holds key-channel blocks cb = w*NCB .. +NCB-1, lane
   // (column v0 + m, rows 16cb + 4gq + i).
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
       wn[kb].load(stg + SG::oWn + kb * tile_bytes<typename P::W>(), lane);
       sf[kb] = LdsPlane<PS>::template read<kVT, SP>(s_state, m, kb, gq);
     }
-    f32x4 d = reinterpret_cast<const f32x4*>(stg + SG::oU)[lane];
+    f32x4 d = reinterpret_cast<const f32x4*>(stg + SG::oU + 1024 * tl)[lane];
 #pragma unroll
     for (int kb = 0; kb < K / 32; ++kb) mma(d, wn[kb], sf[kb]);
     {
@@ -328,8 +345,8 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
     }
     block_sync();   // B1
 
-    // S <- diag(exp(G_C)) S + Kt^T Delta; the Delta operand stays in
-    // registers for the output phase.
+    // S <- diag(exp(G_C)) S + Kt^T Delta (with one tile per workgroup the
+    // Delta operand stays in registers for the output phase)
     PD dd[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) dd[kb] = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
@@ -350,18 +367,38 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
     block_sync();   // B15
 
     // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
-    typename P::Q qg[K / 32], aq[2];
-#pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) qg[kb].load(stg + SG::oQg + kb * tile_bytes<typename P::Q>(), lane);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) aq[kb].load(stg + SG::oAqk + kb * SG::kAqkTile, lane);
     f32x4 ov = {0, 0, 0, 0};
+    if constexpr (TPW == 1) {
+      typename P::Q qg[K / 32], aq[2];
 #pragma unroll
-    for (int kb = 0; kb < K / 32; ++kb) mma(ov, qg[kb], sf[kb]);
+      for (int kb = 0; kb < K / 32; ++kb) qg[kb].load(stg + SG::oQg + kb * tile_bytes<typename P::Q>(), lane);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) mma(ov, aq[kb], dd[kb]);
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= w / 2) aq[kb].load(stg + SG::oAqk + kb * SG::kAqkTile, lane);
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) mma(ov, qg[kb], sf[kb]);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        if (kb <= w / 2) mma(ov, aq[kb], dd[kb]);
+    } else {
+      // Four waves per SIMD leave 128 registers: operands are loaded as they
+      // are used and Delta is re-read (it stays in LDS until the next chunk's
+      // Delta phase).
+#pragma unroll
+      for (int kb = 0; kb < K / 32; ++kb) {
+        typename P::Q qg;
+        qg.load(stg + SG::oQg + kb * tile_bytes<typename P::Q>(), lane);
+        mma(ov, qg, sf[kb]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (kb > w / 2) continue;
+        typename P::Q aq;
+        aq.load(stg + SG::oAqk + kb * SG::kAqkTile, lane);
+        const PD d2 = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
+        mma(ov, aq, d2);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * gq + i;
@@ -380,17 +417,25 @@ __global__ __launch_bounds__(kRecurThreads) void kda_recur_kernel(RecurParams p)
   }
 }
 
+template <class TI, class TO, int K, int V, int TPW>
+hipError_t launch_recur_w(const RecurParams& p, int64_t seq_heads, hipStream_t stream) {
+  constexpr int NVW = V / kVT / TPW;
+  const int64_t grid = (seq_heads + 7) / 8 * 8 * NVW;
+  hipLaunchKernelGGL((kda_recur_kernel<TI, TO, K, V, TPW>), dim3((unsigned)grid), dim3(Roles<TPW>::kThreads), 0,
+                     stream, p);
+  return hipGetLastError();
+}
+
 template <class TI, class TO, int K, int V>
 hipError_t launch_recur_t(const CallArgs& a) {
-  constexpr int NV = V / kVT;
   RecurParams p{a.B, a.T, a.H, a.nc_fixed, a.n_max > 0, a.n_max, a.B * a.H, a.hdr, a.segs,
                 a.records, a.record_bytes, a.init, a.fin, a.o};
   const int64_t seq_heads = (a.n_max > 0 ? a.smax : a.B) * a.H;
   if (seq_heads <= 0) return hipSuccess;
-  const int64_t groups = (seq_heads + 7) / 8;
-  const int64_t grid = groups * 8 * NV;
-  hipLaunchKernelGGL((kda_recur_kernel<TI, TO, K, V>), dim3((unsigned)grid), dim3(kRecurThreads), 0, a.stream, p);
-  return hipGetLastError();
+  // Two tiles per workgroup once one tile per workgroup would need several
+  // rounds of workgroups over the CUs.
+  if (seq_heads * (V / kVT) > 2 * (int64_t)cu_count()) return launch_recur_w<TI, TO, K, V, 2>(p, seq_heads, a.stream);
+  return launch_recur_w<TI, TO, K, V, 1>(p, seq_heads, a.stream);
 }
 
 template <class TI, class TO>

@@ -80,6 +80,11 @@ CASES = {
     "bf16_state_safe": dict(dtype="bf16", B=2, T=333, H=2, K=128, V=128, initial_state=True, final_state=True,
                             gate="neg5_sigmoid", safe_gate=True, lower_bound=-5.0),
     "bf16_l2_in_kernel": dict(dtype="bf16", B=1, T=256, H=2, K=128, V=128, l2norm_in_kernel=True, final_state=True),
+    # more than 2 x 256 value tiles: the recurrence runs two tiles per workgroup
+    "tiles2_bf16_state": dict(dtype="bf16", B=2, T=200, H=40, K=128, V=128, initial_state=True, final_state=True,
+                              gate="neg5_sigmoid", safe_gate=True, lower_bound=-5.0),
+    "tiles2_k128_v64": dict(dtype="bf16", B=3, T=130, H=48, K=128, V=64, final_state=True),
+    "tiles2_fp32_k64": dict(dtype="f32", B=3, T=100, H=48, K=64, V=64, initial_state=True, final_state=True),
 }
 
 
