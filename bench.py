@@ -10,10 +10,12 @@ workload (in-kernel q/k L2 norm) is timed the same way and reported under
 "extra".
 
 Timing follows the pages' method (compile first, then synchronized timed
-iterations, median reported): W untimed warm-up steps, then K timed steps
-between two device synchronizations, with a HIP event on the launch stream
-around every step and around every kernel of every step (through the
-library's launch observer).  Prints ONE JSON line on stdout.
+iterations): W untimed warm-up steps, then K timed steps between two device
+synchronizations and two HIP events on the launch stream, with nothing else
+in the stream (this gives `value` and `ms_per_step`); then K more steps with
+an event around every kernel (through the library's launch observer) and at
+every step boundary, for the per-kernel durations behind the roofline and the
+per-step statistics.  Prints ONE JSON line on stdout.
 """
 from __future__ import annotations
 
@@ -128,12 +130,32 @@ def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32"):
         call.enqueue()
     torch.cuda.synchronize()
 
-    # Kernel events through the launch observer, step events around each call.
+    # 1) Throughput: `steps` forwards between two events and nothing else in
+    #    the stream (per-kernel events and the host callbacks that record them
+    #    would add gaps between the kernels).
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        call.enqueue()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+
+    # 2) Per-kernel durations: another `steps` forwards with an event before
+    #    and after every kernel (recorded on the launch stream by the library's
+    #    launch observer from a pre-created pool) and at every step boundary.
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(16 * steps + 8)]
+    used = []
     pending = {}
     kernel_events = {}
 
     def observer(name, stream, phase):
-        ev = torch.cuda.Event(enable_timing=True)
+        ev = pool[len(used)]
+        used.append(ev)
         ev.record()
         if phase == 0:
             pending[name] = ev
@@ -143,17 +165,14 @@ def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32"):
     cb = kda.set_launch_observer(observer)
     step_events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
     step_events[0].record()
     for i in range(steps):
         call.enqueue()
         step_events[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     kda.set_launch_observer(None)
     del cb
     step_ms = [step_events[i].elapsed_time(step_events[i + 1]) for i in range(steps)]
-    total_ms = step_events[0].elapsed_time(step_events[-1])
     kern_ms = {n: [a.elapsed_time(b) for a, b in evs] for n, evs in kernel_events.items()}
     return dict(inp=inp, call=call, step_ms=step_ms, total_ms=total_ms, wall_s=wall, kernel_ms=kern_ms)
 
@@ -242,7 +261,9 @@ def main():
                 "traffic": measured_traffic(s["dominant"], w.name), "alg_bytes": dom["alg_bytes"],
                 "mfma_tflops": dom["achieved_tflops"],
                 "mfma_frac": round(dom["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
-    extra = {"path": {"alg_bytes": s["path_bytes"], "alg_flops": s["path_flops"],
+    extra = {"timing": "value/ms_per_step: K steps with no per-kernel events; kernels and step_ms: K further "
+                       "steps with an event around every kernel",
+             "path": {"alg_bytes": s["path_bytes"], "alg_flops": s["path_flops"],
                       "gbps": round(s["path_gbps"], 1), "hbm_frac": round(s["path_gbps"] / HBM_PEAK_GBPS, 4),
                       "tflops": round(s["path_tflops"], 2)},
              "step_ms": {"median": round(s["median_ms"], 4), "min": round(s["min_ms"], 4),
