@@ -49,26 +49,42 @@ struct SwzRows {
 
 template <class TI, int K, int V>
 struct IntraSmem {
-  static constexpr bool kDB = sizeof(TI) == 2;   // k and g/v double-buffered (fits LDS for bf16)
+  static constexpr bool kDB = sizeof(TI) == 2;   // g/v double-buffered (fits LDS for bf16)
   static constexpr int NB = kDB ? 2 : 1;
+  // bf16 inputs: the decayed keys X of the column operands are tabulated once
+  // per item (fp32 inputs compute them pair by pair, for lack of LDS).
+  static constexpr bool kXT = sizeof(TI) == 2;
   static constexpr int kGVW = K > V ? K : V;      // g (width K) and later v (width V) share a buffer
-  static constexpr int kGP = K + 4;               // row pitch (floats) of G, later exp(G)
+  static constexpr int kGP = K + 4;               // row pitch (floats) of G and X
   static constexpr int kMP = 68;                  // row pitch of M (T below the diagonal, A^T above)
+  static constexpr int kPairs = 10;               // (row block, column block) pairs with I <= R
   TI q[kChunk * K];
-  TI k[NB][kChunk * K];
+  TI k[kChunk * K];
   TI gv[NB][kChunk * kGVW];
   float G[kChunk * kGP];
   float beta[kChunk];
   float M[kChunk * kMP];
   alignas(16) float nk[kChunk];
-  float part[2 * kIntraThreads];
+  // Per-channel decay factors (bf16 inputs): exp(G_f(R) - G_l(I)) for the ten
+  // pairs, exp(G_f(R)) for the four row blocks (f = first, l = last row),
+  // then exp(G_C - G_l(I)) for the four column blocks.
+  static constexpr int kTabRows = kPairs + 8;
+  alignas(16) float tab[kXT ? kTabRows * K : 4];
   // Partial A / Aqk tiles of the upper key-channel half: 10 (row block, column
   // block) tiles x {A, Aqk} x 64 lanes x 4.  They reuse the q buffer (dead by
-  // then) when it is large enough (fp32 inputs with K = 128), else their own.
+  // then) when it is large enough (fp32 inputs with K = 128), else the scratch.
   static constexpr int kRedFloats = 10 * 2 * kWave * 4;
   static constexpr bool kRedInQ = sizeof(TI) * kChunk * K >= sizeof(float) * kRedFloats;
-  float red[kRedInQ ? 1 : kRedFloats];
-  __device__ float* red_buf() { return kRedInQ ? reinterpret_cast<float*>(q) : red; }
+  // Scratch used in turn by the running-sum partials, the X table and the
+  // partial tiles.
+  static constexpr int kPartFloats = 2 * kIntraThreads;
+  static constexpr int kXFloats = kXT ? kChunk * kGP : 0;
+  static constexpr int kScratch0 = kPartFloats > kXFloats ? kPartFloats : kXFloats;
+  static constexpr int kScratch = (!kRedInQ && kRedFloats > kScratch0) ? kRedFloats : kScratch0;
+  alignas(16) float scratch[kScratch];
+  __device__ float* part() { return scratch; }
+  __device__ float* X() { return scratch; }
+  __device__ float* red_buf() { return kRedInQ ? reinterpret_cast<float*>(q) : scratch; }
 };
 
 // Four consecutive elements as floats.
@@ -218,8 +234,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
   // once would make the compiler wait for every load in flight, the
   // direct-to-LDS prefetches included.
   TI beta_next = TI(0);
-  auto issue_kgb = [&](const ItemInfo& it, int buf) {
-    issue_rows<TI, K>(sm.k[buf], gk_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
+  auto issue_k = [&](const ItemInfo& it) {
+    issue_rows<TI, K>(sm.k, gk_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
+  };
+  auto issue_gb = [&](const ItemInfo& it, int buf) {
     issue_rows<TI, K>(sm.gv[buf], gg_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
     beta_next = gb_[(it.tok0 + min(lane, it.len - 1)) * H + it.h];
   };
@@ -229,7 +247,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
   {
     const ItemInfo first = item_info(p, blockIdx.x);
-    issue_kgb(first, 0);
+    issue_k(first);
+    issue_gb(first, 0);
     issue_q(first);
   }
 
@@ -243,7 +262,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     const bool has_next = nxt_item < n_items;
     const ItemInfo nxt = has_next ? item_info(p, nxt_item) : cur;
     char* rec = p.records + item * p.record_bytes;
-    TI* kbuf = sm.k[cb];
+    TI* kbuf = sm.k;
     TI* gvbuf = sm.gv[cb];
     const int tid = opaque(threadIdx.x), lane = tid & 63;
     const int m = lane & 15, gq = lane >> 4;
@@ -274,19 +293,76 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
         g0[i] += g0[i - 1];
         g1[i] += g1[i - 1];
       }
-      *reinterpret_cast<float2*>(&sm.part[part * K + c]) = float2{g0[RP - 1], g1[RP - 1]};
+      *reinterpret_cast<float2*>(&sm.part()[part * K + c]) = float2{g0[RP - 1], g1[RP - 1]};
       block_sync();
       float o0 = 0.f, o1 = 0.f;
-      for (int pp = 0; pp < part; ++pp) {
-        const float2 v = *reinterpret_cast<const float2*>(&sm.part[pp * K + c]);
-        o0 += v.x;
-        o1 += v.y;
-      }
+      float2 pv[PARTS - 1];
+#pragma unroll
+      for (int pp = 0; pp < PARTS - 1; ++pp) pv[pp] = *reinterpret_cast<const float2*>(&sm.part()[pp * K + c]);
+#pragma unroll
+      for (int pp = 0; pp < PARTS - 1; ++pp)
+        if (pp < part) {
+          o0 += pv[pp].x;
+          o1 += pv[pp].y;
+        }
 #pragma unroll
       for (int i = 0; i < RP; ++i)
         *reinterpret_cast<float2*>(&sm.G[(r0 + i) * S::kGP + c]) = float2{g0[i] + o0, g1[i] + o1};
     }
     block_sync();   // g consumed: the buffer may receive v
+
+    // ---- bf16 inputs: X[i][c] = k_ic exp(G_l,c - G_ic) with l the last row of
+    //      i's block (every factor <= 1), and the per-channel factors
+    //      exp(G_f(R) - G_l(I)) (pairs I <= R) and exp(G_f(R)).  A column
+    //      operand of the pair (R, I) is then X * exp(G_f(R) - G_l(I)) =
+    //      k_i exp(G_f(R) - G_i), and exp(G_r) = exp(G_r - G_f(R)) exp(G_f(R)).
+    if constexpr (S::kXT) {
+      float* X = sm.X();
+      constexpr int XIT = kChunk * K / 4 / kIntraThreads;
+      static_assert(XIT * kIntraThreads * 4 == kChunk * K, "whole passes");
+      f32x4 gr[XIT], gl[XIT], kx[XIT];
+#pragma unroll
+      for (int it = 0; it < XIT; ++it) {   // all reads first
+        const int e4 = tid + it * kIntraThreads, r = e4 / (K / 4), c = (e4 % (K / 4)) * 4, l = (r | 15);
+        gr[it] = ld4(sm.G + r * S::kGP + c);
+        gl[it] = ld4(sm.G + l * S::kGP + c);
+        kx[it] = ld4(kbuf + SK::idx(r, c));
+      }
+#pragma unroll
+      for (int it = 0; it < XIT; ++it) {
+        const int e4 = tid + it * kIntraThreads, r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
+        f32x4 x;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = kx[it][j] * __expf(gl[it][j] - gr[it][j]);
+        *reinterpret_cast<f32x4*>(X + r * S::kGP + c) = x;
+      }
+      constexpr int TIT = (S::kTabRows * K + kIntraThreads - 1) / kIntraThreads;
+      float ga[TIT], gb[TIT];
+#pragma unroll
+      for (int it = 0; it < TIT; ++it) {
+        const int e = tid + it * kIntraThreads, t = e / K, c = e % K;
+        int ra = 0, rb = kChunk - 1;   // exp(G_ra - G_rb)
+        if (t < S::kPairs) {
+          const int R2 = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3, I2 = t - R2 * (R2 + 1) / 2;
+          ra = 16 * R2;
+          rb = 16 * I2 + 15;
+        } else if (t < S::kPairs + 4) {
+          ra = 16 * (t - S::kPairs);
+          rb = -1;
+        } else {
+          ra = kChunk - 1;
+          rb = 16 * (t - S::kPairs - 4) + 15;
+        }
+        const bool ok = e < S::kTabRows * K;
+        ga[it] = ok ? sm.G[ra * S::kGP + c] : 0.f;
+        gb[it] = (ok && rb >= 0) ? sm.G[rb * S::kGP + c] : 0.f;
+      }
+#pragma unroll
+      for (int it = 0; it < TIT; ++it) {
+        const int e = tid + it * kIntraThreads;
+        if (e < S::kTabRows * K) sm.tab[e] = __expf(ga[it] - gb[it]);
+      }
+    }
 
     // ---- this wave's rows: norms and its block's span (both waves of a row block)
     const int f = 16 * R, r_own = f + m;
@@ -312,7 +388,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
     const bool diag_split = span <= kSpanMax;
-    block_sync();   // nk visible
+    block_sync();   // nk, X and the factor table visible
 
     // ---- A and Aqk for row block R over key-channel half chalf: tiles (I, R)
     //      hold D[i][r], I <= R; the two halves are summed through LDS below.
@@ -328,37 +404,61 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 #pragma unroll
       for (int kbi = 0; kbi < KBH; ++kbi) {
         const int kb = chalf * KBH + kbi;
-        float gr[8], gf[8], kx[8], qx[8], xk[8], xq[8];
+        float gr[8], gf[8], kx[8], qx[8], xk[8], xq[8], er[8];
         row8f(sm.G + r * S::kGP, kb, gq, gr);
         row8f(sm.G + f * S::kGP, kb, gq, gf);
         row8<TI, K>(kbuf, r, kb, gq, kx);
         row8<TI, K>(sm.q, r, kb, gq, qx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float e = __expf(gr[j] - gf[j]);
-          xk[j] = kx[j] * e;
-          xq[j] = qx[j] * e;
+          er[j] = __expf(gr[j] - gf[j]);
+          xk[j] = kx[j] * er[j];
+          xq[j] = qx[j] * er[j];
         }
         PA fkr, fqr;
         fkr.set(xk);
         fqr.set(xq);
         {   // scale * q * exp(G) for this wave's rows: the output's inter-chunk operand
           float xg[8];
+          if constexpr (S::kXT) {
+            float ef[8];
+            row8f(sm.tab + (S::kPairs + R) * K, kb, gq, ef);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) xg[j] = sqr * qx[j] * __expf(gr[j]);
+            for (int j = 0; j < 8; ++j) xg[j] = sqr * qx[j] * er[j] * ef[j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xg[j] = sqr * qx[j] * __expf(gr[j]);
+          }
           PQ qf;
           qf.set(xg);
           qf.store(rec + L::kQg + (int64_t)(R * (K / 32) + kb) * tile_bytes<PQ>(), lane);
+        }
+        // bf16 inputs: the column operands' table rows for every I <= R
+        // are read before any is used
+        float xi[4][8], di[4][8];
+        if constexpr (S::kXT) {
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            if (I > R) continue;
+            row8f(sm.X() + (16 * I + m) * S::kGP, kb, gq, xi[I]);
+            row8f(sm.tab + (R * (R + 1) / 2 + I) * K, kb, gq, di[I]);
+          }
         }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           if (I > R || (I == R && !diag_split)) continue;
           const int i = 16 * I + m;
-          float gi[8], ki[8], xc[8];
-          row8f(sm.G + i * S::kGP, kb, gq, gi);
-          row8<TI, K>(kbuf, i, kb, gq, ki);
+          float xc[8];
+          if constexpr (S::kXT) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) xc[j] = ki[j] * __expf(gf[j] - gi[j]);
+            for (int j = 0; j < 8; ++j) xc[j] = xi[I][j] * di[I][j];
+          } else {
+            float gi[8], ki[8];
+            row8f(sm.G + i * S::kGP, kb, gq, gi);
+            row8<TI, K>(kbuf, i, kb, gq, ki);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xc[j] = ki[j] * __expf(gf[j] - gi[j]);
+          }
           PA fkc;
           fkc.set(xc);
           mma(accKK[I], fkc, fkr);
@@ -401,7 +501,33 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     // This item's v and the next item's k, g and beta go out here, where the
     // other wave of each SIMD has VALU work to fill the issue stalls.
     issue_rows<TI, V>(gvbuf, gv_ + (cur.tok0 * H + h) * V, H * V, len, w, lane);
-    if (S::kDB && has_next) issue_kgb(nxt, cb ^ 1);
+    if (S::kDB && has_next) issue_gb(nxt, cb ^ 1);
+
+    // ---- Kt = (k * exp(G_C - G))^T as operand tiles [c-block][token k-tile].
+    //      bf16 inputs: from X, Kt[c][r] = X[r][c] exp(G_C - G_l(I(r))), by the
+    //      waves of the lower channel half, whose share of the products above
+    //      is the smaller one; fp32 inputs: beside the solve below.
+    constexpr int NKT = (K / 16) * 2;
+    if constexpr (S::kXT) {
+      if (w < 4) {
+        for (int t = w; t < NKT; t += 4) {
+          const int cbk = t >> 1, kb = t & 1, c = 16 * cbk + m;
+          const float e0 = sm.tab[(S::kPairs + 4 + 2 * kb) * K + c], e1 = sm.tab[(S::kPairs + 5 + 2 * kb) * K + c];
+          float xv[8], n8[8], x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {   // all reads first
+            const int r = 32 * kb + kperm(gq, j);
+            xv[j] = sm.X()[r * S::kGP + c];
+            n8[j] = sm.nk[r];
+          }
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = xv[j] * n8[j] * (j < 4 ? e0 : e1);
+          PK fr;
+          fr.set(x);
+          fr.store(rec + L::kKt + (int64_t)(cbk * 2 + kb) * tile_bytes<PK>(), lane);
+        }
+      }
+    }
 
     // ---- the two channel halves exchange partial tiles: the upper half
     //      completes A (into M), the lower half completes Aqk (into the record)
@@ -464,7 +590,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
     // ---- Kt = (k * exp(G_C - G))^T as operand tiles [c-block][token k-tile];
     //      independent of T, so waves 4-7 build them while waves 0-3 solve
-    constexpr int NKT = (K / 16) * 2;
     auto kt_tile = [&](int t) {
       const int cbk = t >> 1, kb = t & 1, c = 16 * cbk + m;
       const float gc = sm.G[(kChunk - 1) * S::kGP + c];
@@ -483,64 +608,139 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       fr.store(rec + L::kKt + (int64_t)(cbk * 2 + kb) * tile_bytes<PK>(), lane);
     };
 
-    // ---- T = (I + A)^-1, diagonal 16x16 blocks first (wave w < 4: block w)
-    if (w < 4 && lane < 16) {
-      const int j = lane;
-      float t[16], acc[16];
+    // ---- T = (I + A)^-1 by 16x16 blocks on the fp32 matrix path.  M holds
+    //      A^T above the diagonal; T goes below it, diagonal included.
+    //      Operand fragments of a 16x16 block X: A layout, lane (m, g) element
+    //      s = X[m][4g + s]; B layout, lane (n, g) element s = X[4g + s][n],
+    //      which is also the accumulator layout.
+    //      With fp32 inputs waves 4-7 build the Kt tiles meanwhile.
+    const int g4 = 4 * gq;
+    // A layout of the block (R0, J0) of A, J0 < R0: A[16R0 + m][16J0 + 4g + s]
+    auto a_of_A = [&](int R0, int J0, float x[4]) {
 #pragma unroll
-      for (int s2 = 0; s2 < 16; ++s2) acc[s2] = 0.f;
+      for (int s2 = 0; s2 < 4; ++s2) x[s2] = sm.M[(16 * J0 + g4 + s2) * S::kMP + 16 * R0 + m];
+    };
+    // B layout of the block (J0, I0) of T, J0 >= I0 (diagonal blocks masked)
+    auto b_of_T = [&](int J0, int I0, float x[4]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        t[r] = (r == j) ? 1.f : (r < j ? 0.f : -acc[r]);
-#pragma unroll
-        for (int s2 = r + 1; s2 < 16; ++s2) acc[s2] += sm.M[(f + r) * S::kMP + f + s2] * t[r];   // A[f+s2][f+r]
+      for (int s2 = 0; s2 < 4; ++s2) {
+        const float t = sm.M[(16 * J0 + g4 + s2) * S::kMP + 16 * I0 + m];
+        x[s2] = (J0 > I0 || g4 + s2 >= m) ? t : 0.f;
       }
+    };
+    // A layout of the block (R0, K0) of T, R0 >= K0 (diagonal blocks masked)
+    auto a_of_T = [&](int R0, int K0, float x[4]) {
+      const f32x4 t = ld4(sm.M + (16 * R0 + m) * S::kMP + 16 * K0 + g4);
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (r >= j) sm.M[(f + r) * S::kMP + f + j] = t[r];
-    } else if (w >= 4) {
+      for (int s2 = 0; s2 < 4; ++s2) x[s2] = (R0 > K0 || g4 + s2 <= m) ? t[s2] : 0.f;
+    };
+    auto as4 = [](const f32x4& c, float x[4]) { x[0] = c[0]; x[1] = c[1]; x[2] = c[2]; x[3] = c[3]; };
+    // -c stored as the block (R0, I0) of T
+    auto store_negT = [&](int R0, int I0, const f32x4& c) {
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) sm.M[(16 * R0 + g4 + ii) * S::kMP + 16 * I0 + m] = -c[ii];
+    };
+
+    // Diagonal blocks, wave w < 4 takes block w: with L the strictly lower
+    // block of A, (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8) since L^16 = 0.
+    // The A layout of X^T is the B layout of X, so the squares are formed in
+    // both orientations, each from the other's accumulators.
+    if (w < 4) {
+      float aL[4], bL[4];
+      {
+        const f32x4 t = ld4(sm.M + (f + m) * S::kMP + f + g4);   // L[4g+s][m] = M[f+m][f+4g+s]
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          bL[s2] = (g4 + s2 > m) ? t[s2] : 0.f;
+          const float u = sm.M[(f + g4 + s2) * S::kMP + f + m];   // L[m][4g+s]
+          aL[s2] = (m > g4 + s2) ? u : 0.f;
+        }
+      }
+      const f32x4 z = {0, 0, 0, 0};
+      f32x4 L2 = z, L2t = z, L4 = z, L4t = z, L8t = z;
+      mma16_f32(L2, aL, bL);     // L L
+      mma16_f32(L2t, bL, aL);    // L^T L^T: accumulators = A layout of L^2
+      float x[4], y[4];
+      as4(L2t, x); as4(L2, y);
+      mma16_f32(L4, x, y);       // L^2 L^2
+      as4(L2, x); as4(L2t, y);
+      mma16_f32(L4t, x, y);      // (L^T)^4: A layout of L^4
+      as4(L4, x); as4(L4t, y);
+      mma16_f32(L8t, x, y);      // (L^T)^8: A layout of L^8
+      f32x4 P;
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) P[s2] = (g4 + s2 == m ? 1.f : 0.f) - bL[s2];   // I - L
+      as4(L2t, x); as4(P, y);
+      mma16_f32(P, x, y);        // (I + L^2)(I - L)
+      as4(L4t, x); as4(P, y);
+      mma16_f32(P, x, y);
+      as4(L8t, x); as4(P, y);
+      mma16_f32(P, x, y);
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii)
+        if (g4 + ii >= m) sm.M[(f + g4 + ii) * S::kMP + f + m] = P[ii];
+    } else if constexpr (!S::kXT) {
       for (int t = w - 4; t < NKT / 2; t += 4) kt_tile(t);
     }
     block_sync();
-    // ---- off-diagonal blocks, one block column per wave, kept in registers:
-    //      T_RI = -T_RR sum_{J=I}^{R-1} A_RJ T_JI for R = I+1 .. 3, I = w
+
+    // Off-diagonal blocks in two levels: T_10 and T_32 from the diagonal
+    // blocks, then T_20, T_21, T_30, T_31 from those, T_RI = -T_RR sum_J A_RJ T_JI.
+    f32x4 y0 = {0, 0, 0, 0}, y1 = {0, 0, 0, 0};
     if (w < 4) {
-      const int I = w;
-      f32x4 tcol[4];   // T_JI for J > I, accumulator layout (= operand layout with k = rows)
-#pragma unroll
-      for (int RR = 1; RR < 4; ++RR) {
-        if (RR <= I) continue;
-        f32x4 mm = {0, 0, 0, 0};
-#pragma unroll
-        for (int J = 0; J < 3; ++J) {
-          if (J < I || J >= RR) continue;
-          float a[4], bb[4];
-#pragma unroll
-          for (int s2 = 0; s2 < 4; ++s2) {
-            a[s2] = sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * RR + m];   // A[16RR+m][16J+4gq+s2]
-            if (J == I)   // T_II: lower part of the diagonal block
-              bb[s2] = (4 * gq + s2 >= m) ? sm.M[(16 * J + 4 * gq + s2) * S::kMP + 16 * I + m] : 0.f;
-            else
-              bb[s2] = tcol[J][s2];
-          }
-          mma16_f32(mm, a, bb);
-        }
-        float a[4];
-        const f32x4 trr = ld4(sm.M + (16 * RR + m) * S::kMP + 16 * RR + 4 * gq);
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) a[s2] = (m >= 4 * gq + s2) ? trr[s2] : 0.f;   // T_RR[m][4gq+s2]
-        float bb[4] = {mm[0], mm[1], mm[2], mm[3]};
-        f32x4 res = {0, 0, 0, 0};
-        mma16_f32(res, a, bb);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          res[ii] = -res[ii];
-          sm.M[(16 * RR + 4 * gq + ii) * S::kMP + 16 * I + m] = res[ii];
-        }
-        tcol[RR] = res;
+      float a[4], b[4];
+      if (w == 0) {          // T_10 = -D_1 A_10 D_0; then A_20 D_0 for T_20
+        f32x4 t = {0, 0, 0, 0}, u = {0, 0, 0, 0};
+        b_of_T(0, 0, b);
+        a_of_A(1, 0, a); mma16_f32(t, a, b);
+        a_of_A(2, 0, a); mma16_f32(y0, a, b);
+        a_of_T(1, 1, a); as4(t, b); mma16_f32(u, a, b);
+        store_negT(1, 0, u);
+      } else if (w == 1) {   // T_32 = -D_3 A_32 D_2; then A_21 D_1 and A_31 D_1 for T_31
+        f32x4 t = {0, 0, 0, 0}, u = {0, 0, 0, 0};
+        b_of_T(2, 2, b);
+        a_of_A(3, 2, a); mma16_f32(t, a, b);
+        b_of_T(1, 1, b);
+        a_of_A(2, 1, a); mma16_f32(y0, a, b);
+        a_of_A(3, 1, a); mma16_f32(y1, a, b);
+        a_of_T(3, 3, a); as4(t, b); mma16_f32(u, a, b);
+        store_negT(3, 2, u);
+      } else if (w == 2) {   // A_21 D_1 for T_21
+        b_of_T(1, 1, b);
+        a_of_A(2, 1, a); mma16_f32(y0, a, b);
+      } else {               // A_20 D_0 and A_30 D_0 for T_30
+        b_of_T(0, 0, b);
+        a_of_A(2, 0, a); mma16_f32(y0, a, b);
+        a_of_A(3, 0, a); mma16_f32(y1, a, b);
       }
-    } else {
-      for (int t = NKT / 2 + w - 4; t < NKT; t += 4) kt_tile(t);
+    } else if constexpr (!S::kXT) {
+      for (int t = NKT / 2 + w - 4; t < 3 * NKT / 4; t += 4) kt_tile(t);
+    }
+    block_sync();
+    if (w < 4) {
+      float a[4], b[4];
+      f32x4 u = {0, 0, 0, 0};
+      if (w == 0) {          // T_20 = -D_2 (A_20 D_0 + A_21 T_10)
+        a_of_A(2, 1, a); b_of_T(1, 0, b); mma16_f32(y0, a, b);
+        a_of_T(2, 2, a); as4(y0, b); mma16_f32(u, a, b);
+        store_negT(2, 0, u);
+      } else if (w == 1) {   // T_31 = -(T_32 A_21 D_1 + D_3 A_31 D_1)
+        a_of_T(3, 2, a); as4(y0, b); mma16_f32(u, a, b);
+        a_of_T(3, 3, a); as4(y1, b); mma16_f32(u, a, b);
+        store_negT(3, 1, u);
+      } else if (w == 2) {   // T_21 = -D_2 A_21 D_1
+        a_of_T(2, 2, a); as4(y0, b); mma16_f32(u, a, b);
+        store_negT(2, 1, u);
+      } else {               // T_30 = -(T_32 (A_20 D_0 + A_21 T_10) + D_3 (A_30 D_0 + A_31 T_10))
+        b_of_T(1, 0, b);
+        a_of_A(2, 1, a); mma16_f32(y0, a, b);
+        a_of_A(3, 1, a); mma16_f32(y1, a, b);
+        a_of_T(3, 2, a); as4(y0, b); mma16_f32(u, a, b);
+        a_of_T(3, 3, a); as4(y1, b); mma16_f32(u, a, b);
+        store_negT(3, 0, u);
+      }
+    } else if constexpr (!S::kXT) {
+      for (int t = 3 * NKT / 4 + w - 4; t < NKT; t += 4) kt_tile(t);
     }
     block_sync();
 
@@ -575,14 +775,6 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       }
     };
 
-    // exp(G) in place of G from here on; the shared T fragments alongside.
-    for (int e4 = tid; e4 < kChunk * K / 4; e4 += kIntraThreads) {
-      const int r = e4 / (K / 4), c = (e4 % (K / 4)) * 4;
-      f32x4 x = ld4(sm.G + r * S::kGP + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = __expf(x[i]);
-      *reinterpret_cast<f32x4*>(sm.G + r * S::kGP + c) = x;
-    }
     if constexpr (kTShared) {
       for (int tt = w; tt < 12; tt += kIntraWaves) {
         const int pr = tt % 6, rb = pr < 2 ? pr : (pr + 2) / 2, kb = pr < 2 ? 0 : pr & 1;
@@ -590,7 +782,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       }
     }
     block_sync();
-    if (tid < K) reinterpret_cast<float*>(rec + L::kGc)[tid] = sm.G[(kChunk - 1) * S::kGP + tid];
+    if (tid < K) reinterpret_cast<float*>(rec + L::kGc)[tid] = __expf(sm.G[(kChunk - 1) * S::kGP + tid]);
 
     // ---- -W: W^T tiles D[c][r] for key-channel block cb = w and every row
     //      block; a W operand tile spans two channel blocks, so each wave
@@ -604,7 +796,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 32 * kb + kperm(gq, j);
-          x[j] = sm.beta[i] * ld1(kbuf + SK::idx(i, c)) * sm.nk[i] * sm.G[i * S::kGP + c];
+          x[j] = sm.beta[i] * ld1(kbuf + SK::idx(i, c)) * sm.nk[i] * __expf(sm.G[i * S::kGP + c]);
         }
         xf[kb].set(x);
       }
@@ -623,7 +815,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
     // ---- U = T diag(beta) V for value block vb = w: v has landed in the g buffer
     wait_loads();
-    block_sync();
+    block_sync();   // k is dead: the next item's keys stream in
+    if (has_next) issue_k(nxt);
     if (len < kChunk)
       for (int e = tid; e < (kChunk - len) * V; e += kIntraThreads) gvbuf[SV::idx(len + e / V, e % V)] = TI(0);
     block_sync();
@@ -648,7 +841,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       }
     }
     block_sync();   // k and the g/v buffer are free
-    if (!S::kDB && has_next) issue_kgb(nxt, 0);
+    if (!S::kDB && has_next) issue_gb(nxt, 0);
   }
 }
 

@@ -417,6 +417,216 @@ __global__ __launch_bounds__(Roles<TPW>::kThreads) void kda_recur_kernel(RecurPa
   }
 }
 
+// One value tile per workgroup, operands straight to registers.  Each
+// compute wave's share of a record (its token block of Wn, U, Qg and Aqk,
+// its key-channel blocks of Kt and exp(G_C)) is read by that wave alone, so
+// it is loaded into the wave's registers one chunk ahead, each group right
+// after its last use; only S and Delta pass through LDS.  Two barriers per
+// chunk: B1 after the Delta phase (Delta visible), B2 at the end (the new
+// state visible, the Delta buffer free).  The fifth wave pulls records a few
+// chunks ahead into L2.
+template <class TI, class TO, int K, int V>
+__global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_kernel(RecurParams p) {
+  using P = Prec<TI>;
+  using PS = typename P::S;
+  using PD = typename P::D;
+  using PW = typename P::W;
+  using PK = typename P::Kt;
+  using PQ = typename P::Q;
+  using L = RecordLayout<TI, K, V>;
+  constexpr int kPrefetchWave = kComputeWaves;
+  constexpr int NV = V / kVT;      // workgroups per (sequence, head)
+  constexpr int SP = K + 8;        // LDS row pitch of the state operand
+  constexpr int DP = kChunk + 8;   // LDS row pitch of the Delta operand
+  constexpr int NCB = K / 64;      // key-channel blocks of the state per wave
+  constexpr int KB = K / 32;       // 32-deep key slabs
+  __shared__ __align__(16) char s_state[LdsPlane<PS>::template bytes<kVT, SP>()];
+  __shared__ __align__(16) char s_delta[LdsPlane<PD>::template bytes<kVT, DP>()];
+  __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15, gq = lane >> 4;
+  const int64_t H = p.H;
+
+  // XCD-aware decode: the NV workgroups of one (sequence, head) sit on
+  // workgroup ids with equal id % 8, which the dispatcher places on one XCD,
+  // so they share that XCD's L2 copy of the chunk records.
+  const int64_t id = blockIdx.x;
+  const int64_t seq_head = (id / (8 * NV)) * 8 + id % 8;
+  const int j = (int)((id / 8) % NV);
+  const int64_t n_seq_heads = p.packed ? (int64_t)p.hdr->n_segments * H : p.n_seq_heads_fixed;
+  if (seq_head >= n_seq_heads) return;
+  const int64_t h = seq_head % H, sq = seq_head / H;
+
+  int64_t b, slot, n_chunks, first_chunk, t_begin, seq_len;
+  if (p.packed) {
+    const SegEntry se = p.segs[sq];
+    b = se.b;
+    slot = ((int64_t)se.b * p.n_max + se.local) * H + h;
+    n_chunks = se.n_chunks;
+    first_chunk = se.chunk_begin;
+    t_begin = se.t0;
+    seq_len = se.len;
+  } else {
+    b = sq;
+    slot = b * H + h;
+    n_chunks = p.nc_fixed;
+    first_chunk = b * p.nc_fixed;
+    t_begin = 0;
+    seq_len = p.T;
+  }
+  auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
+
+  // ---- L2 prefetch wave: touches this workgroup's 1/NV share of the record
+  // kPrefetchAhead chunks ahead (every 64-byte segment once).
+  if (wave == kPrefetchWave) {
+    constexpr int SEGS = (int)(L::kBytes / 64);
+    constexpr int SHARE = (SEGS + NV - 1) / NV;
+    auto prefetch = [&](int64_t n) {
+      const char* r = record(n);
+#pragma unroll
+      for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
+        const int e = i * kWave + lane, seg = j * SHARE + e;
+        if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
+      }
+    };
+    for (int64_t n = 1; n <= kPrefetchAhead && n < n_chunks; ++n) prefetch(n);
+    block_sync();
+    for (int64_t n = 0; n < n_chunks; ++n) {
+      if (n + kPrefetchAhead + 1 < n_chunks) prefetch(n + kPrefetchAhead + 1);
+      block_sync();   // B1
+      block_sync();   // B2
+    }
+    vm_wait<0>();
+    return;
+  }
+
+  // ---- compute wave w: token block w, key-channel blocks w*NCB .. +NCB-1
+  const int w = wave;
+  TO* out = static_cast<TO*>(p.o);
+  const int v0 = kVT * j;
+  PW wn[KB];
+  f32x4 u;
+  PK kt[NCB][2];
+  f32x4 gc[NCB];
+  PQ qg[KB], aq[2];
+  auto load_w = [&](const char* r) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
+    u = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + j) * 1024)[lane];
+  };
+  auto load_kt = [&](const char* r) {
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) kt[c][kb].load(r + L::kKt + (int64_t)((w * NCB + c) * 2 + kb) * tile_bytes<PK>(), lane);
+      gc[c] = reinterpret_cast<const f32x4*>(r + L::kGc)[4 * (w * NCB + c) + gq];
+    }
+  };
+  auto load_q = [&](const char* r) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PQ>(), lane);
+  };
+
+  // State slice: lane (column v0 + m, rows 16cb + 4gq + i) of its blocks.
+  f32x4 st[NCB];
+#pragma unroll
+  for (int c = 0; c < NCB; ++c) {
+    const int c0 = 16 * (w * NCB + c) + 4 * gq;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      st[c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
+    float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
+    LdsPlane<PS>::template write4<kVT, SP>(s_state, m, c0, x);
+  }
+  if (n_chunks > 0) {
+    const char* r0 = record(0);
+    load_w(r0);
+    load_kt(r0);
+    load_q(r0);
+  }
+  block_sync();
+
+  for (int64_t n = 0; n < n_chunks; ++n) {
+    const int64_t t0 = t_begin + n * kChunk;
+    const int len = (int)min<int64_t>(kChunk, seq_len - n * kChunk);
+    const char* rn1 = record(n + 1 < n_chunks ? n + 1 : n);
+
+    // Delta = U - W S for tokens 16w..16w+15; the S operand stays in
+    // registers for the output phase.  Two accumulators halve the
+    // dependent chain.
+    PS sf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sf[kb] = LdsPlane<PS>::template read<kVT, SP>(s_state, m, kb, gq);
+    {
+      f32x4 d0 = u, d1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int kb = 0; kb < KB; kb += 2) {
+        mma(d0, wn[kb], sf[kb]);
+        if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
+      }
+      float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
+      LdsPlane<PD>::template write4<kVT, DP>(s_delta, m, 16 * w + 4 * gq, x);
+    }
+    load_w(rn1);
+    block_sync();   // B1
+
+    // S <- diag(exp(G_C)) S + Kt^T Delta
+    PD dd[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dd[kb] = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int c0 = 16 * (w * NCB + c) + 4 * gq;
+      f32x4 a0, a1 = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a0[i] = st[c][i] * gc[c][i];
+      mma(a0, kt[c][0], dd[0]);
+      mma(a1, kt[c][1], dd[1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[c][i] = a0[i] + a1[i];
+      float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
+      LdsPlane<PS>::template write4<kVT, SP>(s_state, m, c0, x);
+    }
+    load_kt(rn1);
+
+    // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
+    f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 2) {
+      mma(o0, qg[kb], sf[kb]);
+      if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
+    }
+    mma(o1, aq[0], dd[0]);
+    if (w >= 2) mma(o0, aq[1], dd[1]);
+    load_q(rn1);
+    const int rw = 16 * w + 4 * gq;
+    const int64_t ob = ((b * p.T + t0 + rw) * H + h) * V + v0 + m, rs = H * V;
+    if (len == kChunk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) store_out(out, ob + i * rs, o0[i] + o1[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (rw + i < len) store_out(out, ob + i * rs, o0[i] + o1[i]);
+    }
+    block_sync();   // B2
+  }
+
+  if (p.fin) {
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int c0 = 16 * (w * NCB + c) + 4 * gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.fin[(slot * K + c0 + i) * V + v0 + m] = st[c][i];
+    }
+  }
+}
+
 template <class TI, class TO, int K, int V, int TPW>
 hipError_t launch_recur_w(const RecurParams& p, int64_t seq_heads, hipStream_t stream) {
   constexpr int NVW = V / kVT / TPW;
@@ -435,7 +645,10 @@ hipError_t launch_recur_t(const CallArgs& a) {
   // Two tiles per workgroup once one tile per workgroup would need several
   // rounds of workgroups over the CUs.
   if (seq_heads * (V / kVT) > 2 * (int64_t)cu_count()) return launch_recur_w<TI, TO, K, V, 2>(p, seq_heads, a.stream);
-  return launch_recur_w<TI, TO, K, V, 1>(p, seq_heads, a.stream);
+  const int64_t grid = (seq_heads + 7) / 8 * 8 * (V / kVT);
+  hipLaunchKernelGGL((kda_recur_reg_kernel<TI, TO, K, V>), dim3((unsigned)grid), dim3((kComputeWaves + 1) * kWave), 0,
+                     a.stream, p);
+  return hipGetLastError();
 }
 
 template <class TI, class TO>
