@@ -175,17 +175,52 @@ struct ItemInfo {
   int len;
 };
 
-__device__ __forceinline__ ItemInfo item_info(const IntraParams& p, int64_t item) {
+// Position of an item = chunk * H + h, with chunk = b * nc_fixed + ci for
+// fixed rows.  Integer division is a long instruction sequence on the GPU,
+// so it is done once per workgroup; the item loop advances the position by
+// a constant stride with carries.
+struct ItemPos {
+  int64_t chunk, h, b, ci;
+};
+
+__device__ __forceinline__ ItemPos item_pos(const IntraParams& p, int64_t item) {
+  ItemPos q;
+  q.h = item % p.H;
+  q.chunk = item / p.H;
+  q.b = p.packed ? 0 : q.chunk / p.nc_fixed;
+  q.ci = p.packed ? 0 : q.chunk % p.nc_fixed;
+  return q;
+}
+
+// q advanced by d (a position used as a stride: d.chunk whole chunks and
+// d.h heads, d.ci < nc_fixed after d.b whole rows).
+__device__ __forceinline__ ItemPos item_advance(const IntraParams& p, ItemPos q, const ItemPos& d) {
+  q.h += d.h;
+  q.chunk += d.chunk;
+  q.b += d.b;
+  q.ci += d.ci;
+  if (q.h >= p.H) {
+    q.h -= p.H;
+    q.chunk += 1;
+    q.ci += 1;
+  }
+  if (!p.packed && q.ci >= p.nc_fixed) {
+    q.ci -= p.nc_fixed;
+    q.b += 1;
+  }
+  return q;
+}
+
+__device__ __forceinline__ ItemInfo item_info(const IntraParams& p, const ItemPos& q) {
   ItemInfo it;
-  it.h = item % p.H;
-  const int64_t chunk = item / p.H;
+  it.h = q.h;
   if (p.packed) {
-    const ChunkEntry ce = p.chunks[chunk];
+    const ChunkEntry ce = p.chunks[q.chunk];
     it.tok0 = (int64_t)ce.b * p.T + ce.t0;
     it.len = ce.len;
   } else {
-    const int64_t b = chunk / p.nc_fixed, t0 = (chunk % p.nc_fixed) * kChunk;
-    it.tok0 = b * p.T + t0;
+    const int64_t t0 = q.ci * kChunk;
+    it.tok0 = q.b * p.T + t0;
     it.len = (int)min<int64_t>(kChunk, p.T - t0);
   }
   return it;
@@ -246,21 +281,25 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
   };
 
   {
-    const ItemInfo first = item_info(p, blockIdx.x);
+    const ItemInfo first = item_info(p, item_pos(p, blockIdx.x));
     issue_k(first);
     issue_gb(first, 0);
     issue_q(first);
   }
 
   int it_no = 0;
+  const ItemPos stride = item_pos(p, gridDim.x);
+  ItemPos pos = item_pos(p, blockIdx.x);
   for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x, ++it_no) {
     const int cb = S::kDB ? (it_no & 1) : 0;
-    const ItemInfo cur = item_info(p, item);
+    const ItemInfo cur = item_info(p, pos);
     const int len = cur.len;
     const int64_t h = cur.h;
     const int64_t nxt_item = item + gridDim.x;
     const bool has_next = nxt_item < n_items;
-    const ItemInfo nxt = has_next ? item_info(p, nxt_item) : cur;
+    const ItemPos npos = item_advance(p, pos, stride);
+    const ItemInfo nxt = has_next ? item_info(p, npos) : cur;
+    pos = npos;
     char* rec = p.records + item * p.record_bytes;
     TI* kbuf = sm.k;
     TI* gvbuf = sm.gv[cb];
