@@ -99,6 +99,13 @@ kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+// The forward of both entry points; gate_mode 0 takes g as the log decay,
+// 1 and 2 activate it in the kernel (without / with the safe gate).
+kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, int gate_mode, const float* a_log, const float* dt_bias,
+                     const float* initial_state, const int32_t* segment_ids, void* o, float* final_state,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -116,6 +123,27 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void
                            const void* g, const void* beta, const float* initial_state,
                            const int32_t* segment_ids, void* o, float* final_state, void* workspace,
                            size_t workspace_bytes, void* stream) {
+  return forward(desc, q, k, v, g, beta, 0, nullptr, nullptr, initial_state, segment_ids, o, final_state,
+                 workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* A_log, const float* dt_bias,
+                                 const float* initial_state, const int32_t* segment_ids, void* o,
+                                 float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  const int mode = (desc != nullptr && desc->safe_gate) ? 2 : 1;
+  return forward(desc, q, k, v, g, beta, mode, A_log, dt_bias, initial_state, segment_ids, o, final_state,
+                 workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, int gate_mode, const float* a_log, const float* dt_bias,
+                     const float* initial_state, const int32_t* segment_ids, void* o, float* final_state,
+                     void* workspace, size_t workspace_bytes, void* stream) {
   const bool has_seg = segment_ids != nullptr;
   Plan plan;
   kda_status_t st = validate(desc, has_seg, &plan);
@@ -128,6 +156,10 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void
     const void* ptrs[] = {q, k, v, g, beta, o, initial_state, segment_ids, final_state, workspace};
     for (const void* ptr : ptrs)
       if (ptr && !aligned16(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
+    const void* gate_ptrs[] = {a_log, dt_bias};
+    for (const void* ptr : gate_ptrs)
+      if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3) != 0)
+        return fail(KDA_ERR_INVALID_ARGUMENT, "A_log and dt_bias must be float-aligned");
   }
   if (workspace_bytes < plan.total || (plan.total > 0 && workspace == nullptr))
     return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
@@ -144,6 +176,10 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void
   a.cmax = plan.cmax;
   a.smax = plan.smax;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.gate_mode = gate_mode;
+  a.lower_bound = d.lower_bound;
+  a.a_log = a_log;
+  a.dt_bias = dt_bias;
   a.init = initial_state;
   a.seg_ids = segment_ids;
   a.o = o;
@@ -172,6 +208,10 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return KDA_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, void* stream, uint32_t* flags) {
   if (flags == nullptr || workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "NULL argument");

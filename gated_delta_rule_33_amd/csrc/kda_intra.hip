@@ -87,6 +87,16 @@ struct IntraSmem {
   __device__ float* red_buf() { return kRedInQ ? reinterpret_cast<float*>(q) : scratch; }
 };
 
+// Activated log decay of the in-kernel gate for z = exp(A_log) (g + dt_bias):
+// mode 2 (safe gate) lower_bound * sigmoid(z), mode 1 log sigmoid(z) in the
+// form min(z, 0) - log(1 + exp(-|z|)), which neither overflows nor cancels.
+// Hardware exp, log and reciprocal (about one ulp each): the absolute error
+// of g stays near 1e-7, far below what the bf16 operands carry.
+__device__ __forceinline__ float gate_log_decay(int mode, float lower_bound, float z) {
+  if (mode == 2) return lower_bound * __builtin_amdgcn_rcpf(1.f + __expf(-z));
+  return fminf(z, 0.f) - __logf(1.f + __expf(-fabsf(z)));
+}
+
 // Four consecutive elements as floats.
 __device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 ld4(const uint16_t* p) {
@@ -159,6 +169,9 @@ __device__ __forceinline__ void mma16_f32(f32x4& c, const float a[4], const floa
 
 struct IntraParams {
   const void *q, *k, *v, *g, *beta;
+  int gate_mode;               // 0: g is the log decay; 1: log sigmoid(z); 2: lower_bound * sigmoid(z)
+  float lower_bound;
+  const float *a_log, *dt_bias;
   int64_t B, T, H;
   float scale;
   int l2norm;
@@ -269,12 +282,24 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
   // once would make the compiler wait for every load in flight, the
   // direct-to-LDS prefetches included.
   TI beta_next = TI(0);
+  // The gate parameters of the next item for this thread's two running-sum
+  // channels (raw A_log of its head, dt_bias of the channels), likewise.
+  constexpr int kSumPairs = K / 2;
+  const int c_sum = 2 * (tid % kSumPairs);
+  float alog_next = 0.f, db0_next = 0.f, db1_next = 0.f;
   auto issue_k = [&](const ItemInfo& it) {
     issue_rows<TI, K>(sm.k, gk_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
   };
   auto issue_gb = [&](const ItemInfo& it, int buf) {
     issue_rows<TI, K>(sm.gv[buf], gg_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
     beta_next = gb_[(it.tok0 + min(lane, it.len - 1)) * H + it.h];
+    if (p.gate_mode) {
+      if (p.a_log) alog_next = p.a_log[it.h];
+      if (p.dt_bias) {
+        db0_next = p.dt_bias[it.h * K + c_sum];
+        db1_next = p.dt_bias[it.h * K + c_sum + 1];
+      }
+    }
   };
   auto issue_q = [&](const ItemInfo& it) {
     issue_rows<TI, K>(sm.q, gq_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
@@ -322,11 +347,23 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
     // ---- running sum of g over the chunk, per channel
     {   // two channels per thread, rows in PARTS parts of RP
-      constexpr int PAIRS = K / 2, PARTS = kIntraThreads / PAIRS, RP = kChunk / PARTS;
+      constexpr int PAIRS = kSumPairs, PARTS = kIntraThreads / PAIRS, RP = kChunk / PARTS;
       const int c = 2 * (tid % PAIRS), part = tid / PAIRS, r0 = part * RP;
       float g0[RP], g1[RP];
 #pragma unroll
       for (int i = 0; i < RP; ++i) ld2(gvbuf + SK::idx(r0 + i, c), g0[i], g1[i]);   // all reads in flight
+      if (p.gate_mode) {
+        // In-kernel gate: z = exp(A_log_h) (g + dt_bias_hc); the log decay is
+        // lower_bound * sigmoid(z) under the safe gate, else log sigmoid(z).
+        // Rows past the chunk keep g = 0.
+        const float ea = __expf(alog_next);
+#pragma unroll
+        for (int i = 0; i < RP; ++i) {
+          if (r0 + i >= len) continue;
+          g0[i] = gate_log_decay(p.gate_mode, p.lower_bound, ea * (g0[i] + db0_next));
+          g1[i] = gate_log_decay(p.gate_mode, p.lower_bound, ea * (g1[i] + db1_next));
+        }
+      }
 #pragma unroll
       for (int i = 1; i < RP; ++i) {
         g0[i] += g0[i - 1];
@@ -887,7 +924,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
 template <class TI, int K, int V>
 hipError_t launch_intra_t(const CallArgs& a) {
-  IntraParams p{a.q, a.k, a.v, a.g, a.beta, a.B, a.T, a.H, a.scale, a.l2norm, a.nc_fixed,
+  IntraParams p{a.q, a.k, a.v, a.g, a.beta, a.gate_mode, a.lower_bound, a.a_log, a.dt_bias, a.B, a.T, a.H,
+                a.scale, a.l2norm, a.nc_fixed,
                 a.n_max > 0, a.hdr, a.chunks, a.records, a.record_bytes};
   const size_t smem = sizeof(IntraSmem<TI, K, V>);
   auto kern = kda_intra_kernel<TI, K, V>;

@@ -25,6 +25,9 @@ struct CallArgs {
   int64_t nc_fixed;            // chunks per row without segment_ids: ceil(T / 64)
   int64_t cmax, smax;          // chunk / segment capacities of the tables and records
   const void *q, *k, *v, *g, *beta;
+  int gate_mode;               // 0: g is the log decay; 1: log sigmoid(z); 2: lower_bound * sigmoid(z)
+  float lower_bound;
+  const float *a_log, *dt_bias;   // gate parameters ([H], [H,K]) or NULL
   const float* init;
   const int32_t* seg_ids;
   void* o;

@@ -21,8 +21,8 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 
-EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer",
-            "kda_last_error", "kda_version")
+EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_flags",
+            "kda_set_launch_observer", "kda_last_error", "kda_version")
 
 # void (*)(const char* kernel_name, void* stream, int phase, void* user)
 LAUNCH_OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p)
@@ -58,6 +58,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_gated.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_fwd_gated.restype = ctypes.c_int
     lib.kda_chunk_fwd_flags.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_uint32)]
     lib.kda_chunk_fwd_flags.restype = ctypes.c_int
     lib.kda_set_launch_observer.argtypes = [LAUNCH_OBSERVER, ctypes.c_void_p]
@@ -121,12 +123,15 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
     with segment_ids).  segment_ids: int32 [B,T], 1-based, 0 = padding; needs N_max.
     out_dtype: dtype of o (default float32: see the precision notes of the
     library; bfloat16 rounds the result once more).
+    use_gate_in_kernel: g holds raw gate values, activated inside the kernel
+    with A_log (fp32 [H] or None) and dt_bias (fp32 [H, K] or None):
+    z = exp(A_log) (g + dt_bias), log decay lower_bound * sigmoid(z) with
+    safe_gate, log sigmoid(z) without.
     Returns (o, final_state or None).
     """
     import torch
-    if A_log is not None or dt_bias is not None or use_gate_in_kernel:
-        raise NotImplementedError("in-kernel gate activation (A_log, dt_bias) is not implemented: pass the "
-                                  "activated log decay as g")
+    if (A_log is not None or dt_bias is not None) and not use_gate_in_kernel:
+        raise ValueError("A_log and dt_bias are used only with use_gate_in_kernel=True")
     if disable_recompute:
         raise NotImplementedError("disable_recompute concerns the backward pass, which is not implemented")
     if cp_context is not None:
@@ -144,6 +149,7 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
     V = v.shape[-1]
     if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:3]) != (B, T, H) or tuple(beta.shape) != (B, T, H):
         raise ValueError("shape mismatch: q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H]")
+    gate_args = _gate_tensors(use_gate_in_kernel, A_log, dt_bias, H, K, q.device)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     n_max = 0
     if segment_ids is not None:
@@ -165,12 +171,34 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
     o = torch.empty((B, T, H, V), dtype=out_dtype, device=q.device)
     fin = torch.empty(state_shape, dtype=torch.float32, device=q.device) if output_final_state else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = load_library().kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                      _ptr(initial_state), _ptr(segment_ids), _ptr(o), _ptr(fin),
-                                      _ptr(workspace), ctypes.c_size_t(workspace.numel()),
-                                      ctypes.c_void_p(stream))
-    _raise_for(st, "kda_chunk_fwd")
+    lib = load_library()
+    tail = (_ptr(initial_state), _ptr(segment_ids), _ptr(o), _ptr(fin), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
+    if use_gate_in_kernel:
+        st = lib.kda_chunk_fwd_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(gate_args[0]), _ptr(gate_args[1]), *tail)
+        _raise_for(st, "kda_chunk_fwd_gated")
+    else:
+        st = lib.kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), *tail)
+        _raise_for(st, "kda_chunk_fwd")
     return o, fin
+
+
+def _gate_tensors(use_gate_in_kernel, A_log, dt_bias, H, K, device):
+    """Checked (A_log, dt_bias) for the gated entry point (each None or a
+    contiguous fp32 device tensor of shape [H] / [H, K])."""
+    import torch
+    if not use_gate_in_kernel:
+        return None, None
+    out = []
+    for name, t, shape in (("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, K))):
+        if t is None:
+            out.append(None)
+            continue
+        if t.dtype != torch.float32 or tuple(t.shape) != shape or not t.is_contiguous() or t.device != device:
+            raise ValueError(f"{name} must be a contiguous float32 {shape} tensor on the inputs' device")
+        out.append(t)
+    return tuple(out)
 
 
 def set_launch_observer(fn):
@@ -187,15 +215,18 @@ def set_launch_observer(fn):
 
 
 class PreparedCall:
-    """kda_chunk_fwd with every argument marshalled once: ``enqueue()`` only
-    crosses the C ABI (for timing loops).  Holds references to its tensors."""
+    """kda_chunk_fwd (or kda_chunk_fwd_gated) with every argument marshalled
+    once: ``enqueue()`` only crosses the C ABI (for timing loops).  Holds
+    references to its tensors."""
 
-    def __init__(self, desc: KdaFwdDesc, tensors: dict, workspace, stream: int):
+    def __init__(self, desc: KdaFwdDesc, tensors: dict, workspace, stream: int, gated: bool = False):
         self.desc, self.tensors, self.workspace = desc, tensors, workspace
-        names = ("q", "k", "v", "g", "beta", "initial_state", "segment_ids", "o", "final_state")
+        names = ("q", "k", "v", "g", "beta") + (("A_log", "dt_bias") if gated else ()) + \
+            ("initial_state", "segment_ids", "o", "final_state")
         self.args = [ctypes.byref(desc)] + [_ptr(tensors.get(n)) for n in names] + \
             [_ptr(workspace), ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)]
-        self.fn = load_library().kda_chunk_fwd
+        lib = load_library()
+        self.fn = lib.kda_chunk_fwd_gated if gated else lib.kda_chunk_fwd
 
     def enqueue(self):
         _raise_for(self.fn(*self.args), "kda_chunk_fwd")
@@ -203,7 +234,8 @@ class PreparedCall:
 
 def prepare_call(q, k, v, g, beta, scale=None, initial_state=None, output_final_state=False,
                  use_qk_l2norm_in_kernel=False, safe_gate=False, lower_bound=None, segment_ids=None,
-                 N_max=None, out_dtype=None) -> PreparedCall:
+                 N_max=None, out_dtype=None, use_gate_in_kernel=False, A_log=None,
+                 dt_bias=None) -> PreparedCall:
     """Allocate o, final state and workspace for one shape and return a
     PreparedCall that enqueues the forward on the current stream."""
     import torch
@@ -215,11 +247,13 @@ def prepare_call(q, k, v, g, beta, scale=None, initial_state=None, output_final_
                      safe_gate, lower_bound if safe_gate else None, n_max)
     ws = torch.empty(max(workspace_size(desc, segment_ids is not None), 1), dtype=torch.uint8, device=q.device)
     state_shape = (B, H, K, V) if segment_ids is None else (B, n_max, H, K, V)
-    t = dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state, segment_ids=segment_ids,
-             o=torch.empty((B, T, H, V), dtype=out_dtype, device=q.device),
+    a_log, dt_b = _gate_tensors(use_gate_in_kernel, A_log, dt_bias, H, K, q.device)
+    t = dict(q=q, k=k, v=v, g=g, beta=beta, A_log=a_log, dt_bias=dt_b, initial_state=initial_state,
+             segment_ids=segment_ids, o=torch.empty((B, T, H, V), dtype=out_dtype, device=q.device),
              final_state=torch.empty(state_shape, dtype=torch.float32, device=q.device) if output_final_state
              else None)
-    return PreparedCall(desc, t, ws, torch.cuda.current_stream(q.device).cuda_stream)
+    return PreparedCall(desc, t, ws, torch.cuda.current_stream(q.device).cuda_stream,
+                        gated=bool(use_gate_in_kernel))
 
 
 def read_flags(workspace) -> int:

@@ -103,6 +103,30 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward with the gate activated inside the kernel (chunk_kda options
+ * use_gate_in_kernel, A_log and dt_bias of the page "feat(kda): integrate KDA
+ * attention with tokamax backend and CP support", Public API; the layer's
+ * "Gate generation" step there activates the gate with a sigmoid from A_log
+ * and dt_bias; the safe gate has sigmoid lower-bound semantics).  g holds
+ * raw gate values; for head h and key channel c the kernel uses
+ *     z = exp(A_log[h]) * (g + dt_bias[h*K + c])
+ *     safe_gate:  log decay = lower_bound * sigmoid(z)   (in (lower_bound, 0))
+ *     otherwise:  log decay = log(sigmoid(z))            (decay = sigmoid(z))
+ * evaluated in fp32.
+ *   A_log    NULL (exp(A_log) = 1) or fp32 [H], device memory.
+ *   dt_bias  NULL (zero) or fp32 [H,K], device memory.
+ * Every other argument, the workspace size and the errors are those of
+ * kda_chunk_fwd.  A_log and dt_bias need no alignment beyond that of float.
+ */
+kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* A_log, const float* dt_bias,
+                                 const float* initial_state, const int32_t* segment_ids,
+                                 void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Waits for `stream`, then reads the KDA_FLAG_* word the last kda_chunk_fwd
  * call on this workspace left behind (0 when nothing was flagged).
  */

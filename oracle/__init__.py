@@ -59,6 +59,10 @@ def _lib(prec: str):
         fn.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, ctypes.c_double, ctypes.c_int,
                        p, p, i64, p, p, ctypes.c_int]
         fn.restype = ctypes.c_int
+        fg = lib.kda_oracle_fwd_gate
+        fg.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, ctypes.c_double, ctypes.c_int,
+                       ctypes.c_int, ctypes.c_double, p, p, p, p, i64, p, p, ctypes.c_int]
+        fg.restype = ctypes.c_int
         lib.kda_oracle_real_bytes.restype = ctypes.c_int
         _loaded[prec] = lib
     return _loaded[prec]
@@ -75,13 +79,19 @@ def default_threads() -> int:
 def kda_forward(q, k, v, g, beta, scale: Optional[float] = None, initial_state=None,
                 output_final_state: bool = False, use_qk_l2norm: bool = False,
                 segment_ids=None, max_segments: int = 0, precision: str = "f64",
-                num_threads: Optional[int] = None):
+                num_threads: Optional[int] = None, use_gate_in_kernel: bool = False,
+                A_log=None, dt_bias=None, safe_gate: bool = False,
+                lower_bound: Optional[float] = None):
     """Token-by-token KDA forward on the CPU.
 
     q, k, g: [B,T,H,K]; v: [B,T,H,V]; beta: [B,T,H]; all converted to fp32
     (callers pass the exact values the GPU sees).  initial_state: None, or fp32
     [B,H,K,V] (no segment_ids) / [B,max_segments,H,K,V] (with segment_ids).
     segment_ids: None or int32 [B,T], 1-based, 0 = padding.
+    use_gate_in_kernel: g holds raw gate values, activated with A_log (fp32
+    [H] or None) and dt_bias (fp32 [H,K] or None) as described in
+    kda_oracle.c: lower_bound * sigmoid(z) with safe_gate, log sigmoid(z)
+    without.
     Returns (o, final_state_or_None) as float64 arrays.
     """
     f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
@@ -104,14 +114,33 @@ def kda_forward(q, k, v, g, beta, scale: Optional[float] = None, initial_state=N
         init = f32(initial_state)
         if init.shape != state_shape:
             raise ValueError(f"initial_state must be {state_shape}")
+    a_log = dtb = None
+    gate_mode, lb = 0, 0.0
+    if use_gate_in_kernel:
+        gate_mode = 2 if safe_gate else 1
+        if safe_gate:
+            if lower_bound is None:
+                raise ValueError("the safe gate needs a lower_bound")
+            lb = float(lower_bound)
+        if A_log is not None:
+            a_log = f32(A_log)
+            if a_log.shape != (H,):
+                raise ValueError("A_log must be [H]")
+        if dt_bias is not None:
+            dtb = f32(dt_bias)
+            if dtb.shape != (H, K):
+                raise ValueError("dt_bias must be [H, K]")
+    elif A_log is not None or dt_bias is not None:
+        raise ValueError("A_log and dt_bias need use_gate_in_kernel")
     o = np.zeros((B, T, H, V), dtype=np.float64)
     fin = np.zeros(state_shape, dtype=np.float64) if output_final_state else None
     if num_threads is None:
         num_threads = default_threads()
-    rc = _lib(precision).kda_oracle_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                                         _ptr(beta), float(scale), int(bool(use_qk_l2norm)),
-                                         _ptr(init), _ptr(seg), int(max_segments), _ptr(o),
-                                         _ptr(fin), int(num_threads))
+    rc = _lib(precision).kda_oracle_fwd_gate(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                              _ptr(beta), float(scale), int(bool(use_qk_l2norm)),
+                                              gate_mode, lb, _ptr(a_log), _ptr(dtb),
+                                              _ptr(init), _ptr(seg), int(max_segments), _ptr(o),
+                                              _ptr(fin), int(num_threads))
     if rc != 0:
         raise ValueError(f"oracle: {ORACLE_ERRORS.get(rc, rc)}")
     return o, fin

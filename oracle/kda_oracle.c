@@ -29,7 +29,17 @@
  *     zero); padding tokens leave the state alone and get o = 0;
  *   - initial_state / output_final_state: one K x V state per (b, h), or per
  *     (b, segment, h) when segment_ids are given, segments numbered in order
- *     of appearance within the row, at most n_max of them.
+ *     of appearance within the row, at most n_max of them;
+ *   - use_gate_in_kernel with A_log, dt_bias (kda_oracle_fwd_gate): g holds
+ *     raw gate values that are activated here before use.  The pages name
+ *     the parameters and a sigmoid (layer pipeline, "Gate generation": the
+ *     activation is a sigmoid from A_log and dt_bias; page 2 follow-ups: the
+ *     safe gate has sigmoid lower-bound semantics with lower_bound in
+ *     [-5, 0)).  Reading taken here, per head h and key channel c:
+ *         z = exp(A_log_h) * (g_raw + dt_bias_{h,c})
+ *         safe gate:  g = lower_bound * sigmoid(z)    (in (lower_bound, 0))
+ *         otherwise:  g = log(sigmoid(z))             (decay exp(g) = sigmoid(z))
+ *     with A_log absent meaning exp(A_log) = 1 and dt_bias absent meaning 0.
  *
  * Arithmetic is in REAL (double by default; float in the fp32 build), sums
  * run over the channel index in ascending order, exp/sqrt from libm.
@@ -57,6 +67,10 @@ typedef struct {
   const float *q, *k, *v, *g, *beta;
   double scale;
   int l2norm;
+  int gate_mode;                /* 0: g is the log decay; 1: log sigmoid; 2: lower_bound * sigmoid */
+  double lower_bound;
+  const float *a_log;           /* [H] or NULL */
+  const float *dt_bias;         /* [H,K] or NULL */
   const float *initial_state;   /* may be NULL */
   const int32_t *segment_ids;   /* may be NULL */
   int64_t n_max;
@@ -69,6 +83,16 @@ typedef struct {
   int64_t first, stride;        /* items first, first+stride, ... over B*H */
   int status;
 } worker_t;
+
+/* The log decay of key channel c of head h for the stored gate value x. */
+static REAL gate_log_decay(const job_t *j, int64_t h, int64_t c, REAL x) {
+  if (j->gate_mode == 0) return x;
+  const REAL a = j->a_log ? rexp((REAL)j->a_log[h]) : (REAL)1;
+  const REAL z = a * (x + (j->dt_bias ? (REAL)j->dt_bias[h * j->K + c] : (REAL)0));
+  const REAL sig = (REAL)1 / ((REAL)1 + rexp(-z));
+  if (j->gate_mode == 2) return (REAL)j->lower_bound * sig;
+  return (REAL)log((double)sig);
+}
 
 /* Index of the state slot for (b, seg, h) in [B,H,K,V] or [B,N_max,H,K,V]. */
 static int64_t state_offset(const job_t *j, int64_t b, int64_t seg, int64_t h) {
@@ -136,7 +160,7 @@ static int run_row_head(const job_t *j, int64_t b, int64_t h, REAL *S, REAL *qq,
 
     /* S' = diag(exp(g_t)) S : row c of S (key channel c) scaled by exp(g_tc) */
     for (int64_t c = 0; c < K; ++c) {
-      const REAL d = rexp((REAL)j->g[qk_off + c]);
+      const REAL d = rexp(gate_log_decay(j, h, c, (REAL)j->g[qk_off + c]));
       REAL *row = S + c * V;
       for (int64_t x = 0; x < V; ++x) row[x] *= d;
     }
@@ -189,16 +213,18 @@ static void *worker_main(void *arg) {
  * inputs widened exactly).  o [B,T,H,V] and final_state are written in
  * double.  Returns 0, or a nonzero ORACLE_* code.
  */
-int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
-                   const float *q, const float *k, const float *v,
-                   const float *g, const float *beta, double scale, int l2norm,
-                   const float *initial_state, const int32_t *segment_ids,
-                   int64_t n_max, double *o, double *final_state, int num_threads) {
+int kda_oracle_fwd_gate(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                        const float *q, const float *k, const float *v,
+                        const float *g, const float *beta, double scale, int l2norm,
+                        int gate_mode, double lower_bound, const float *a_log, const float *dt_bias,
+                        const float *initial_state, const int32_t *segment_ids,
+                        int64_t n_max, double *o, double *final_state, int num_threads) {
   if (B < 0 || T < 0 || H < 0 || K < 1 || V < 1 || !q || !k || !v || !g || !beta || !o)
     return ORACLE_BAD_ARGS;
+  if (gate_mode < 0 || gate_mode > 2) return ORACLE_BAD_ARGS;
   if (segment_ids && (initial_state || final_state) && n_max < 1) return ORACLE_BAD_ARGS;
-  job_t job = {B, T, H, K, V, q, k, v, g, beta, scale, l2norm, initial_state,
-               segment_ids, n_max, o, final_state};
+  job_t job = {B, T, H, K, V, q, k, v, g, beta, scale, l2norm, gate_mode, lower_bound, a_log, dt_bias,
+               initial_state, segment_ids, n_max, o, final_state};
   if (final_state) {
     /* Slots no segment reaches stay zero. */
     const int64_t n = (segment_ids ? B * n_max : B) * H * K * V;
@@ -221,6 +247,16 @@ int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
   for (int i = 0; i < num_threads; ++i) if (ws[i].status != ORACLE_OK) status = ws[i].status;
   free(ws); free(th);
   return status;
+}
+
+/* The forward with g already the log decay. */
+int kda_oracle_fwd(int64_t B, int64_t T, int64_t H, int64_t K, int64_t V,
+                   const float *q, const float *k, const float *v,
+                   const float *g, const float *beta, double scale, int l2norm,
+                   const float *initial_state, const int32_t *segment_ids,
+                   int64_t n_max, double *o, double *final_state, int num_threads) {
+  return kda_oracle_fwd_gate(B, T, H, K, V, q, k, v, g, beta, scale, l2norm, 0, 0.0, NULL, NULL,
+                             initial_state, segment_ids, n_max, o, final_state, num_threads);
 }
 
 /* Size in bytes of REAL in this build (8 for the fp64 build, 4 for fp32). */

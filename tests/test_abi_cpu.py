@@ -95,10 +95,30 @@ def test_forward_rejects_before_any_launch():
     assert st == kda.KDA_ERR_INVALID_ARGUMENT
 
 
+def test_gated_forward_rejects_before_any_launch():
+    lib = kda.load_library()
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    n = kda.workspace_size(d, False)
+    # misaligned gate parameter
+    st = lib.kda_chunk_fwd_gated(ctypes.byref(d), fake, fake, fake, fake, fake, ctypes.c_void_p(0x1002), None,
+                                 None, None, fake, None, fake, ctypes.c_size_t(n), None)
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
+    # the safe gate's bound is checked as for the plain entry point
+    bad = _desc(safe_gate=True, lower_bound=-6.0)
+    st = lib.kda_chunk_fwd_gated(ctypes.byref(bad), fake, fake, fake, fake, fake, None, None, None, None, fake,
+                                 None, fake, ctypes.c_size_t(n), None)
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
+    # too small a workspace
+    st = lib.kda_chunk_fwd_gated(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, None, None, fake,
+                                 None, fake, ctypes.c_size_t(16), None)
+    assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_python_wrapper_rejects_unsupported_options():
     torch = pytest.importorskip("torch")
     z = torch.zeros(1)
-    with pytest.raises(NotImplementedError):
+    with pytest.raises(ValueError, match="use_gate_in_kernel"):
         kda.chunk_kda(z, z, z, z, z, A_log=z)
     with pytest.raises(NotImplementedError):
         kda.chunk_kda(z, z, z, z, z, cp_context=object())

@@ -29,8 +29,17 @@ MUTATIONS = {
     "beta dropped": ("const REAL w = bt * kk[c];", "const REAL w = kk[c];"),
     "decay on value axis": ("for (int64_t x = 0; x < V; ++x) row[x] *= d;",
                             "for (int64_t x = 0; x < V; ++x) S[x * V + c] *= d;"),
-    "decay sign": ("const REAL d = rexp((REAL)j->g[qk_off + c]);",
-                   "const REAL d = rexp(-(REAL)j->g[qk_off + c]);"),
+    "decay sign": ("const REAL d = rexp(gate_log_decay(j, h, c, (REAL)j->g[qk_off + c]));",
+                   "const REAL d = rexp(-gate_log_decay(j, h, c, (REAL)j->g[qk_off + c]));"),
+    "gate sigmoid mirrored": ("const REAL sig = (REAL)1 / ((REAL)1 + rexp(-z));",
+                              "const REAL sig = (REAL)1 / ((REAL)1 + rexp(z));"),
+    "gate A_log not exponentiated": ("const REAL a = j->a_log ? rexp((REAL)j->a_log[h]) : (REAL)1;",
+                                     "const REAL a = j->a_log ? (REAL)j->a_log[h] : (REAL)1;"),
+    "gate dt_bias dropped": ("(j->dt_bias ? (REAL)j->dt_bias[h * j->K + c] : (REAL)0)", "((REAL)0)"),
+    "gate dt_bias per head only": ("(REAL)j->dt_bias[h * j->K + c]", "(REAL)j->dt_bias[h * j->K]"),
+    "gate lower bound dropped": ("if (j->gate_mode == 2) return (REAL)j->lower_bound * sig;",
+                                 "if (j->gate_mode == 2) return -sig;"),
+    "gate log dropped": ("return (REAL)log((double)sig);", "return -sig;"),
     "decay skipped": ("row[x] *= d;", "row[x] *= (REAL)1;"),
     "residual on transposed state": ("for (int64_t c = 0; c < K; ++c) acc += kk[c] * S[c * V + x];",
                                      "for (int64_t c = 0; c < K; ++c) acc += kk[c] * S[x * V + c];"),
@@ -93,8 +102,9 @@ def test_planted_mistake_fails_a_pin(mutation, tmp_path, monkeypatch):
     for prec, real in (("f64", "double"), ("f32", "float")):
         lib = ctypes.CDLL(_build(src, real, str(tmp_path), tag))
         ref = oracle._lib(prec)
-        lib.kda_oracle_fwd.argtypes = ref.kda_oracle_fwd.argtypes
-        lib.kda_oracle_fwd.restype = ctypes.c_int
+        for fn_name in ("kda_oracle_fwd", "kda_oracle_fwd_gate"):
+            getattr(lib, fn_name).argtypes = getattr(ref, fn_name).argtypes
+            getattr(lib, fn_name).restype = ctypes.c_int
         lib.kda_oracle_real_bytes.restype = ctypes.c_int
         libs[prec] = lib
     monkeypatch.setattr(oracle, "_loaded", libs)

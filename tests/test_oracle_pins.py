@@ -345,6 +345,81 @@ def test_in_kernel_l2norm_equals_normalising_outside():
     assert oracle.rel_err(o_raw, o_in) > 1e-2
 
 
+# ------------------------------------------------------- in-kernel gate activation
+
+def _decay_readout(g_raw, A_log, dt_bias, safe_gate, lower_bound, scale=0.5):
+    """exp(g) of the activated gate, read back through the recurrence: row b
+    writes unit key e_b with value 1 at t = 0 (beta = 1), then at t = 1
+    (beta = 0) reads with q = e_b, so o = scale exp(g_1) for channel b of the
+    gate at t = 1.  g_raw: [K, H] raw gate values of t = 1 (row b = channel b)."""
+    K, H = g_raw.shape
+    B, T, V = K, 2, 1
+    q = np.zeros((B, T, H, K)); k = np.zeros((B, T, H, K)); g = np.zeros((B, T, H, K))
+    for b in range(K):
+        q[b, 1, :, b] = 1.0
+        k[b, 0, :, b] = 1.0
+        g[b, 1, :, b] = g_raw[b]
+    v = np.ones((B, T, H, V))
+    beta = np.zeros((B, T, H)); beta[:, 0] = 1.0
+    o, _ = oracle.kda_forward(q, k, v, g, beta, scale=scale, use_gate_in_kernel=True, A_log=A_log,
+                              dt_bias=dt_bias, safe_gate=safe_gate, lower_bound=lower_bound)
+    return o[:, 1, :, 0] / scale      # [K, H]: exp(g) of channel b, head h
+
+
+def test_gate_activation_special_values():
+    """The in-kernel gate (reading of "sigmoid from A_log, dt_bias" and the
+    sigmoid lower-bound safe gate): z = exp(A_log_h) (g_raw + dt_bias_hc);
+    decay sigmoid(z) without the safe gate, exp(lower_bound sigmoid(z)) with
+    it.  Pinned at sigmoid(0) = 1/2, sigmoid(+-ln 3) = 3/4, 1/4, with dt_bias
+    varying per channel and head, and exp(A_log) = 2 doubling z."""
+    ln3 = np.log(3.0)
+    K, H = 4, 3
+    g_raw = np.zeros((K, H))
+    dt_bias = np.zeros((H, K))
+    dt_bias[0] = [0.0, ln3, -ln3, 0.0]            # head 0: z = 0, ln 3, -ln 3, 0
+    dt_bias[1] = [-ln3, 0.0, ln3, 0.0]            # head 1: per-channel order differs
+    g_raw[:, 2] = ln3 / 2                          # head 2: A_log = ln 2 doubles z to ln 3
+    A_log = np.array([0.0, 0.0, np.log(2.0)])
+    sig = np.array([[0.5, 0.25, 0.75], [0.75, 0.5, 0.75], [0.25, 0.75, 0.75], [0.5, 0.5, 0.75]])
+    plain = _decay_readout(g_raw, A_log, dt_bias, False, None)
+    np.testing.assert_allclose(plain, sig, rtol=2e-7, atol=0)
+    safe = _decay_readout(g_raw, A_log, dt_bias, True, -2.0)
+    np.testing.assert_allclose(safe, np.exp(-2.0 * sig), rtol=2e-7, atol=0)
+    # no A_log, no dt_bias: z = g_raw
+    g2 = np.full((K, H), 0.0)
+    g2[1] = ln3
+    np.testing.assert_allclose(_decay_readout(g2, None, None, False, None)[:, 0], [0.5, 0.75, 0.5, 0.5],
+                               rtol=2e-7, atol=0)
+
+
+def test_gate_activation_limits_and_order():
+    """Limits and monotonicity: without the safe gate the decay sigmoid(z) lies
+    in (0, 1), tends to 1 for large z and to exp(z) for very negative z; with
+    it the decay lies in (exp(lower_bound), 1), reaching exp(lower_bound) for
+    large z and 1 for very negative z; both increase (plain) or decrease (safe)
+    monotonically in z."""
+    K, H = 8, 1
+    z = np.array([-60.0, -20.0, -3.0, -0.5, 0.5, 3.0, 20.0, 60.0])
+    g_raw = z[:, None]
+    plain = _decay_readout(g_raw, None, None, False, None)[:, 0]
+    assert np.all(np.diff(plain) > 0) and np.all(plain > 0) and np.all(plain <= 1)
+    np.testing.assert_allclose(plain[:2], np.exp(z[:2]), rtol=1e-8)
+    np.testing.assert_allclose(plain[-1], 1.0, rtol=0, atol=1e-15)
+    lb = -3.5
+    safe = _decay_readout(g_raw, None, None, True, lb)[:, 0]
+    assert np.all(np.diff(safe) < 0) and np.all(safe > np.exp(lb) * (1 - 1e-12)) and np.all(safe <= 1)
+    np.testing.assert_allclose(safe[0], 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(safe[-1], np.exp(lb), rtol=1e-12)
+
+
+def test_gate_parameters_need_the_gate_flag():
+    x = np.zeros((1, 2, 1, 4))
+    with pytest.raises(ValueError):
+        oracle.kda_forward(x, x, x, x, np.zeros((1, 2, 1)), A_log=np.zeros(1))
+    with pytest.raises(ValueError):
+        oracle.kda_forward(x, x, x, x, np.zeros((1, 2, 1)), use_gate_in_kernel=True, safe_gate=True)
+
+
 def test_empty_inputs():
     z = np.zeros((1, 0, 2, 4))
     o, fin = oracle.kda_forward(z, z, np.zeros((1, 0, 2, 3)), z, np.zeros((1, 0, 2)), output_final_state=True)
