@@ -144,6 +144,18 @@ struct FragP {
     t[lane] = hi;
     t[64 + lane] = lo;
   }
+  // Elements 4 half .. 4 half + 3 of this lane's fragment, split into a pair.
+  __device__ static __forceinline__ void store_half(void* tile, int lane, int half, const float x[4]) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 b = to_bf16(x[j]);
+      h[j] = b;
+      l[j] = to_bf16(x[j] - from_bf16(b));
+    }
+    reinterpret_cast<bf16x4*>(tile)[2 * lane + half] = h;
+    reinterpret_cast<bf16x4*>(tile)[128 + 2 * lane + half] = l;
+  }
 };
 
 struct FragF {

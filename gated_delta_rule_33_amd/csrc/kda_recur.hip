@@ -436,12 +436,14 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   using L = RecordLayout<TI, K, V>;
   constexpr int kPrefetchWave = kComputeWaves;
   constexpr int NV = V / kVT;      // workgroups per (sequence, head)
-  constexpr int SP = K + 8;        // LDS row pitch of the state operand
-  constexpr int DP = kChunk + 8;   // LDS row pitch of the Delta operand
   constexpr int NCB = K / 64;      // key-channel blocks of the state per wave
   constexpr int KB = K / 32;       // 32-deep key slabs
-  __shared__ __align__(16) char s_state[LdsPlane<PS>::template bytes<kVT, SP>()];
-  __shared__ __align__(16) char s_delta[LdsPlane<PD>::template bytes<kVT, DP>()];
+  // S and Delta as operand tiles in fragment order (k = key channel / token):
+  // the accumulator rows a wave holds are one half of the same lane's
+  // fragment, and each lane reads its fragment as whole 16-byte words.
+  constexpr int TS = tile_bytes<PS>(), TD = tile_bytes<PD>();
+  __shared__ __align__(16) char s_state[KB * TS];
+  __shared__ __align__(16) char s_delta[2 * TD];
   __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -541,7 +543,8 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     for (int i = 0; i < 4; ++i)
       st[c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
     float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
-    LdsPlane<PS>::template write4<kVT, SP>(s_state, m, c0, x);
+    const int cb = w * NCB + c;
+    PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
   }
   if (n_chunks > 0) {
     const char* r0 = record(0);
@@ -561,7 +564,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     // dependent chain.
     PS sf[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sf[kb] = LdsPlane<PS>::template read<kVT, SP>(s_state, m, kb, gq);
+    for (int kb = 0; kb < KB; ++kb) sf[kb].load(s_state + kb * TS, lane);
     {
       f32x4 d0 = u, d1 = {0, 0, 0, 0};
 #pragma unroll
@@ -570,7 +573,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
         if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
       }
       float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
-      LdsPlane<PD>::template write4<kVT, DP>(s_delta, m, 16 * w + 4 * gq, x);
+      PD::store_half(s_delta + (w / 2) * TD, lane, w & 1, x);
     }
     load_w(rn1);
     block_sync();   // B1
@@ -578,10 +581,9 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     // S <- diag(exp(G_C)) S + Kt^T Delta
     PD dd[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dd[kb] = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
+    for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta + kb * TD, lane);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-      const int c0 = 16 * (w * NCB + c) + 4 * gq;
       f32x4 a0, a1 = {0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 4; ++i) a0[i] = st[c][i] * gc[c][i];
@@ -590,7 +592,8 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
 #pragma unroll
       for (int i = 0; i < 4; ++i) st[c][i] = a0[i] + a1[i];
       float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
-      LdsPlane<PS>::template write4<kVT, SP>(s_state, m, c0, x);
+      const int cb = w * NCB + c;
+      PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
     }
     load_kt(rn1);
 
