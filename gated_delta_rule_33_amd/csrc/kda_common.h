@@ -28,7 +28,9 @@ constexpr int kThreads = 256;   // four waves per workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Direct-to-LDS loads.  One instruction moves 16 bytes per lane from each
 // lane's global address to LDS at (M0 = wave-uniform LDS base) + 16 * lane,
@@ -87,6 +89,16 @@ __device__ __forceinline__ float from_bf16(__bf16 x) { return (float)x; }
 
 __device__ __forceinline__ float bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
+// Two floats rounded to bf16 (nearest even) with one packed conversion.
+__device__ __forceinline__ bf16x2 to_bf16x2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, bf16x2); }
+// The pair a, b split as hi + lo: hi = bf16(x), lo = bf16(x - hi); two packed
+// conversions, the hi values widened back with one shift and one mask.
+__device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x2& lo) {
+  hi = to_bf16x2(a, b);
+  const uint32_t hb = __builtin_bit_cast(uint32_t, hi);
+  lo = to_bf16x2(a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u));
+}
+
 // Input element loads (the raw input types are float and bf16 bits).
 __device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) { return bits_to_f32(p[i]); }
@@ -104,7 +116,11 @@ struct FragB {
   static constexpr int kBytesPerLane = 16;
   __device__ __forceinline__ void set(const float x[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = to_bf16(x[j]);
+    for (int j = 0; j < 8; j += 2) {
+      const bf16x2 h = to_bf16x2(x[j], x[j + 1]);
+      v[j] = h[0];
+      v[j + 1] = h[1];
+    }
   }
   __device__ __forceinline__ void load(const void* tile, int lane) {
     v = reinterpret_cast<const bf16x8*>(tile)[lane];
@@ -117,7 +133,11 @@ struct FragB {
   __device__ static __forceinline__ void store_half(void* tile, int lane, int half, const float x[4]) {
     bf16x4 h;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) h[j] = to_bf16(x[j]);
+    for (int j = 0; j < 4; j += 2) {
+      const bf16x2 p = to_bf16x2(x[j], x[j + 1]);
+      h[j] = p[0];
+      h[j + 1] = p[1];
+    }
     reinterpret_cast<bf16x4*>(tile)[2 * lane + half] = h;
   }
 };
@@ -127,10 +147,11 @@ struct FragP {
   static constexpr int kBytesPerLane = 32;
   __device__ __forceinline__ void set(const float x[8]) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      __bf16 h = to_bf16(x[j]);
-      hi[j] = h;
-      lo[j] = to_bf16(x[j] - from_bf16(h));
+    for (int j = 0; j < 8; j += 2) {
+      bf16x2 h, l;
+      split_bf16x2(x[j], x[j + 1], h, l);
+      hi[j] = h[0]; hi[j + 1] = h[1];
+      lo[j] = l[0]; lo[j + 1] = l[1];
     }
   }
   // Tile storage: the 64 hi vectors, then the 64 lo vectors.
@@ -148,10 +169,11 @@ struct FragP {
   __device__ static __forceinline__ void store_half(void* tile, int lane, int half, const float x[4]) {
     bf16x4 h, l;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 b = to_bf16(x[j]);
-      h[j] = b;
-      l[j] = to_bf16(x[j] - from_bf16(b));
+    for (int j = 0; j < 4; j += 2) {
+      bf16x2 hp, lp;
+      split_bf16x2(x[j], x[j + 1], hp, lp);
+      h[j] = hp[0]; h[j + 1] = hp[1];
+      l[j] = lp[0]; l[j + 1] = lp[1];
     }
     reinterpret_cast<bf16x4*>(tile)[2 * lane + half] = h;
     reinterpret_cast<bf16x4*>(tile)[128 + 2 * lane + half] = l;

@@ -463,7 +463,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     for (int c = lane; c < K; c += kWave) span = fmaxf(span, sm.G[f * S::kGP + c] - sm.G[(f + 15) * S::kGP + c]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
-    const bool diag_split = span <= kSpanMax;
+    // wave-uniform (the reduction above leaves it in every lane); stated so,
+    // the block loop below branches on scalars instead of masking lanes
+    const bool diag_split = __builtin_amdgcn_readfirstlane(span <= kSpanMax ? 1 : 0) != 0;
     block_sync();   // nk, X and the factor table visible
 
     // ---- A and Aqk for row block R over key-channel half chalf: tiles (I, R)
