@@ -232,8 +232,8 @@ __device__ __forceinline__ void mma(f32x4& c, const FragF& a, const FragF& b) {
 }
 
 // Operand precisions per role.  bf16 inputs: the products whose rounding
-// reaches the output at the 1e-3 level use pairs, T and W stay single bf16
-// (their rounding stays below 2e-3 of the output's rms on the benchmark
+// reaches the output at the 1e-2 level use pairs; T, W and Qg stay single
+// bf16 (each costs at most a few 1e-3 of the output's rms on the benchmark
 // workloads), V is an exact bf16 input.  fp32 inputs: fp32 throughout.
 template <class TI> struct Prec;
 template <> struct Prec<uint16_t> {
@@ -243,13 +243,14 @@ template <> struct Prec<uint16_t> {
   using V = FragB;   // values (exact)
   using W = FragB;   // -W as stored for the recurrence
   using Kt = FragP;  // k * exp(G_C - G) (state update)
-  using Q = FragP;   // scale * q * exp(G) and scale * Aqk (output)
+  using Qg = FragB;  // scale * q * exp(G) (output, inter-chunk part)
+  using Aq = FragP;  // scale * Aqk (output, intra-chunk part)
   using S = FragP;   // the state as an operand
   using D = FragP;   // the scaled residuals Delta as an operand
 };
 template <> struct Prec<float> {
   using A = FragF; using T = FragF; using X = FragF; using V = FragF; using W = FragF;
-  using Kt = FragF; using Q = FragF; using S = FragF; using D = FragF;
+  using Kt = FragF; using Qg = FragF; using Aq = FragF; using S = FragF; using D = FragF;
 };
 
 // ----------------------------------------------------------------------------
@@ -270,9 +271,9 @@ struct RecordLayout {
   static constexpr int64_t kKt = kWn + kWnBytes;
   static constexpr int64_t kKtBytes = (K / 16) * 2 * tile_bytes<typename P::Kt>();
   static constexpr int64_t kQg = kKt + kKtBytes;
-  static constexpr int64_t kQgBytes = 4 * (K / 32) * tile_bytes<typename P::Q>();
+  static constexpr int64_t kQgBytes = 4 * (K / 32) * tile_bytes<typename P::Qg>();
   static constexpr int64_t kAqk = kQg + kQgBytes;
-  static constexpr int64_t kAqkBytes = 4 * 2 * tile_bytes<typename P::Q>();
+  static constexpr int64_t kAqkBytes = 4 * 2 * tile_bytes<typename P::Aq>();
   static constexpr int64_t kU = kAqk + kAqkBytes;
   static constexpr int64_t kUBytes = 4 * (V / 16) * kWave * 16;
   static constexpr int64_t kGc = kU + kUBytes;

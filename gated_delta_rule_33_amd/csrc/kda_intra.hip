@@ -255,7 +255,8 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
   using PV = typename Prec<TI>::V;
   using PW = typename Prec<TI>::W;
   using PK = typename Prec<TI>::Kt;
-  using PQ = typename Prec<TI>::Q;
+  using PQ = typename Prec<TI>::Qg;
+  using PAq = typename Prec<TI>::Aq;
   using L = RecordLayout<TI, K, V>;
   extern __shared__ __align__(16) char smem_raw[];
   S& sm = *reinterpret_cast<S*>(smem_raw);
@@ -657,9 +658,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
             x[ii] = (2 * kb <= R) ? accQK[2 * kb][ii] : 0.f;
             x[4 + ii] = (2 * kb + 1 <= R) ? accQK[2 * kb + 1][ii] : 0.f;
           }
-          PQ af;
+          PAq af;
           af.set(x);
-          af.store(rec + L::kAqk + (int64_t)(R * 2 + kb) * tile_bytes<PQ>(), lane);
+          af.store(rec + L::kAqk + (int64_t)(R * 2 + kb) * tile_bytes<PAq>(), lane);
         }
       }
     }

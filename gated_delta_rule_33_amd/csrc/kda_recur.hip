@@ -125,8 +125,8 @@ struct Stage {
   static constexpr int NCB = K / 64;
   static constexpr int kWnBytes = (K / 32) * tile_bytes<typename P::W>();
   static constexpr int kKtBytes = NCB * 2 * tile_bytes<typename P::Kt>();
-  static constexpr int kQgBytes = (K / 32) * tile_bytes<typename P::Q>();
-  static constexpr int kAqkTile = tile_bytes<typename P::Q>();
+  static constexpr int kQgBytes = (K / 32) * tile_bytes<typename P::Qg>();
+  static constexpr int kAqkTile = tile_bytes<typename P::Aq>();
   static constexpr int oWn = 0;
   static constexpr int oU = oWn + kWnBytes;
   static constexpr int oKt = oU + TPW * 1024;
@@ -369,9 +369,10 @@ __global__ __launch_bounds__(Roles<TPW>::kThreads) void kda_recur_kernel(RecurPa
     // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
     f32x4 ov = {0, 0, 0, 0};
     if constexpr (TPW == 1) {
-      typename P::Q qg[K / 32], aq[2];
+      typename P::Qg qg[K / 32];
+      typename P::Aq aq[2];
 #pragma unroll
-      for (int kb = 0; kb < K / 32; ++kb) qg[kb].load(stg + SG::oQg + kb * tile_bytes<typename P::Q>(), lane);
+      for (int kb = 0; kb < K / 32; ++kb) qg[kb].load(stg + SG::oQg + kb * tile_bytes<typename P::Qg>(), lane);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
         if (kb <= w / 2) aq[kb].load(stg + SG::oAqk + kb * SG::kAqkTile, lane);
@@ -386,14 +387,14 @@ __global__ __launch_bounds__(Roles<TPW>::kThreads) void kda_recur_kernel(RecurPa
       // Delta phase).
 #pragma unroll
       for (int kb = 0; kb < K / 32; ++kb) {
-        typename P::Q qg;
-        qg.load(stg + SG::oQg + kb * tile_bytes<typename P::Q>(), lane);
+        typename P::Qg qg;
+        qg.load(stg + SG::oQg + kb * tile_bytes<typename P::Qg>(), lane);
         mma(ov, qg, sf[kb]);
       }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (kb > w / 2) continue;
-        typename P::Q aq;
+        typename P::Aq aq;
         aq.load(stg + SG::oAqk + kb * SG::kAqkTile, lane);
         const PD d2 = LdsPlane<PD>::template read<kVT, DP>(s_delta, m, kb, gq);
         mma(ov, aq, d2);
@@ -432,7 +433,8 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   using PD = typename P::D;
   using PW = typename P::W;
   using PK = typename P::Kt;
-  using PQ = typename P::Q;
+  using PQ = typename P::Qg;
+  using PA = typename P::Aq;
   using L = RecordLayout<TI, K, V>;
   constexpr int kPrefetchWave = kComputeWaves;
   constexpr int NV = V / kVT;      // workgroups per (sequence, head)
@@ -512,7 +514,8 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   f32x4 u;
   PK kt[NCB][2];
   f32x4 gc[NCB];
-  PQ qg[KB], aq[2];
+  PQ qg[KB];
+  PA aq[2];
   auto load_w = [&](const char* r) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
@@ -531,7 +534,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PQ>(), lane);
+      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PA>(), lane);
   };
 
   // State slice: lane (column v0 + m, rows 16cb + 4gq + i) of its blocks.
