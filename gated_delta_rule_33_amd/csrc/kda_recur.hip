@@ -104,10 +104,12 @@ template <> struct LdsPlane<FragF> {   // one fp32 plane
   }
 };
 
-__device__ __forceinline__ void store_out(float* o, int64_t i, float x) { o[i] = x; }
+// Output stores are non-temporal: o is not read again by this forward, and
+// streaming it past the caches leaves them to the chunk records.
+__device__ __forceinline__ void store_out(float* o, int64_t i, float x) { __builtin_nontemporal_store(x, o + i); }
 __device__ __forceinline__ void store_out(uint16_t* o, int64_t i, float x) {
   const __bf16 h = to_bf16(x);
-  o[i] = *reinterpret_cast<const uint16_t*>(&h);
+  __builtin_nontemporal_store(*reinterpret_cast<const uint16_t*>(&h), o + i);
 }
 
 // The record operands compute wave w uses in one chunk, staged in its own LDS
