@@ -188,6 +188,46 @@ def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32", gate_
     return dict(inp=inp, call=call, step_ms=step_ms, total_ms=total_ms, wall_s=wall, kernel_ms=kern_ms)
 
 
+def time_layer_ops(w, steps: int, warmup: int):
+    """The layer steps around the kernel at the workload's shape: the short
+    convolution (width 4, SiLU) of one [B, T, H*K] bf16 projection (q, k and
+    v each take one such call) and the gated RMSNorm of the fp32 output with a
+    bf16 gate into a bf16 result.  Each timed as `steps` back-to-back calls
+    between two events; memory-bound, so GB/s of algorithmic bytes."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    g = torch.Generator(device="cuda").manual_seed(w.seed + 7)
+    x = torch.randn(w.B, w.T, w.H * w.K, device="cuda", generator=g).to(torch.bfloat16)
+    cw = torch.randn(w.H * w.K, 4, device="cuda", generator=g) * 0.5
+    o = torch.randn(w.B, w.T, w.H, w.V, device="cuda", generator=g)
+    z = torch.randn(w.B, w.T, w.H, w.V, device="cuda", generator=g).to(torch.bfloat16)
+    nw = torch.ones(w.V, device="cuda")
+    yc = torch.empty_like(x)
+    yn = torch.empty(o.shape, dtype=torch.bfloat16, device="cuda")
+    ops = {
+        "kda_short_conv": (lambda: kda.short_convolution(x, cw, out=yc), 2 * x.numel() * 2 + cw.numel() * 4),
+        "kda_gated_rmsnorm": (lambda: kda.gated_rmsnorm(o, z, nw, out=yn, out_dtype=torch.bfloat16),
+                              o.numel() * 4 + z.numel() * 2 + yn.numel() * 2 + w.V * 4),
+    }
+    out = {}
+    for name, (fn, nbytes) in ops.items():
+        for _ in range(warmup):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"avg_us": round(us, 2), "alg_bytes": nbytes, "achieved_gbps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    out["shape"] = f"x [{w.B}, {w.T}, {w.H * w.K}] bf16 (one of q, k, v); o [{w.B}, {w.T}, {w.H}, {w.V}] fp32"
+    return out
+
+
 def summarize(w, res, out_bytes):
     steps = len(res["step_ms"])
     ms = res["total_ms"] / steps
@@ -235,6 +275,8 @@ def main():
     ap.add_argument("--extra", default="bf16_b1_h32_t8192_packed25_l2",
                     help="second workload timed and reported under 'extra' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-layer-ops", dest="layer_ops", action="store_false",
+                    help="skip the timing of the short convolution and the gated RMSNorm")
     ap.add_argument("--no-gate-in-kernel", dest="gate_in_kernel", action="store_false",
                     help="skip the timing of the same workload with the gate activated in the kernel")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -301,6 +343,9 @@ def main():
                                    "note": "raw N(0,1) gate, A_log = 0, dt_bias = 0, safe gate at -5: "
                                            "the same decay distribution, activated in the kernel"}
         del res3
+    if args.layer_ops:
+        log("[bench] layer steps (short convolution, gated RMSNorm)")
+        extra["layer_ops"] = time_layer_ops(w, args.steps, args.warmup)
     line = {
         "metric": METRIC, "value": round(s["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(s["ms"], 4), "higher_is_better": True,

@@ -213,6 +213,44 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
 
 extern "C" {
 
+kda_status_t kda_short_conv_fwd(int64_t B, int64_t T, int64_t D, int32_t W, kda_dtype_t dtype, const void* x,
+                                const float* weight, const int32_t* segment_ids, void* y, void* stream) {
+  if (B < 0 || T < 0 || D < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B, T and D must be >= 0");
+  if (W < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "W must be >= 1 (W = 0 disables the convolution: skip the call)");
+  if (W > 8) return fail(KDA_ERR_NOT_IMPLEMENTED, "kernel sizes above 8 are not supported");
+  if (D % 8 != 0) return fail(KDA_ERR_NOT_IMPLEMENTED, "D must be a multiple of 8");
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_F32 or KDA_BF16");
+  if (B * T * D == 0) return KDA_OK;
+  if (!x || !weight || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "x, weight and y must be non-NULL");
+  if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 15) ||
+      (reinterpret_cast<uintptr_t>(weight) & 3) || (reinterpret_cast<uintptr_t>(segment_ids) & 3))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, weight and segment_ids 4-byte aligned");
+  kda::ConvArgs a{B, T, D, W, dtype == KDA_BF16, x, weight, segment_ids, y, static_cast<hipStream_t>(stream)};
+  const hipError_t e = observed("kda_short_conv", a.stream, [&] { return kda::launch_short_conv(a); });
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status_t kda_gated_rmsnorm_fwd(int64_t rows, int64_t V, kda_dtype_t o_dtype, kda_dtype_t gate_dtype,
+                                   kda_dtype_t y_dtype, const void* o, const void* gate, const float* weight,
+                                   float eps, void* y, void* stream) {
+  if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "rows must be >= 0");
+  if (V != 64 && V != 128 && V != 256) return fail(KDA_ERR_NOT_IMPLEMENTED, "V must be 64, 128 or 256");
+  for (kda_dtype_t t : {o_dtype, gate_dtype, y_dtype})
+    if (t != KDA_F32 && t != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "dtypes must be KDA_F32 or KDA_BF16");
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+  if (rows == 0) return KDA_OK;
+  if (!o || !gate || !weight || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "o, gate, weight and y must be non-NULL");
+  const void* ptrs[] = {o, gate, weight, y};
+  for (const void* p : ptrs)
+    if (reinterpret_cast<uintptr_t>(p) & 3) return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 4-byte aligned");
+  kda::NormArgs a{rows, V, o_dtype == KDA_BF16, gate_dtype == KDA_BF16, y_dtype == KDA_BF16, o, gate, weight, eps, y,
+                  static_cast<hipStream_t>(stream)};
+  const hipError_t e = observed("kda_gated_rmsnorm", a.stream, [&] { return kda::launch_gated_rmsnorm(a); });
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return KDA_OK;
+}
+
 kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, void* stream, uint32_t* flags) {
   if (flags == nullptr || workspace == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "NULL argument");
   if (workspace_bytes < sizeof(kda::TableHeader))

@@ -41,12 +41,36 @@ struct CallArgs {
   hipStream_t stream;
 };
 
+// Short convolution of x [B,T,D] with weight [D,W] (layer step before the kernel).
+struct ConvArgs {
+  int64_t B, T, D;
+  int W;
+  bool bf16;                  // x and y are bf16 (else fp32)
+  const void* x;
+  const float* weight;
+  const int32_t* seg;         // [B,T] or NULL
+  void* y;
+  hipStream_t stream;
+};
+// Gated RMSNorm over rows of V values (output stage after the kernel).
+struct NormArgs {
+  int64_t rows, V;
+  bool o_bf16, gate_bf16, y_bf16;
+  const void *o, *gate;
+  const float* weight;        // [V]
+  float eps;
+  void* y;
+  hipStream_t stream;
+};
+
 int64_t record_bytes(InType in, int64_t K, int64_t V);
 
 hipError_t launch_prep(const CallArgs& a);
 hipError_t launch_intra(const CallArgs& a);
 hipError_t launch_recur(const CallArgs& a);
 hipError_t launch_zero_states(const CallArgs& a);
+hipError_t launch_short_conv(const ConvArgs& a);
+hipError_t launch_gated_rmsnorm(const NormArgs& a);
 int cu_count();
 
 }  // namespace kda

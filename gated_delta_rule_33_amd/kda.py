@@ -21,8 +21,9 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 
-EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_flags",
-            "kda_set_launch_observer", "kda_last_error", "kda_version")
+EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_short_conv_fwd",
+            "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer", "kda_last_error",
+            "kda_version")
 
 # void (*)(const char* kernel_name, void* stream, int phase, void* user)
 LAUNCH_OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p)
@@ -60,6 +61,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_gated.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.kda_short_conv_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, p]
+    lib.kda_short_conv_fwd.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm_fwd.argtypes = [i64, i64, i32, i32, i32, p, p, p, ctypes.c_float, p, p]
+    lib.kda_gated_rmsnorm_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_flags.argtypes = [p, sz, p, ctypes.POINTER(ctypes.c_uint32)]
     lib.kda_chunk_fwd_flags.restype = ctypes.c_int
     lib.kda_set_launch_observer.argtypes = [LAUNCH_OBSERVER, ctypes.c_void_p]
@@ -199,6 +205,57 @@ def _gate_tensors(use_gate_in_kernel, A_log, dt_bias, H, K, device):
             raise ValueError(f"{name} must be a contiguous float32 {shape} tensor on the inputs' device")
         out.append(t)
     return tuple(out)
+
+
+def short_convolution(x, weight, segment_ids=None, out=None):
+    """Causal depthwise short convolution with SiLU (the layer step q, k and v
+    pass through before the kernel): x [B, T, D] (fp32 or bf16, contiguous,
+    D a multiple of 8), weight [D, W] fp32 (or PyTorch's [D, 1, W]),
+    segment_ids None or int32 [B, T].  A tap never reaches before the start
+    of its token's segment; padding tokens get 0.  W = 0 disables the
+    convolution (x is returned as is)."""
+    import torch
+    if weight.dim() == 3:
+        weight = weight.reshape(weight.shape[0], weight.shape[2])
+    D, W = weight.shape
+    if W == 0:
+        return x
+    if x.dim() != 3 or x.shape[2] != D:
+        raise ValueError("x must be [B, T, D] with D = weight.shape[0]")
+    if not x.is_contiguous() or weight.dtype != torch.float32 or not weight.is_contiguous():
+        raise ValueError("x must be contiguous and weight a contiguous float32 [D, W] tensor")
+    if segment_ids is not None and (segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != tuple(x.shape[:2])
+                                    or not segment_ids.is_contiguous()):
+        raise ValueError("segment_ids must be a contiguous int32 [B, T] tensor")
+    B, T, _ = x.shape
+    y = torch.empty_like(x) if out is None else out
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    _raise_for(load_library().kda_short_conv_fwd(B, T, D, W, _dtype_code(x.dtype), _ptr(x), _ptr(weight),
+                                                 _ptr(segment_ids), _ptr(y), ctypes.c_void_p(stream)),
+               "kda_short_conv_fwd")
+    return y
+
+
+def gated_rmsnorm(o, gate, weight, eps: float = 1e-6, out_dtype=None, out=None):
+    """Output stage after the kernel: per-head RMSNorm over the last axis (V)
+    with a sigmoid output gate, y = weight * o / sqrt(mean(o^2) + eps) *
+    sigmoid(gate).  o, gate [..., V] (fp32 or bf16, contiguous, same shape),
+    weight fp32 [V]; V in {64, 128, 256}."""
+    import torch
+    if gate.shape != o.shape or not o.is_contiguous() or not gate.is_contiguous():
+        raise ValueError("o and gate must be contiguous tensors of one shape")
+    V = o.shape[-1]
+    if weight.dtype != torch.float32 or tuple(weight.shape) != (V,) or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous float32 [V] tensor")
+    out_dtype = o.dtype if out_dtype is None else out_dtype
+    y = torch.empty(o.shape, dtype=out_dtype, device=o.device) if out is None else out
+    rows = o.numel() // V if V else 0
+    stream = torch.cuda.current_stream(o.device).cuda_stream
+    _raise_for(load_library().kda_gated_rmsnorm_fwd(rows, V, _dtype_code(o.dtype), _dtype_code(gate.dtype),
+                                                    _dtype_code(out_dtype), _ptr(o), _ptr(gate), _ptr(weight),
+                                                    float(eps), _ptr(y), ctypes.c_void_p(stream)),
+               "kda_gated_rmsnorm_fwd")
+    return y
 
 
 def set_launch_observer(fn):

@@ -127,6 +127,45 @@ kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Short convolution, the layer step that q, k and v each pass through before
+ * the kernel (page "feat(kda): integrate KDA attention with tokamax backend
+ * and CP support", Implementation Details, Layer architecture, step 1: a
+ * causal depthwise 1D convolution with SiLU; kernel size
+ * linear_conv_kernel_dim of its configuration table; its review notes make
+ * the convolution segment-aware):
+ *     y[b,t,d] = SiLU( sum_{j<W} weight[d*W + j] * x[b, t-(W-1)+j, d] )
+ * where a tap before the start of t's segment (or before t = 0) reads zero and
+ * padding tokens (segment id 0) get y = 0.  No bias.
+ *   x, y         [B,T,D] of `dtype` (fp32 or bf16), device memory, 16-byte
+ *                aligned; y may not overlap x.
+ *   weight       fp32 [D,W] (PyTorch's depthwise Conv1d weight [D,1,W]),
+ *                device memory; tap W-1 multiplies the current token.
+ *   segment_ids  NULL (one segment per row) or int32 [B,T] as for
+ *                kda_chunk_fwd.
+ * W must be 1..8 and D a multiple of 8 (else NOT_IMPLEMENTED; W = 0, which
+ * the configuration uses to disable the convolution, is INVALID_ARGUMENT:
+ * the caller skips the call).  Asynchronous on `stream`; allocates nothing.
+ */
+kda_status_t kda_short_conv_fwd(int64_t B, int64_t T, int64_t D, int32_t W, kda_dtype_t dtype,
+                                const void* x, const float* weight, const int32_t* segment_ids,
+                                void* y, void* stream);
+
+/*
+ * Output stage after the kernel (same page, Layer architecture: a per-head
+ * RMSNorm and a sigmoid output gate), over rows of V values (one row per
+ * token and head):
+ *     y = weight * o / sqrt(mean(o^2) + eps) * sigmoid(gate)
+ *   o       [rows, V] of o_dtype; gate [rows, V] of gate_dtype; y [rows, V]
+ *           of y_dtype (each fp32 or bf16), device memory, 4-byte aligned.
+ *   weight  fp32 [V], shared by the heads.   eps >= 0, finite.
+ * V must be 64, 128 or 256 (else NOT_IMPLEMENTED).  Asynchronous on
+ * `stream`; allocates nothing.
+ */
+kda_status_t kda_gated_rmsnorm_fwd(int64_t rows, int64_t V, kda_dtype_t o_dtype, kda_dtype_t gate_dtype,
+                                   kda_dtype_t y_dtype, const void* o, const void* gate,
+                                   const float* weight, float eps, void* y, void* stream);
+
+/*
  * Waits for `stream`, then reads the KDA_FLAG_* word the last kda_chunk_fwd
  * call on this workspace left behind (0 when nothing was flagged).
  */

@@ -115,6 +115,22 @@ def test_gated_forward_rejects_before_any_launch():
     assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL
 
 
+def test_layer_steps_reject_before_any_launch():
+    lib = kda.load_library()
+    fake = ctypes.c_void_p(0x1000)
+    conv = lambda B, T, D, W, dt=kda.KDA_BF16, x=fake: lib.kda_short_conv_fwd(B, T, D, W, dt, x, fake, None, fake, None)
+    assert conv(1, 8, 64, 0) == kda.KDA_ERR_INVALID_ARGUMENT      # W = 0: the caller skips the call
+    assert conv(1, 8, 64, 9) == kda.KDA_ERR_NOT_IMPLEMENTED
+    assert conv(1, 8, 68, 4) == kda.KDA_ERR_NOT_IMPLEMENTED
+    assert conv(1, 8, 64, 4, x=ctypes.c_void_p(0x1008)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert conv(0, 8, 64, 4) == kda.KDA_OK                          # empty: nothing to do
+    norm = lambda rows, V, eps=1e-6: lib.kda_gated_rmsnorm_fwd(rows, V, kda.KDA_F32, kda.KDA_BF16, kda.KDA_F32,
+                                                               fake, fake, fake, eps, fake, None)
+    assert norm(4, 96) == kda.KDA_ERR_NOT_IMPLEMENTED
+    assert norm(4, 128, eps=-1.0) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert norm(0, 128) == kda.KDA_OK
+
+
 def test_python_wrapper_rejects_unsupported_options():
     torch = pytest.importorskip("torch")
     z = torch.zeros(1)
