@@ -137,6 +137,17 @@ def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32", gate_
                             lower_bound=w.lower_bound, segment_ids=d["segment_ids"],
                             N_max=inp["max_segments"] if d["segment_ids"] is not None else None,
                             out_dtype=out_dtype, **gate_kw)
+    res = time_call(call, steps, warmup)
+    res.update(inp=inp, call=call)
+    return res
+
+
+def time_call(call, steps: int, warmup: int):
+    """Time a prepared call (anything with enqueue()): `steps` back-to-back
+    enqueues between two events, then `steps` more with an event around every
+    kernel launch and at every step boundary."""
+    import torch
+    from gated_delta_rule_33_amd import kda
     for _ in range(warmup):
         call.enqueue()
     torch.cuda.synchronize()
@@ -159,7 +170,7 @@ def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32", gate_
     # 2) Per-kernel durations: another `steps` forwards with an event before
     #    and after every kernel (recorded on the launch stream by the library's
     #    launch observer from a pre-created pool) and at every step boundary.
-    pool = [torch.cuda.Event(enable_timing=True) for _ in range(16 * steps + 8)]
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(32 * steps + 8)]
     used = []
     pending = {}
     kernel_events = {}
@@ -185,7 +196,27 @@ def time_workload(w, steps: int, warmup: int, out_dtype_name: str = "f32", gate_
     del cb
     step_ms = [step_events[i].elapsed_time(step_events[i + 1]) for i in range(steps)]
     kern_ms = {n: [a.elapsed_time(b) for a, b in evs] for n, evs in kernel_events.items()}
-    return dict(inp=inp, call=call, step_ms=step_ms, total_ms=total_ms, wall_s=wall, kernel_ms=kern_ms)
+    return dict(step_ms=step_ms, total_ms=total_ms, wall_s=wall, kernel_ms=kern_ms)
+
+
+def time_cp(w, steps: int, warmup: int, P: int):
+    """The workload cut into P context-parallel slices on this one GPU (plan,
+    forward with transitions, chain, rerun of the recurrence, state routing):
+    what P ranks would do, with the P-1 state hops run by one kernel."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    inp = make_inputs(w)
+    d = to_device(inp, w.dtype)
+    call = kda.CpCall(d["q"], d["k"], d["v"], d["g"], d["beta"], P, scale=inp["scale"],
+                      initial_state=d["initial_state"], output_final_state=w.final_state,
+                      use_qk_l2norm_in_kernel=w.l2norm_in_kernel, safe_gate=w.safe_gate, lower_bound=w.lower_bound,
+                      segment_ids=d["segment_ids"],
+                      N_max=inp["max_segments"] if d["segment_ids"] is not None else None)
+    res = time_call(call, steps, warmup)
+    ms = res["total_ms"] / steps
+    kern = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in res["kernel_ms"].items()}
+    return {"ranks": P, "ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "kernel_avg_us": kern}
 
 
 def time_layer_ops(w, steps: int, warmup: int):
@@ -279,6 +310,8 @@ def main():
                     help="skip the timing of the short convolution and the gated RMSNorm")
     ap.add_argument("--no-gate-in-kernel", dest="gate_in_kernel", action="store_false",
                     help="skip the timing of the same workload with the gate activated in the kernel")
+    ap.add_argument("--no-cp", dest="cp", action="store_false",
+                    help="skip the timing of the workload cut into 2 and 4 context-parallel slices")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help=f"run one {COPY_CALIBRATION_MIB} MiB elementwise copy first (counter calibration)")
     args = ap.parse_args()
@@ -343,6 +376,11 @@ def main():
                                    "note": "raw N(0,1) gate, A_log = 0, dt_bias = 0, safe gate at -5: "
                                            "the same decay distribution, activated in the kernel"}
         del res3
+    if args.cp:
+        for P in (2, 4):
+            log(f"[bench] {w.name} cut into {P} context-parallel slices")
+            extra.setdefault("context_parallel", {"workload": w.name})[f"P{P}"] = time_cp(w, args.steps,
+                                                                                           args.warmup, P)
     if args.layer_ops:
         log("[bench] layer steps (short convolution, gated RMSNorm)")
         extra["layer_ops"] = time_layer_ops(w, args.steps, args.warmup)

@@ -12,7 +12,9 @@
 
 #include <cmath>
 #include <cstdio>
+#include <cstdint>
 #include <cstring>
+#include <initializer_list>
 #include <string>
 
 #include "kda.h"
@@ -99,12 +101,18 @@ kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-// The forward of both entry points; gate_mode 0 takes g as the log decay,
-// 1 and 2 activate it in the kernel (without / with the safe gate).
+// What the forward entry points add to the plain call.
+struct FwdExtra {
+  int gate_mode = 0;          // 0: g is the log decay; 1, 2: activated in the kernel (without / with safe gate)
+  const float* a_log = nullptr;
+  const float* dt_bias = nullptr;
+  float* transition = nullptr;   // also compute each row's transition
+  bool rerun = false;            // only the recurrence, from the records already in the workspace
+};
+
 kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
-                     const void* beta, int gate_mode, const float* a_log, const float* dt_bias,
-                     const float* initial_state, const int32_t* segment_ids, void* o, float* final_state,
-                     void* workspace, size_t workspace_bytes, void* stream);
+                     const void* beta, const FwdExtra& x, const float* initial_state, const int32_t* segment_ids,
+                     void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
 }  // namespace
 
@@ -123,16 +131,38 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc, const void* q, const void
                            const void* g, const void* beta, const float* initial_state,
                            const int32_t* segment_ids, void* o, float* final_state, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return forward(desc, q, k, v, g, beta, 0, nullptr, nullptr, initial_state, segment_ids, o, final_state,
-                 workspace, workspace_bytes, stream);
+  return forward(desc, q, k, v, g, beta, FwdExtra{}, initial_state, segment_ids, o, final_state, workspace,
+                 workspace_bytes, stream);
 }
 
 kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v,
                                  const void* g, const void* beta, const float* A_log, const float* dt_bias,
                                  const float* initial_state, const int32_t* segment_ids, void* o,
                                  float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
-  const int mode = (desc != nullptr && desc->safe_gate) ? 2 : 1;
-  return forward(desc, q, k, v, g, beta, mode, A_log, dt_bias, initial_state, segment_ids, o, final_state,
+  FwdExtra x;
+  x.gate_mode = (desc != nullptr && desc->safe_gate) ? 2 : 1;
+  x.a_log = A_log;
+  x.dt_bias = dt_bias;
+  return forward(desc, q, k, v, g, beta, x, initial_state, segment_ids, o, final_state, workspace, workspace_bytes,
+                 stream);
+}
+
+kda_status_t kda_chunk_fwd_transition(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v,
+                                      const void* g, const void* beta, const float* initial_state,
+                                      const int32_t* segment_ids, void* o, float* final_state, float* transition,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (transition == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "transition is NULL");
+  FwdExtra x;
+  x.transition = transition;
+  return forward(desc, q, k, v, g, beta, x, initial_state, segment_ids, o, final_state, workspace, workspace_bytes,
+                 stream);
+}
+
+kda_status_t kda_chunk_fwd_rerun(const kda_fwd_desc_t* desc, const float* initial_state, const int32_t* segment_ids,
+                                 void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdExtra x;
+  x.rerun = true;
+  return forward(desc, nullptr, nullptr, nullptr, nullptr, nullptr, x, initial_state, segment_ids, o, final_state,
                  workspace, workspace_bytes, stream);
 }
 
@@ -141,9 +171,8 @@ kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc, const void* q, cons
 namespace {
 
 kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
-                     const void* beta, int gate_mode, const float* a_log, const float* dt_bias,
-                     const float* initial_state, const int32_t* segment_ids, void* o, float* final_state,
-                     void* workspace, size_t workspace_bytes, void* stream) {
+                     const void* beta, const FwdExtra& x, const float* initial_state, const int32_t* segment_ids,
+                     void* o, float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
   const bool has_seg = segment_ids != nullptr;
   Plan plan;
   kda_status_t st = validate(desc, has_seg, &plan);
@@ -151,12 +180,13 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
   const kda_fwd_desc_t& d = *desc;
   const int64_t tokens = d.B * d.T;
   if (tokens > 0 && d.H > 0) {
-    if (!q || !k || !v || !g || !beta || !o)
+    if (!x.rerun && (!q || !k || !v || !g || !beta))
       return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-NULL");
-    const void* ptrs[] = {q, k, v, g, beta, o, initial_state, segment_ids, final_state, workspace};
+    if (!o) return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and o must be non-NULL");
+    const void* ptrs[] = {q, k, v, g, beta, o, initial_state, segment_ids, final_state, workspace, x.transition};
     for (const void* ptr : ptrs)
       if (ptr && !aligned16(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
-    const void* gate_ptrs[] = {a_log, dt_bias};
+    const void* gate_ptrs[] = {x.a_log, x.dt_bias};
     for (const void* ptr : gate_ptrs)
       if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3) != 0)
         return fail(KDA_ERR_INVALID_ARGUMENT, "A_log and dt_bias must be float-aligned");
@@ -176,10 +206,11 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
   a.cmax = plan.cmax;
   a.smax = plan.smax;
   a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
-  a.gate_mode = gate_mode;
+  a.gate_mode = x.gate_mode;
   a.lower_bound = d.lower_bound;
-  a.a_log = a_log;
-  a.dt_bias = dt_bias;
+  a.a_log = x.a_log;
+  a.dt_bias = x.dt_bias;
+  a.trans = x.transition;
   a.init = initial_state;
   a.seg_ids = segment_ids;
   a.o = o;
@@ -195,16 +226,22 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
   if (d.B == 0 || d.H == 0) return KDA_OK;
   hipError_t e = hipSuccess;
   const hipStream_t s = a.stream;
-  if (has_seg) {
-    if (d.T == 0) return KDA_OK;
-    e = observed("kda_prep", s, [&] { return kda::launch_prep(a); });
-  } else if (d.T == 0) {
-    e = observed("kda_zero_states", s, [&] { return kda::launch_zero_states(a); });
+  if (d.T == 0) {
+    // No token, so no segment: every requested state slot (and transition) is zero.
+    if (!x.rerun) e = observed("kda_zero_states", s, [&] { return kda::launch_zero_states(a); });
     if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
     return KDA_OK;
   }
-  if (e == hipSuccess) e = observed("kda_intra", s, [&] { return kda::launch_intra(a); });
+  if (!x.rerun) {
+    if (has_seg) e = observed("kda_prep", s, [&] { return kda::launch_prep(a); });
+    if (e == hipSuccess) e = observed("kda_intra", s, [&] { return kda::launch_intra(a); });
+  }
   if (e == hipSuccess) e = observed("kda_recur", s, [&] { return kda::launch_recur(a); });
+  if (e == hipSuccess && a.trans != nullptr) {
+    kda::CallArgs t = a;
+    t.trans_only = true;
+    e = observed("kda_transition", s, [&] { return kda::launch_recur(t); });
+  }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return KDA_OK;
 }
@@ -272,5 +309,108 @@ void kda_set_launch_observer(kda_launch_observer_t fn, void* user) {
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
 const char* kda_version(void) { return "kda-mi355x 0.1.0"; }
+
+}  // extern "C"
+
+namespace {
+
+kda_status_t cp_validate(const kda_cp_desc_t* d) {
+  if (d == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
+  if (d->B < 0 || d->T < 0 || d->H < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "B, T and H must be >= 0");
+  if (d->P < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "P must be >= 1");
+  if (d->T % d->P != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "T must be a multiple of P");
+  if (d->n_states < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "n_states must be >= 1");
+  if (!is_pow_ok(d->K) || !is_pow_ok(d->V)) return fail(KDA_ERR_NOT_IMPLEMENTED, "K and V must each be 64 or 128");
+  if (d->B * d->P * d->n_states * d->H > (int64_t)INT32_MAX)
+    return fail(KDA_ERR_NOT_IMPLEMENTED, "B * P * n_states * H above 2^31 is not supported");
+  return KDA_OK;
+}
+
+kda::CpArgs cp_args(const kda_cp_desc_t* d, void* stream) {
+  kda::CpArgs a{};
+  a.B = d->B; a.T = d->T; a.H = d->H; a.K = d->K; a.V = d->V;
+  a.P = d->P;
+  a.nm = d->n_states;
+  a.stream = static_cast<hipStream_t>(stream);
+  return a;
+}
+
+kda_status_t cp_launch(const char* name, hipStream_t s, hipError_t (*fn)(const kda::CpArgs&), const kda::CpArgs& a) {
+  const hipError_t e = observed(name, s, [&] { return fn(a); });
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return KDA_OK;
+}
+
+bool all_aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_cp_plan(const kda_cp_desc_t* desc, const int32_t* segment_ids, int32_t* plan, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0) return KDA_OK;
+  if (plan == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (desc->T == 0) return fail(KDA_ERR_INVALID_ARGUMENT, "T must be >= 1 to be cut into slices");
+  if (!all_aligned16({segment_ids, plan})) return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.seg = segment_ids;
+  a.plan = plan;
+  return cp_launch("kda_cp_plan", a.stream, kda::launch_cp_plan, a);
+}
+
+kda_status_t kda_cp_gather_states(const kda_cp_desc_t* desc, const int32_t* plan, const float* initial_state,
+                                  const float* carry, float* local_states, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0 || desc->H == 0) return KDA_OK;
+  if (!plan || !local_states) return fail(KDA_ERR_INVALID_ARGUMENT, "plan and local_states must be non-NULL");
+  if (!all_aligned16({plan, initial_state, carry, local_states}))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.plan = const_cast<int32_t*>(plan);
+  a.init = initial_state;
+  a.carry = const_cast<float*>(carry);
+  a.local = local_states;
+  return cp_launch("kda_cp_gather", a.stream, kda::launch_cp_gather, a);
+}
+
+kda_status_t kda_cp_chain(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_final,
+                          const float* transition, float* carry, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0 || desc->H == 0) return KDA_OK;
+  if (!plan || !local_final || !transition || !carry)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "plan, local_final, transition and carry must be non-NULL");
+  if (!all_aligned16({plan, local_final, transition, carry}))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.plan = const_cast<int32_t*>(plan);
+  a.local = const_cast<float*>(local_final);
+  a.trans = transition;
+  a.carry = carry;
+  return cp_launch("kda_cp_chain", a.stream, kda::launch_cp_chain, a);
+}
+
+kda_status_t kda_cp_scatter_states(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_final,
+                                   float* final_state, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0 || desc->H == 0) return KDA_OK;
+  if (!plan || !local_final || !final_state)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "plan, local_final and final_state must be non-NULL");
+  if (!all_aligned16({plan, local_final, final_state}))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.plan = const_cast<int32_t*>(plan);
+  a.local = const_cast<float*>(local_final);
+  a.fin = final_state;
+  return cp_launch("kda_cp_scatter", a.stream, kda::launch_cp_scatter, a);
+}
 
 }  // extern "C"

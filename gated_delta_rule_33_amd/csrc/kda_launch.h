@@ -32,6 +32,8 @@ struct CallArgs {
   const int32_t* seg_ids;
   void* o;
   float* fin;
+  float* trans;                // [B,H,K,K] transition of each row's first segment, or NULL
+  bool trans_only;             // launch_recur: compute the transition instead of o / states
   // Workspace carve-up.
   TableHeader* hdr;
   SegEntry* segs;
@@ -63,14 +65,34 @@ struct NormArgs {
   hipStream_t stream;
 };
 
+// Context-parallel glue over B rows cut into P slices (one call covers all
+// slices).  nm = state slots per row (max_segments, or 1 without segment ids).
+struct CpArgs {
+  int64_t B, T, H, K, V;
+  int P, nm;
+  const int32_t* seg;         // [B,T] or NULL (plan)
+  int32_t* plan;              // [B,P,4]: carried, first global segment, local segments, overflow
+  const float* init;          // [B,nm,H,K,V] caller's start states or NULL (gather)
+  float* carry;               // [B*P,H,K,V] chain states (chain: out; gather: in, NULL = zeros)
+  float* local;               // [B*P,nm,H,K,V] per-slice states (gather: out; chain, scatter: in)
+  const float* trans;         // [B*P,H,K,K] (chain)
+  float* fin;                 // [B,nm,H,K,V] (scatter: out)
+  hipStream_t stream;
+};
+
 int64_t record_bytes(InType in, int64_t K, int64_t V);
 
 hipError_t launch_prep(const CallArgs& a);
 hipError_t launch_intra(const CallArgs& a);
 hipError_t launch_recur(const CallArgs& a);
 hipError_t launch_zero_states(const CallArgs& a);
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
+hipError_t launch_cp_plan(const CpArgs& a);
+hipError_t launch_cp_gather(const CpArgs& a);
+hipError_t launch_cp_chain(const CpArgs& a);
+hipError_t launch_cp_scatter(const CpArgs& a);
 int cu_count();
 
 }  // namespace kda

@@ -173,13 +173,19 @@ hipError_t launch_prep(const CallArgs& a) {
   return hipGetLastError();
 }
 
-// final_state when no segment can occur (T == 0 without segment_ids).
-hipError_t launch_zero_states(const CallArgs& a) {
-  const int64_t n = a.B * a.H * a.K * a.V;
-  if (n <= 0 || a.fin == nullptr) return hipSuccess;
+hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream) {
+  if (n <= 0 || x == nullptr) return hipSuccess;
   const unsigned grid = (unsigned)std::min<int64_t>(1024, (n + 255) / 256);
-  hipLaunchKernelGGL(kda_fill_zero_kernel, dim3(grid), dim3(256), 0, a.stream, a.fin, n);
+  hipLaunchKernelGGL(kda_fill_zero_kernel, dim3(grid), dim3(256), 0, stream, x, n);
   return hipGetLastError();
+}
+
+// final_state (every slot: one per row, or max_segments per row with
+// segment ids) and the transition when no segment can occur (T == 0).
+hipError_t launch_zero_states(const CallArgs& a) {
+  hipError_t e = launch_fill_zero(a.fin, a.smax * a.H * a.K * a.V, a.stream);
+  if (e == hipSuccess) e = launch_fill_zero(a.trans, a.B * a.H * a.K * a.K, a.stream);
+  return e;
 }
 
 }  // namespace kda

@@ -174,6 +174,7 @@ struct RecurParams {
   const float* init;
   float* fin;
   void* o;
+  float* trans;   // [B,H,K,K] transition of each row's carried state, or NULL
 };
 
 template <class TI, class TO, int K, int V, int TPW>
@@ -428,7 +429,17 @@ __global__ __launch_bounds__(Roles<TPW>::kThreads) void kda_recur_kernel(RecurPa
 // chunk: B1 after the Delta phase (Delta visible), B2 at the end (the new
 // state visible, the Delta buffer free).  The fifth wave pulls records a few
 // chunks ahead into L2.
-template <class TI, class TO, int K, int V>
+//
+// With kTrans the same loop carries, instead of the state, the transition of
+// a row's first segment: the recurrence is affine in the state a segment
+// starts from, S_end = M S_start + (S_end for S_start = 0), and M is the
+// chunk product of diag(exp(G_C)) - Kt^T W, i.e. the loop above with U = 0
+// and S_start = I, with no read-out.  Its columns (K of them, one 16-wide
+// tile per workgroup) index the key channels of S_start.  It exists only
+// where one segment runs from the row's first token to its last (every row
+// without segment ids); the caller zero-fills the others.  This is the
+// transfer matrix a context-parallel rank passes on with its end state.
+template <class TI, class TO, int K, int V, bool kTrans>
 __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_kernel(RecurParams p) {
   using P = Prec<TI>;
   using PS = typename P::S;
@@ -439,7 +450,8 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   using PA = typename P::Aq;
   using L = RecordLayout<TI, K, V>;
   constexpr int kPrefetchWave = kComputeWaves;
-  constexpr int NV = V / kVT;      // workgroups per (sequence, head)
+  constexpr int NCOL = kTrans ? K : V;   // columns of the carried matrix
+  constexpr int NV = NCOL / kVT;   // workgroups per (sequence, head)
   constexpr int NCB = K / 64;      // key-channel blocks of the state per wave
   constexpr int KB = K / 32;       // 32-deep key slabs
   // S and Delta as operand tiles in fragment order (k = key channel / token):
@@ -468,6 +480,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   int64_t b, slot, n_chunks, first_chunk, t_begin, seq_len;
   if (p.packed) {
     const SegEntry se = p.segs[sq];
+    if (kTrans && (se.t0 != 0 || se.len != p.T)) return;   // no segment spans this row
     b = se.b;
     slot = ((int64_t)se.b * p.n_max + se.local) * H + h;
     n_chunks = se.n_chunks;
@@ -487,7 +500,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   // ---- L2 prefetch wave: touches this workgroup's 1/NV share of the record
   // kPrefetchAhead chunks ahead (every 64-byte segment once).
   if (wave == kPrefetchWave) {
-    constexpr int SEGS = (int)(L::kBytes / 64);
+    constexpr int SEGS = (int)((kTrans ? L::kQg : L::kBytes) / 64);   // the transition reads Wn and Kt only
     constexpr int SHARE = (SEGS + NV - 1) / NV;
     auto prefetch = [&](int64_t n) {
       const char* r = record(n);
@@ -521,7 +534,8 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   auto load_w = [&](const char* r) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
-    u = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + j) * 1024)[lane];
+    if constexpr (kTrans) u = f32x4{0, 0, 0, 0};
+    else u = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + j) * 1024)[lane];
   };
   auto load_kt = [&](const char* r) {
 #pragma unroll
@@ -532,6 +546,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     }
   };
   auto load_q = [&](const char* r) {
+    if constexpr (kTrans) return;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
 #pragma unroll
@@ -545,8 +560,10 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   for (int c = 0; c < NCB; ++c) {
     const int c0 = 16 * (w * NCB + c) + 4 * gq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      st[c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kTrans) st[c][i] = (c0 + i == v0 + m) ? 1.f : 0.f;
+      else st[c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
+    }
     float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
     const int cb = w * NCB + c;
     PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
@@ -602,30 +619,39 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     }
     load_kt(rn1);
 
-    // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
-    f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+    if constexpr (!kTrans) {
+      // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
+      f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
 #pragma unroll
-    for (int kb = 0; kb < KB; kb += 2) {
-      mma(o0, qg[kb], sf[kb]);
-      if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
-    }
-    mma(o1, aq[0], dd[0]);
-    if (w >= 2) mma(o0, aq[1], dd[1]);
-    load_q(rn1);
-    const int rw = 16 * w + 4 * gq;
-    const int64_t ob = ((b * p.T + t0 + rw) * H + h) * V + v0 + m, rs = H * V;
-    if (len == kChunk) {
+      for (int kb = 0; kb < KB; kb += 2) {
+        mma(o0, qg[kb], sf[kb]);
+        if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
+      }
+      mma(o1, aq[0], dd[0]);
+      if (w >= 2) mma(o0, aq[1], dd[1]);
+      load_q(rn1);
+      const int rw = 16 * w + 4 * gq;
+      const int64_t ob = ((b * p.T + t0 + rw) * H + h) * V + v0 + m, rs = H * V;
+      if (len == kChunk) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) store_out(out, ob + i * rs, o0[i] + o1[i]);
-    } else {
+        for (int i = 0; i < 4; ++i) store_out(out, ob + i * rs, o0[i] + o1[i]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (rw + i < len) store_out(out, ob + i * rs, o0[i] + o1[i]);
+        for (int i = 0; i < 4; ++i)
+          if (rw + i < len) store_out(out, ob + i * rs, o0[i] + o1[i]);
+      }
     }
     block_sync();   // B2
   }
 
-  if (p.fin) {
+  if constexpr (kTrans) {
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int c0 = 16 * (w * NCB + c) + 4 * gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p.trans[((b * H + h) * K + c0 + i) * K + v0 + m] = st[c][i];
+    }
+  } else if (p.fin) {
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
       const int c0 = 16 * (w * NCB + c) + 4 * gq;
@@ -647,14 +673,25 @@ hipError_t launch_recur_w(const RecurParams& p, int64_t seq_heads, hipStream_t s
 template <class TI, class TO, int K, int V>
 hipError_t launch_recur_t(const CallArgs& a) {
   RecurParams p{a.B, a.T, a.H, a.nc_fixed, a.n_max > 0, a.n_max, a.B * a.H, a.hdr, a.segs,
-                a.records, a.record_bytes, a.init, a.fin, a.o};
+                a.records, a.record_bytes, a.init, a.fin, a.o, a.trans};
   const int64_t seq_heads = (a.n_max > 0 ? a.smax : a.B) * a.H;
   if (seq_heads <= 0) return hipSuccess;
+  if (a.trans_only) {
+    // Rows without a segment that spans them keep the zero transition.
+    if (a.n_max > 0) {
+      const hipError_t e = launch_fill_zero(a.trans, a.B * a.H * a.K * a.K, a.stream);
+      if (e != hipSuccess) return e;
+    }
+    const int64_t tgrid = (seq_heads + 7) / 8 * 8 * (K / kVT);
+    hipLaunchKernelGGL((kda_recur_reg_kernel<TI, TO, K, V, true>), dim3((unsigned)tgrid),
+                       dim3((kComputeWaves + 1) * kWave), 0, a.stream, p);
+    return hipGetLastError();
+  }
   // Two tiles per workgroup once one tile per workgroup would need several
   // rounds of workgroups over the CUs.
   if (seq_heads * (V / kVT) > 2 * (int64_t)cu_count()) return launch_recur_w<TI, TO, K, V, 2>(p, seq_heads, a.stream);
   const int64_t grid = (seq_heads + 7) / 8 * 8 * (V / kVT);
-  hipLaunchKernelGGL((kda_recur_reg_kernel<TI, TO, K, V>), dim3((unsigned)grid), dim3((kComputeWaves + 1) * kWave), 0,
+  hipLaunchKernelGGL((kda_recur_reg_kernel<TI, TO, K, V, false>), dim3((unsigned)grid), dim3((kComputeWaves + 1) * kWave), 0,
                      a.stream, p);
   return hipGetLastError();
 }

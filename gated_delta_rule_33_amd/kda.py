@@ -21,9 +21,10 @@ KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 
-EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_short_conv_fwd",
-            "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer", "kda_last_error",
-            "kda_version")
+EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_transition",
+            "kda_chunk_fwd_rerun", "kda_cp_plan", "kda_cp_gather_states", "kda_cp_chain", "kda_cp_scatter_states",
+            "kda_short_conv_fwd", "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer",
+            "kda_last_error", "kda_version")
 
 # void (*)(const char* kernel_name, void* stream, int phase, void* user)
 LAUNCH_OBSERVER = ctypes.CFUNCTYPE(None, ctypes.c_char_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p)
@@ -36,6 +37,12 @@ class KdaFwdDesc(ctypes.Structure):
                 ("scale", ctypes.c_float), ("chunk_size", ctypes.c_int32),
                 ("use_qk_l2norm", ctypes.c_int32), ("safe_gate", ctypes.c_int32),
                 ("lower_bound", ctypes.c_float), ("max_segments", ctypes.c_int32)]
+
+
+class KdaCpDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
+                ("K", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("P", ctypes.c_int32), ("n_states", ctypes.c_int32)]
 
 
 class KdaError(RuntimeError):
@@ -61,6 +68,17 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd_gated.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    lib.kda_chunk_fwd_transition.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_fwd_transition.restype = ctypes.c_int
+    lib.kda_chunk_fwd_rerun.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, sz, p]
+    lib.kda_chunk_fwd_rerun.restype = ctypes.c_int
+    cpd = ctypes.POINTER(KdaCpDesc)
+    lib.kda_cp_plan.argtypes = [cpd, p, p, p]
+    lib.kda_cp_gather_states.argtypes = [cpd, p, p, p, p, p]
+    lib.kda_cp_chain.argtypes = [cpd, p, p, p, p, p]
+    lib.kda_cp_scatter_states.argtypes = [cpd, p, p, p, p]
+    for f in (lib.kda_cp_plan, lib.kda_cp_gather_states, lib.kda_cp_chain, lib.kda_cp_scatter_states):
+        f.restype = ctypes.c_int
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     lib.kda_short_conv_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, p]
     lib.kda_short_conv_fwd.restype = ctypes.c_int
@@ -141,7 +159,8 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
     if disable_recompute:
         raise NotImplementedError("disable_recompute concerns the backward pass, which is not implemented")
     if cp_context is not None:
-        raise NotImplementedError("context parallelism is not implemented (single device)")
+        raise NotImplementedError("context parallelism across devices is not implemented; chunk_kda_cp runs "
+                                  "its state chaining with the ranks' slices on one device")
     if lower_bound is not None and not safe_gate:
         warnings.warn("lower_bound is ignored without safe_gate", stacklevel=2)
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
@@ -178,7 +197,11 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
     fin = torch.empty(state_shape, dtype=torch.float32, device=q.device) if output_final_state else None
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lib = load_library()
-    tail = (_ptr(initial_state), _ptr(segment_ids), _ptr(o), _ptr(fin), _ptr(workspace),
+    seg_arg = segment_ids
+    if segment_ids is not None and segment_ids.numel() == 0:
+        # an empty tensor has no address, and NULL would mean "no segment ids"
+        seg_arg = torch.zeros(4, dtype=torch.int32, device=q.device)
+    tail = (_ptr(initial_state), _ptr(seg_arg), _ptr(o), _ptr(fin), _ptr(workspace),
             ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream))
     if use_gate_in_kernel:
         st = lib.kda_chunk_fwd_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
@@ -322,3 +345,107 @@ def read_flags(workspace) -> int:
                                                   ctypes.c_void_p(stream), ctypes.byref(flags)),
                "kda_chunk_fwd_flags")
     return int(flags.value)
+
+
+class CpCall:
+    """The context-parallel forward of ``chunk_kda_cp`` with every buffer
+    allocated and every argument marshalled once; ``enqueue()`` makes the
+    seven C-ABI calls on the current stream (for timing loops too)."""
+
+    def __init__(self, q, k, v, g, beta, cp_size: int, scale=None, initial_state=None,
+                 output_final_state=False, use_qk_l2norm_in_kernel=False, safe_gate=False, lower_bound=None,
+                 segment_ids=None, N_max=None, out_dtype=None):
+        import torch
+        for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+            if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+                raise ValueError(f"{name} must be a contiguous device tensor of q's dtype")
+        B, T, H, K = q.shape
+        V = v.shape[-1]
+        if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:3]) != (B, T, H) \
+                or tuple(beta.shape) != (B, T, H):
+            raise ValueError("shape mismatch: q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H]")
+        P = int(cp_size)
+        if P < 1 or T == 0 or T % P != 0:
+            raise ValueError("cp_size must be >= 1 and divide T >= 1")
+        L = T // P
+        out_dtype = torch.float32 if out_dtype is None else out_dtype
+        packed = segment_ids is not None
+        if packed:
+            if segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != (B, T) \
+                    or not segment_ids.is_contiguous():
+                raise ValueError("segment_ids must be a contiguous int32 [B, T] tensor")
+            if N_max is None or N_max < 1:
+                raise ValueError("packed input (segment_ids) needs a positive N_max (max segments per row)")
+        nm = int(N_max) if packed else 1
+        gshape = (B, H, K, V) if not packed else (B, nm, H, K, V)
+        if initial_state is not None and (initial_state.dtype != torch.float32
+                                          or tuple(initial_state.shape) != gshape
+                                          or not initial_state.is_contiguous()):
+            raise ValueError(f"initial_state must be a contiguous float32 {gshape} tensor")
+        dev = q.device
+        rows = B * P
+        lshape = (rows, H, K, V) if not packed else (rows, nm, H, K, V)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.plan = torch.empty((B, P, 4), dtype=torch.int32, device=dev)
+        self.local_init = torch.empty(lshape, **f32)
+        self.local_fin = torch.empty(lshape, **f32)
+        self.transition = torch.empty((rows, H, K, K), **f32)
+        self.carry = torch.empty((rows, H, K, V), **f32)
+        self.o = torch.empty((B, T, H, V), dtype=out_dtype, device=dev)
+        self.final_state = torch.empty(gshape, **f32) if output_final_state else None
+        self.cp = KdaCpDesc(B=B, T=T, H=H, K=K, V=V, P=P, n_states=nm)
+        self.desc = make_desc(rows, L, H, K, V, _dtype_code(q.dtype), _dtype_code(out_dtype), scale,
+                              use_qk_l2norm_in_kernel, safe_gate, lower_bound if safe_gate else None,
+                              nm if packed else 0)
+        ws_bytes = max(workspace_size(self.desc, packed), 1)
+        self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        self.views = [t.view((rows, L) + tuple(t.shape[2:])) for t in (q, k, v, g, beta)]
+        self.keep = (q, k, v, g, beta, initial_state, segment_ids)
+        seg_local = segment_ids.view(rows, L) if packed else None
+        stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        cp, d, ws = ctypes.byref(self.cp), ctypes.byref(self.desc), (_ptr(self.workspace), ctypes.c_size_t(ws_bytes))
+        lib = load_library()
+        plan, init = _ptr(self.plan), _ptr(initial_state)
+        self.steps = [
+            (lib.kda_cp_plan, (cp, _ptr(segment_ids), plan, stream)),
+            (lib.kda_cp_gather_states, (cp, plan, init, None, _ptr(self.local_init), stream)),
+            (lib.kda_chunk_fwd_transition, (d, *[_ptr(t) for t in self.views], _ptr(self.local_init),
+                                            _ptr(seg_local), _ptr(self.o), _ptr(self.local_fin),
+                                            _ptr(self.transition), *ws, stream)),
+            (lib.kda_cp_chain, (cp, plan, _ptr(self.local_fin), _ptr(self.transition), _ptr(self.carry), stream)),
+            (lib.kda_cp_gather_states, (cp, plan, init, _ptr(self.carry), _ptr(self.local_init), stream)),
+            (lib.kda_chunk_fwd_rerun, (d, _ptr(self.local_init), _ptr(seg_local), _ptr(self.o),
+                                       _ptr(self.local_fin), *ws, stream)),
+        ]
+        if output_final_state:
+            self.steps.append((lib.kda_cp_scatter_states, (cp, plan, _ptr(self.local_fin), _ptr(self.final_state),
+                                                           stream)))
+
+    def enqueue(self):
+        for fn, args in self.steps:
+            _raise_for(fn(*args), fn.__name__)
+
+
+def chunk_kda_cp(q, k, v, g, beta, cp_size: int, scale: Optional[float] = None, initial_state=None,
+                 output_final_state: bool = False, use_qk_l2norm_in_kernel: bool = False, safe_gate: bool = False,
+                 lower_bound: Optional[float] = None, segment_ids=None, N_max: Optional[int] = None,
+                 out_dtype=None, return_internals: bool = False):
+    """The forward with T cut into cp_size equal slices, one per
+    context-parallel rank, and the recurrent state carried across the cuts
+    (the state chaining of the page "feat(kda): integrate KDA attention with
+    tokamax backend and CP support", Context Parallelism Support), all
+    slices on one device.  Arguments and results are those of chunk_kda
+    (T must be a multiple of cp_size); the result equals the unsplit forward
+    up to rounding.  The C-ABI steps, in order: plan, gather (zero carried
+    states), forward with transitions, chain, gather (chained states), rerun
+    of the recurrence, scatter of the final states.
+    With return_internals, also returns a dict with the plan [B, P, 4], the
+    transitions [B*P, H, K, K] and the chained states [B*P, H, K, V]."""
+    if lower_bound is not None and not safe_gate:
+        warnings.warn("lower_bound is ignored without safe_gate", stacklevel=2)
+    call = CpCall(q, k, v, g, beta, cp_size, scale, initial_state, output_final_state, use_qk_l2norm_in_kernel,
+                  safe_gate, lower_bound, segment_ids, N_max, out_dtype)
+    call.enqueue()
+    if return_internals:
+        return call.o, call.final_state, dict(plan=call.plan, transition=call.transition, carry=call.carry)
+    return call.o, call.final_state

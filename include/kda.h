@@ -127,6 +127,121 @@ kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * The forward, plus each row's transition: the recurrence is affine in the
+ * state the row's first segment starts from, so the state after the row's
+ * last token is  M * S_start + (that state for S_start = 0),  with M the
+ * K x K matrix this call writes (the product over the tokens t of the
+ * segment, last on the left, of (I - beta_t k_t k_t^T) diag(exp(g_t))).
+ * This is what a context-parallel rank hands on with its end state (page
+ * "feat(kda): integrate KDA attention with tokamax backend and CP support",
+ * Context Parallelism Support: the recurrent state is coordinated across
+ * ranks).
+ *   transition  fp32 [B,H,K,K], row-major (row = key channel of the end
+ *               state, column = key channel of S_start), device memory,
+ *               non-NULL.  M is zero for a row whose first and last tokens
+ *               are not in one segment (a segment boundary or padding in
+ *               between, or padding at either end) and for T = 0.
+ * Every other argument, the workspace size and the errors are those of
+ * kda_chunk_fwd.  The workspace keeps the chunk records for
+ * kda_chunk_fwd_rerun.
+ */
+kda_status_t kda_chunk_fwd_transition(const kda_fwd_desc_t* desc,
+                                      const void* q, const void* k, const void* v,
+                                      const void* g, const void* beta,
+                                      const float* initial_state, const int32_t* segment_ids,
+                                      void* o, float* final_state, float* transition,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Runs again only the inter-chunk recurrence of the last forward call
+ * (kda_chunk_fwd, kda_chunk_fwd_gated or kda_chunk_fwd_transition) made on
+ * `workspace`, with new start states: the chunk-local work does not depend
+ * on the state, and the workspace still holds its results.  desc and
+ * segment_ids (only whether it is NULL matters) must be those of that call,
+ * and the workspace must be untouched since.  Writes o for every token of a
+ * segment and final_state for every segment that occurs; positions the
+ * earlier call zeroed (padding tokens, slots of absent segments) are not
+ * written again, so pass the same o and final_state buffers to keep them.
+ * This is the second pass of a context-parallel rank, once the state its
+ * slice continues from is known.
+ */
+kda_status_t kda_chunk_fwd_rerun(const kda_fwd_desc_t* desc, const float* initial_state,
+                                 const int32_t* segment_ids, void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Context-parallel state chaining (page "feat(kda): integrate KDA attention
+ * with tokamax backend and CP support", Context Parallelism Support: the
+ * kernel derives per-rank sequence metadata from segment_ids and carries the
+ * recurrent state across ranks; its tests split T over 2 or 4 ranks,
+ * including packed segments that cross a split or begin exactly at one).
+ * Each of B rows of T tokens is cut into P slices of T/P tokens, slice r
+ * being rank r's share; one call handles all B*P slices, which are the rows
+ * of the per-slice forward calls ([B*P, T/P, ...] views of the inputs).
+ *   1. kda_cp_plan                per slice: continues the previous slice's
+ *                                 segment?, global index of its first local
+ *                                 segment, local segment count.
+ *   2. kda_cp_gather_states       per-slice start states, carry = NULL (the
+ *                                 continued segment starts from zero).
+ *   3. kda_chunk_fwd_transition   on the slices: end states and transitions.
+ *   4. kda_cp_chain               C_{r+1} = E_r + [slice r continues] M_r C_r,
+ *                                 the state each continuing slice starts from.
+ *   5. kda_cp_gather_states       with carry = C.
+ *   6. kda_chunk_fwd_rerun        on the same workspace: exact o and states.
+ *   7. kda_cp_scatter_states      per-segment final states, global layout.
+ * Across GPUs step 4 is P-1 point-to-point hops of one state per (row,
+ * head); this library runs all hops on one GPU.
+ *
+ * n_states is the number of state slots per row: max_segments with segment
+ * ids (states [B,n_states,H,K,V] globally, [B*P,n_states,H,K,V] per slice),
+ * 1 without (the [B,H,K,V] / [B*P,H,K,V] layouts).  A row with more than
+ * n_states segments sets the overflow field of the plan; results for such
+ * rows are unspecified.  All pointers are device pointers, 16-byte aligned;
+ * calls are asynchronous on `stream` and allocate nothing.
+ */
+typedef struct {
+  int64_t B, T, H;   /* rows, tokens per row (a multiple of P), heads */
+  int64_t K, V;      /* 64 or 128 each */
+  int32_t P;         /* slices per row (ranks), >= 1 */
+  int32_t n_states;  /* state slots per row, >= 1 */
+} kda_cp_desc_t;
+
+/*
+ * plan: int32 [B,P,4] written per slice (b, r): {continues (0/1), global
+ * index of the first local segment, local segments, overflow (0/1)}.
+ * segment_ids: NULL (each row one sequence) or int32 [B,T] as for
+ * kda_chunk_fwd.  T must be >= 1.
+ */
+kda_status_t kda_cp_plan(const kda_cp_desc_t* desc, const int32_t* segment_ids, int32_t* plan, void* stream);
+
+/*
+ * local_states [B*P,n_states,H,K,V]: slot l of slice (b, r) gets the start
+ * state of its local segment l: carry[b*P + r] (zero if carry is NULL) for a
+ * continued segment, else initial_state of its global segment (zero if
+ * initial_state is NULL); unused slots get zero.
+ * initial_state: NULL or [B,n_states,H,K,V];  carry: NULL or [B*P,H,K,V].
+ */
+kda_status_t kda_cp_gather_states(const kda_cp_desc_t* desc, const int32_t* plan, const float* initial_state,
+                                  const float* carry, float* local_states, void* stream);
+
+/*
+ * carry [B*P,H,K,V]: the state slice (b, r) continues from (C_r above; zero
+ * for r = 0 and for slices that start a new segment or padding).
+ * local_final [B*P,n_states,H,K,V] and transition [B*P,H,K,K] are the outputs
+ * of step 3.  Accumulates in fp32.
+ */
+kda_status_t kda_cp_chain(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_final,
+                          const float* transition, float* carry, void* stream);
+
+/*
+ * final_state [B,n_states,H,K,V]: each segment's state after its last token,
+ * taken from the last slice that holds it; slots of segments that do not
+ * occur get zero.  local_final is the final_state of step 6.
+ */
+kda_status_t kda_cp_scatter_states(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_final,
+                                   float* final_state, void* stream);
+
+/*
  * Short convolution, the layer step that q, k and v each pass through before
  * the kernel (page "feat(kda): integrate KDA attention with tokamax backend
  * and CP support", Implementation Details, Layer architecture, step 1: a

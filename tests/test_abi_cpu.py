@@ -131,6 +131,53 @@ def test_layer_steps_reject_before_any_launch():
     assert norm(0, 128) == kda.KDA_OK
 
 
+def test_transition_and_rerun_reject_before_any_launch():
+    lib = kda.load_library()
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    n = kda.workspace_size(d, False)
+    # no transition buffer
+    st = lib.kda_chunk_fwd_transition(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, fake, None, None,
+                                      fake, ctypes.c_size_t(n), None)
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
+    # misaligned transition buffer
+    st = lib.kda_chunk_fwd_transition(ctypes.byref(d), fake, fake, fake, fake, fake, None, None, fake, None,
+                                      ctypes.c_void_p(0x1004), fake, ctypes.c_size_t(n), None)
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
+    # the rerun needs o and a workspace of the forward's size
+    st = lib.kda_chunk_fwd_rerun(ctypes.byref(d), None, None, None, None, fake, ctypes.c_size_t(n), None)
+    assert st == kda.KDA_ERR_INVALID_ARGUMENT
+    st = lib.kda_chunk_fwd_rerun(ctypes.byref(d), None, None, fake, None, fake, ctypes.c_size_t(16), None)
+    assert st == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_cp_steps_reject_before_any_launch():
+    lib = kda.load_library()
+    fake = ctypes.c_void_p(0x1000)
+
+    def cp(**kw):
+        base = dict(B=1, T=256, H=2, K=128, V=128, P=2, n_states=1)
+        base.update(kw)
+        return kda.KdaCpDesc(**base)
+
+    plan = lambda d, seg=None, out=fake: lib.kda_cp_plan(ctypes.byref(d), seg, out, None)
+    assert plan(cp(P=0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert plan(cp(T=250, P=4)) == kda.KDA_ERR_INVALID_ARGUMENT       # T not a multiple of P
+    assert plan(cp(T=0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert plan(cp(K=96)) == kda.KDA_ERR_NOT_IMPLEMENTED
+    assert plan(cp(n_states=0)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert plan(cp(), out=None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert plan(cp(), seg=ctypes.c_void_p(0x1004)) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert plan(cp(B=0)) == kda.KDA_OK                                 # empty: nothing to do
+    d = cp()
+    assert lib.kda_cp_gather_states(ctypes.byref(d), fake, None, None, None, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_cp_chain(ctypes.byref(d), fake, fake, None, fake, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_cp_chain(ctypes.byref(d), fake, fake, fake, ctypes.c_void_p(0x1008), None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_cp_scatter_states(ctypes.byref(cp(V=32)), fake, fake, fake, None) == kda.KDA_ERR_NOT_IMPLEMENTED
+    assert lib.kda_cp_scatter_states(ctypes.byref(d), fake, None, fake, None) == kda.KDA_ERR_INVALID_ARGUMENT
+
+
 def test_python_wrapper_rejects_unsupported_options():
     torch = pytest.importorskip("torch")
     z = torch.zeros(1)
@@ -140,3 +187,5 @@ def test_python_wrapper_rejects_unsupported_options():
         kda.chunk_kda(z, z, z, z, z, cp_context=object())
     with pytest.raises(ValueError, match="device tensor"):
         kda.chunk_kda(z, z, z, z, z)
+    with pytest.raises(ValueError, match="device tensor"):
+        kda.chunk_kda_cp(z, z, z, z, z, cp_size=2)

@@ -1,0 +1,208 @@
+"""Context-parallel state chaining on the GPU (through the C ABI) against the
+oracle: the forward with T cut into P slices, one per rank, must equal the
+unsplit forward, as the CP tests of the page "feat(kda): integrate KDA
+attention with tokamax backend and CP support" require (CP = 2 and 4
+equivalence; packed segments that cross a cut or begin exactly at one).
+The pieces are checked too: the slice plan (bit-exact), each slice's
+transition (against the oracle's product of per-token maps) and the chained
+states (against the oracle's state at each cut).
+Bar: max|err| / rms(ref) <= 1e-4 for fp32 inputs, <= 2e-2 for bf16 inputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import cp as cp_oracle
+from gated_delta_rule_33_amd.inputs import WORKLOADS, Workload, bf16_bits_to_f32, f32_to_bf16_bits, make_inputs
+from tests.gpu_helpers import TOL_BF16, TOL_F32, check, oracle_ref, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _tol(w):
+    return TOL_F32 if w.dtype == "f32" else TOL_BF16
+
+
+def _run_cp(inp, w, P, **over):
+    import torch
+    from gated_delta_rule_33_amd import kda
+    d = to_device(inp, w.dtype)
+    kw = dict(scale=inp["scale"], initial_state=d["initial_state"], output_final_state=w.final_state,
+              use_qk_l2norm_in_kernel=w.l2norm_in_kernel, safe_gate=w.safe_gate, lower_bound=w.lower_bound,
+              segment_ids=d["segment_ids"], N_max=inp["max_segments"] if d["segment_ids"] is not None else None,
+              return_internals=True)
+    kw.update(over)
+    o, fin, extra = kda.chunk_kda_cp(d["q"], d["k"], d["v"], d["g"], d["beta"], P, **kw)
+    torch.cuda.synchronize()
+    np64 = lambda t: None if t is None else t.float().cpu().numpy().astype(np.float64)
+    return np64(o), np64(fin), {k: v.cpu().numpy() for k, v in extra.items()}
+
+
+def _slices(a, P):
+    """[B, T, ...] -> [B*P, T/P, ...] (the rows of the per-slice calls)."""
+    B, T = a.shape[:2]
+    return np.ascontiguousarray(a.reshape((B * P, T // P) + a.shape[2:]))
+
+
+def _inputs(w, g_scale=1.0, segment_ids=None):
+    """The workload's seeded inputs; g_scale < 1 weakens the decay (so that
+    a slice's transition is not lost to underflow) and re-rounds g for bf16."""
+    inp = make_inputs(w, segment_ids=segment_ids)
+    if g_scale != 1.0:
+        g = (inp["g"] * np.float32(g_scale)).astype(np.float32)
+        if w.dtype == "bf16":
+            inp["g_bits"] = f32_to_bf16_bits(g)
+            g = bf16_bits_to_f32(inp["g_bits"])
+        inp["g"] = g
+    return inp
+
+
+FIXED = [
+    (Workload("cp_f32_fixed", "f32", 2, 384, 2, 64, 64, initial_state=True, final_state=True, seed=71), 0.02),
+    (Workload("cp_bf16_fixed", "bf16", 1, 1024, 4, 128, 128, gate="neg5_sigmoid", initial_state=True,
+              final_state=True, safe_gate=True, lower_bound=-5.0, seed=72), 1.0),
+    (Workload("cp_bf16_fixed_mild", "bf16", 1, 1024, 4, 128, 128, initial_state=True, final_state=True,
+              seed=74), 0.01),
+    (Workload("cp_bf16_fixed_kv", "bf16", 2, 512, 2, 128, 64, l2norm_in_kernel=True, final_state=True, seed=73),
+     0.05),
+]
+
+
+@pytest.mark.parametrize("P", [1, 2, 4])
+@pytest.mark.parametrize("case", FIXED, ids=lambda c: c[0].name)
+def test_cp_fixed_rows_match_the_unsplit_oracle(case, P):
+    w, g_scale = case
+    _say(f"[cp] {w.name} P={P}")
+    inp = _inputs(w, g_scale)
+    o, fin, _ = _run_cp(inp, w, P)
+    o_ref, fin_ref = oracle_ref(inp, w)
+    e = check(f"{w.name} P={P} o", o, o_ref, _tol(w))
+    _say(f"[cp] {w.name} P={P} o rel err {e:.3e}")
+    if w.final_state:
+        e = check(f"{w.name} P={P} final", fin, fin_ref, _tol(w))
+        _say(f"[cp] {w.name} P={P} final rel err {e:.3e}")
+
+
+def _packed_ids(P, T=1024):
+    """Three rows of segments, as (first, last + 1) runs, ids 1, 2, ...: for
+    P = 2 (cut at 512) one crossing the cut, one beginning exactly at it
+    after padding, one spanning the row; for P = 4 (cuts at 256, 512, 768)
+    crossings, a segment beginning at a cut, single padding tokens, a row
+    spanned by one segment (carried through every cut) and a slice of
+    padding only."""
+    layouts = {
+        2: [[(0, 170), (170, 549), (549, 1019)], [(0, 300), (512, 900), (900, 1024)], [(0, 1024)]],
+        4: [[(0, 85), (85, 293), (293, 507), (512, 582), (583, 1024)], [(0, 1024)], [(0, 256), (512, 1024)]],
+    }[P]
+    ids = np.zeros((len(layouts), T), np.int32)
+    for b, runs in enumerate(layouts):
+        for i, (s, e) in enumerate(runs):
+            ids[b, s:e] = i + 1
+    return ids
+
+
+@pytest.mark.parametrize("P", [2, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_cp_packed_segments_match_the_unsplit_oracle(dtype, P):
+    K = V = 64 if dtype == "f32" else 128
+    T = 1024
+    w = Workload(f"cp_{dtype}_packed", dtype, 3, T, 3, K, V, initial_state=True, final_state=True,
+                 max_segments=8, seed=80 + P)
+    seg = _packed_ids(P, T)
+    inp = _inputs(w, 0.02, segment_ids=seg)
+    _say(f"[cp] {w.name} P={P}")
+    o, fin, extra = _run_cp(inp, w, P)
+    o_ref, fin_ref = oracle_ref(inp, w)
+    np.testing.assert_array_equal(extra["plan"], cp_oracle.cp_plan(seg, w.B, T, P, w.max_segments))
+    live = seg != 0
+    e = check(f"{w.name} P={P} o", o[live], o_ref[live], _tol(w))
+    assert np.all(o[~live] == 0.0), "padding tokens must get o = 0"
+    _say(f"[cp] {w.name} P={P} o rel err {e:.3e}")
+    e = check(f"{w.name} P={P} final", fin, fin_ref, _tol(w))
+    _say(f"[cp] {w.name} P={P} final rel err {e:.3e}")
+
+
+def test_cp_plan_matches_the_oracle_on_random_layouts():
+    """Bit-exact per-slice plan over random packings (ids 0..3 in runs of 1..9)."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    rng = np.random.default_rng(90)
+    B, T, P = 7, 720, 12
+    seg = np.repeat(rng.integers(0, 4, (B, T)), rng.integers(1, 10, T), axis=1)[:, :T].astype(np.int32)
+    seg = np.ascontiguousarray(seg)
+    plan = torch.empty((B, P, 4), dtype=torch.int32, device="cuda")
+    d = kda.KdaCpDesc(B=B, T=T, H=1, K=64, V=64, P=P, n_states=40)
+    st = kda.load_library().kda_cp_plan(__import__("ctypes").byref(d), kda._ptr(torch.from_numpy(seg).cuda()),
+                                        kda._ptr(plan), None)
+    assert st == kda.KDA_OK
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(plan.cpu().numpy(), cp_oracle.cp_plan(seg, B, T, P, 40))
+
+
+@pytest.mark.parametrize("case", [FIXED[0], FIXED[2], FIXED[3]], ids=lambda c: c[0].name)
+def test_cp_transitions_and_chained_states_match_the_oracle(case):
+    """Each slice's transition against the oracle's product of per-token
+    maps, and each chained state against the oracle's state after the
+    prefix that ends at that cut (a weak decay keeps the transitions away
+    from underflow, so the chain's M C term carries weight)."""
+    w, g_scale = case
+    P = 4
+    inp = _inputs(w, g_scale)
+    _say(f"[cp] {w.name} transitions")
+    _, _, extra = _run_cp(inp, w, P)
+    sl = {n: _slices(inp[n], P) for n in ("k", "g", "beta")}
+    M_ref = cp_oracle.transition(sl["k"], sl["g"], sl["beta"], use_qk_l2norm=w.l2norm_in_kernel)
+    e = check(f"{w.name} transitions", extra["transition"], M_ref, _tol(w))
+    _say(f"[cp] {w.name} transition rel err {e:.3e}")
+    L = w.T // P
+    carry = extra["carry"].reshape(w.B, P, w.H, w.K, w.V)
+    assert np.all(carry[:, 0] == 0.0)
+    for r in range(1, P):
+        pre = {n: np.ascontiguousarray(inp[n][:, :r * L]) for n in ("q", "k", "v", "g", "beta")}
+        _, S_cut = oracle.kda_forward(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], scale=inp["scale"],
+                                      initial_state=inp["initial_state"], output_final_state=True,
+                                      use_qk_l2norm=w.l2norm_in_kernel)
+        e = check(f"{w.name} chained state at cut {r}", carry[:, r], S_cut, _tol(w))
+        _say(f"[cp] {w.name} cut {r} state rel err {e:.3e}")
+
+
+def test_cp_two_slices_on_chunk_boundaries_equal_the_unsplit_call_bitwise():
+    """With P = 2 and T/2 a multiple of 64 the second slice starts from the
+    first slice's exact end state (no transition term) and runs the same
+    chunks, so o and the final state equal the unsplit call bit for bit."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    w = FIXED[1][0]
+    inp = _inputs(w)
+    o, fin, _ = _run_cp(inp, w, 2)
+    d = to_device(inp, w.dtype)
+    o1, f1 = kda.chunk_kda(d["q"], d["k"], d["v"], d["g"], d["beta"], scale=inp["scale"],
+                           initial_state=d["initial_state"], output_final_state=True, safe_gate=True,
+                           lower_bound=-5.0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o, o1.cpu().numpy().astype(np.float64))
+    np.testing.assert_array_equal(fin, f1.cpu().numpy().astype(np.float64))
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_cp_full_size_sampled_heads(P):
+    """H=32, T=8192 with P ranks (the fixed benchmark workload cut into P
+    slices): three heads checked end to end against the unsplit oracle."""
+    w = WORKLOADS["bf16_b1_h32_t8192_fixed_state"]
+    _say(f"[cp] {w.name} full size P={P}")
+    inp = make_inputs(w)
+    o, fin, _ = _run_cp(inp, w, P)
+    assert np.all(np.isfinite(o))
+    heads = [0, 17, 31]
+    o_ref, fin_ref = oracle_ref(inp, w, heads)
+    e = check(f"full P={P} o", o[:, :, heads], o_ref, TOL_BF16)
+    _say(f"[cp] full P={P} o rel err (heads {heads}) {e:.3e}")
+    e = check(f"full P={P} final", fin[:, heads], fin_ref, TOL_BF16)
+    _say(f"[cp] full P={P} final rel err {e:.3e}")

@@ -328,3 +328,9 @@ def test_empty_inputs():
                            output_final_state=True)
     torch.cuda.synchronize()
     assert o.shape == (1, 0, 2, 128) and torch.all(fin == 0)
+    # packed: every state slot of an empty row is zero too
+    seg = torch.zeros((1, 0), dtype=torch.int32, device="cuda")
+    o, fin = kda.chunk_kda(z, z, z, z, torch.zeros((1, 0, 2), dtype=torch.bfloat16, device="cuda"),
+                           output_final_state=True, segment_ids=seg, N_max=3)
+    torch.cuda.synchronize()
+    assert fin.shape == (1, 3, 2, 128, 128) and torch.all(fin == 0)
