@@ -12,9 +12,14 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the HIP library
 in ``gated_delta_rule_33_amd/`` and never imports it.
 
-Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
-(closed forms, a transition-matrix product form, a chunk-size-independent
-block evaluation, invariants).  No part is left unpinned.
+The backward (``kda_oracle_bwd.c``, ``kda_backward``) is the reverse mode of
+the same token loop, written out by hand.
+
+Parity pins: the forward is pinned by ``tests/test_oracle_pins.py`` (closed
+forms, a transition-matrix product form, a chunk-size-independent block
+evaluation, invariants), the backward by ``tests/test_oracle_bwd_pins.py``
+(finite differences of the forward, closed forms).  No part is left
+unpinned.
 """
 from __future__ import annotations
 
@@ -29,22 +34,28 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIBS = {"f64": os.path.join(_HERE, "libkda_oracle_f64.so"),
          "f32": os.path.join(_HERE, "libkda_oracle_f32.so")}
+_BWD_SRC = os.path.join(_HERE, "kda_oracle_bwd.c")
+_BWD_LIBS = {"f64": os.path.join(_HERE, "libkda_oracle_bwd_f64.so"),
+             "f32": os.path.join(_HERE, "libkda_oracle_bwd_f32.so")}
 _REAL = {"f64": "double", "f32": "float"}
 _loaded: dict = {}
+_bwd_loaded: dict = {}
 
 ORACLE_ERRORS = {1: "bad arguments", 2: "more segments in a row than n_max", 3: "out of memory"}
 
 
 def build(force: bool = True) -> None:
-    """Compile both oracle builds with gcc (plain -O2: no fast-math, no reordering)."""
-    for prec, out in _LIBS.items():
-        if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(_SRC):
-            continue
-        tmp = out + ".tmp"
-        subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-                        f"-DREAL={_REAL[prec]}", "-o", tmp, _SRC, "-lm", "-lpthread"],
-                       check=True)
-        os.replace(tmp, out)
+    """Compile both builds of the forward and backward oracles with gcc (plain
+    -O2: no fast-math, no reordering)."""
+    for src, libs in ((_SRC, _LIBS), (_BWD_SRC, _BWD_LIBS)):
+        for prec, out in libs.items():
+            if not force and os.path.exists(out) and os.path.getmtime(out) >= os.path.getmtime(src):
+                continue
+            tmp = out + ".tmp"
+            subprocess.run(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+                            f"-DREAL={_REAL[prec]}", "-o", tmp, src, "-lm", "-lpthread"],
+                           check=True)
+            os.replace(tmp, out)
 
 
 def _lib(prec: str):
@@ -66,6 +77,20 @@ def _lib(prec: str):
         lib.kda_oracle_real_bytes.restype = ctypes.c_int
         _loaded[prec] = lib
     return _loaded[prec]
+
+
+def _bwd_lib(prec: str):
+    if prec not in _bwd_loaded:
+        path = _BWD_LIBS[prec]
+        if not os.path.exists(path) or os.path.getmtime(path) < os.path.getmtime(_BWD_SRC):
+            build(force=False)
+        lib = ctypes.CDLL(path)
+        p, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.kda_oracle_bwd.argtypes = [i64, i64, i64, i64, i64, p, p, p, p, p, ctypes.c_double, ctypes.c_int,
+                                       p, p, i64, p, p, p, p, p, p, p, p, ctypes.c_int]
+        lib.kda_oracle_bwd.restype = ctypes.c_int
+        _bwd_loaded[prec] = lib
+    return _bwd_loaded[prec]
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -144,6 +169,48 @@ def kda_forward(q, k, v, g, beta, scale: Optional[float] = None, initial_state=N
     if rc != 0:
         raise ValueError(f"oracle: {ORACLE_ERRORS.get(rc, rc)}")
     return o, fin
+
+
+def kda_backward(q, k, v, g, beta, d_o, scale: Optional[float] = None, initial_state=None, d_final_state=None,
+                 use_qk_l2norm: bool = False, segment_ids=None, max_segments: int = 0,
+                 want_d_initial_state: bool = True, precision: str = "f64", num_threads: Optional[int] = None):
+    """Gradients of the token-by-token KDA forward (``kda_oracle_bwd.c``).
+
+    The loss is sum(o * d_o) + sum(final_state * d_final_state); inputs as
+    for ``kda_forward`` (converted to fp32), d_o [B,T,H,V] and d_final_state
+    (None = zero, else the state shape) in fp64.  Returns a dict of float64
+    arrays dq, dk, dv, dg, dbeta and d_initial_state (None unless wanted).
+    """
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    f64 = lambda a: np.ascontiguousarray(a, dtype=np.float64)
+    q, k, v, g, beta = f32(q), f32(k), f32(v), f32(g), f32(beta)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    d_o = f64(d_o)
+    if d_o.shape != (B, T, H, V):
+        raise ValueError("d_o must be [B,T,H,V]")
+    if scale is None:
+        scale = 1.0 / np.sqrt(K)
+    seg = None if segment_ids is None else np.ascontiguousarray(segment_ids, dtype=np.int32)
+    state_shape = (B, H, K, V) if seg is None else (B, max_segments, H, K, V)
+    init = None if initial_state is None else f32(initial_state)
+    dfin = None if d_final_state is None else f64(d_final_state)
+    for name, a in (("initial_state", init), ("d_final_state", dfin)):
+        if a is not None and a.shape != state_shape:
+            raise ValueError(f"{name} must be {state_shape}")
+    out = {n: np.zeros(a.shape) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
+    dinit = np.zeros(state_shape) if want_d_initial_state else None
+    if num_threads is None:
+        num_threads = default_threads()
+    rc = _bwd_lib(precision).kda_oracle_bwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                            float(scale), int(bool(use_qk_l2norm)), _ptr(init), _ptr(seg),
+                                            int(max_segments), _ptr(d_o), _ptr(dfin), _ptr(out["dq"]),
+                                            _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]), _ptr(out["dbeta"]),
+                                            _ptr(dinit), int(num_threads))
+    if rc != 0:
+        raise ValueError(f"oracle: {ORACLE_ERRORS.get(rc, rc)}")
+    out["d_initial_state"] = dinit
+    return out
 
 
 def forward_inputs(inp: dict, workload, precision: str = "f64", num_threads: Optional[int] = None,
