@@ -414,3 +414,122 @@ kda_status_t kda_cp_scatter_states(const kda_cp_desc_t* desc, const int32_t* pla
 }
 
 }  // extern "C"
+
+namespace {
+
+struct BwdPlan {
+  Plan t;                      // tables (the forward's layout up to its records)
+  size_t off_rec = 0, off_hs = 0, off_dhs = 0, total = 0;
+};
+
+kda_status_t bwd_validate(const kda_fwd_desc_t* d, bool has_seg, BwdPlan* bp) {
+  BwdPlan b;
+  const kda_status_t st = validate(d, has_seg, &b.t);
+  if (st != KDA_OK) return st;
+  const size_t slots = 4 * (size_t)b.t.cmax, H = (size_t)d->H;
+  b.off_rec = b.t.off_records;
+  size_t off = align_up(b.off_rec + slots * H * (size_t)kda::bwd_record_floats(d->K, d->V) * sizeof(float));
+  b.off_hs = off;
+  off = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
+  b.off_dhs = off;
+  b.total = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
+  *bp = b;
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_bwd_workspace_size(const kda_fwd_desc_t* desc, int has_segment_ids, size_t* bytes) {
+  if (bytes == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  BwdPlan bp;
+  const kda_status_t st = bwd_validate(desc, has_segment_ids != 0, &bp);
+  if (st != KDA_OK) return st;
+  *bytes = bp.total;
+  return KDA_OK;
+}
+
+kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* initial_state, const int32_t* segment_ids,
+                           const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                           float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  const bool has_seg = segment_ids != nullptr;
+  BwdPlan bp;
+  kda_status_t st = bwd_validate(desc, has_seg, &bp);
+  if (st != KDA_OK) return st;
+  const kda_fwd_desc_t& d = *desc;
+  if (d.B * d.T > 0 && d.H > 0) {
+    const void* need[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta};
+    for (const void* ptr : need)
+      if (!ptr) return fail(KDA_ERR_INVALID_ARGUMENT, "q, k, v, g, beta, d_o and every gradient must be non-NULL");
+    const void* ptrs[] = {q, k, v, g, beta, d_o, dq, dk, dv, dg, dbeta, initial_state, segment_ids, d_final_state,
+                          d_initial_state, workspace};
+    for (const void* ptr : ptrs)
+      if (ptr && !aligned16(ptr)) return fail(KDA_ERR_INVALID_ARGUMENT, "every pointer must be 16-byte aligned");
+  }
+  if (workspace_bytes < bp.total || (bp.total > 0 && workspace == nullptr))
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL,
+                "workspace needs " + std::to_string(bp.total) + " bytes, got " + std::to_string(workspace_bytes));
+  if (d.B == 0 || d.H == 0) return KDA_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  kda::CallArgs t{};   // the segment tables, built as for the forward
+  t.B = d.B; t.T = d.T; t.H = d.H; t.K = d.K; t.V = d.V;
+  t.in = d.dtype == KDA_BF16 ? kda::InType::BF16 : kda::InType::F32;
+  t.out = kda::OutType::F32;
+  t.n_max = has_seg ? d.max_segments : 0;
+  t.nc_fixed = bp.t.nc_fixed;
+  t.cmax = bp.t.cmax;
+  t.smax = bp.t.smax;
+  t.seg_ids = segment_ids;
+  t.hdr = reinterpret_cast<kda::TableHeader*>(ws + bp.t.off_hdr);
+  t.segs = reinterpret_cast<kda::SegEntry*>(ws + bp.t.off_segs);
+  t.chunks = reinterpret_cast<kda::ChunkEntry*>(ws + bp.t.off_chunks);
+  t.stream = s;
+  const int64_t slot_elems = d.H * d.K * d.V;
+  hipError_t e = hipSuccess;
+  auto zero = [&](float* x, int64_t n) {
+    if (e == hipSuccess) e = observed("kda_bwd_zero", s, [&] { return kda::launch_fill_zero(x, n, s); });
+  };
+  if (d.T == 0) {
+    zero(d_initial_state, bp.t.smax * slot_elems);
+  } else {
+    if (has_seg) {
+      // padding tokens, unrecorded segments and absent state slots keep zero gradients
+      e = observed("kda_prep", s, [&] { return kda::launch_prep(t); });
+      const int64_t tok = d.B * d.T * d.H;
+      zero(dq, tok * d.K);
+      zero(dk, tok * d.K);
+      zero(dg, tok * d.K);
+      zero(dv, tok * d.V);
+      zero(dbeta, tok);
+      zero(d_initial_state, bp.t.smax * slot_elems);
+    }
+    kda::BwdArgs a{};
+    a.B = d.B; a.T = d.T; a.H = d.H; a.K = d.K; a.V = d.V;
+    a.in = t.in;
+    a.do_bf16 = d.o_dtype == KDA_BF16;
+    a.scale = std::isnan(d.scale) ? (float)(1.0 / std::sqrt((double)d.K)) : d.scale;
+    a.l2norm = d.use_qk_l2norm;
+    a.n_max = t.n_max;
+    a.nc_fixed = t.nc_fixed;
+    a.cmax = t.cmax;
+    a.smax = t.smax;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.d_o = d_o;
+    a.init = initial_state;
+    a.d_final = d_final_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.d_init = d_initial_state;
+    a.hdr = t.hdr; a.segs = t.segs; a.chunks = t.chunks;
+    a.rec = reinterpret_cast<float*>(ws + bp.off_rec);
+    a.hs = reinterpret_cast<float*>(ws + bp.off_hs);
+    a.dhs = reinterpret_cast<float*>(ws + bp.off_dhs);
+    a.stream = s;
+    if (e == hipSuccess) e = observed("kda_bwd", s, [&] { return kda::launch_bwd(a); });
+  }
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // extern "C"

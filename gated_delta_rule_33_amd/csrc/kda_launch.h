@@ -80,7 +80,27 @@ struct CpArgs {
   hipStream_t stream;
 };
 
+// The backward: gradients of the plain forward (g is the log decay).
+struct BwdArgs {
+  int64_t B, T, H, K, V;
+  InType in;
+  bool do_bf16;               // d_o is bf16 (else fp32)
+  float scale;
+  int l2norm;
+  int n_max;                  // segments per row with packed input (0: fixed rows)
+  int64_t nc_fixed, cmax, smax;
+  const void *q, *k, *v, *g, *beta, *d_o;
+  const float *init, *d_final;
+  float *dq, *dk, *dv, *dg, *dbeta, *d_init;
+  TableHeader* hdr;
+  SegEntry* segs;
+  ChunkEntry* chunks;
+  float *rec, *hs, *dhs;      // chunk records, states entering and gradients leaving each 16-row chunk
+  hipStream_t stream;
+};
+
 int64_t record_bytes(InType in, int64_t K, int64_t V);
+int64_t bwd_record_floats(int64_t K, int64_t V);
 
 hipError_t launch_prep(const CallArgs& a);
 hipError_t launch_intra(const CallArgs& a);
@@ -89,6 +109,7 @@ hipError_t launch_zero_states(const CallArgs& a);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
 hipError_t launch_cp_plan(const CpArgs& a);
 hipError_t launch_cp_gather(const CpArgs& a);
 hipError_t launch_cp_chain(const CpArgs& a);

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
   const int64_t T = p.T, HV = p.H * p.V;
   TO* o = static_cast<TO*>(p.o);
   if (blockIdx.x > 0) {
-    // Padding tokens: one wave per token.
+    // Padding tokens: one wave per token (nothing to do without an output).
+    if (o == nullptr) return;
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)(blockIdx.x - 1) * (kPrepThreads / 64) + (threadIdx.x >> 6);
     const int64_t n_waves = (int64_t)(gridDim.x - 1) * (kPrepThreads / 64);
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
     }
     // Outputs of unrecorded segments are zero; so are the final states of
     // slots no segment of this row reaches.
-    if (row_segs > p.n_max) {
+    if (row_segs > p.n_max && o != nullptr) {
       const SegEntry last = p.segs[seg_base + nrec - 1];
       for (int64_t t = last.t0 + last.len; t < T; ++t)
         if (row[t] != 0) zero_token(o, b * T + t, HV, tid, kPrepThreads);

@@ -22,6 +22,7 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 
 EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_transition",
+            "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
             "kda_chunk_fwd_rerun", "kda_cp_plan", "kda_cp_gather_states", "kda_cp_chain", "kda_cp_scatter_states",
             "kda_short_conv_fwd", "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer",
             "kda_last_error", "kda_version")
@@ -72,6 +73,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_transition.restype = ctypes.c_int
     lib.kda_chunk_fwd_rerun.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd_rerun.restype = ctypes.c_int
+    lib.kda_chunk_bwd_workspace_size.argtypes = [ctypes.POINTER(KdaFwdDesc), ctypes.c_int, ctypes.POINTER(sz)]
+    lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(KdaFwdDesc)] + [p] * 16 + [sz, p]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
     cpd = ctypes.POINTER(KdaCpDesc)
     lib.kda_cp_plan.argtypes = [cpd, p, p, p]
     lib.kda_cp_gather_states.argtypes = [cpd, p, p, p, p, p]
@@ -157,7 +162,8 @@ def chunk_kda(q, k, v, g, beta, scale: Optional[float] = None, initial_state=Non
     if (A_log is not None or dt_bias is not None) and not use_gate_in_kernel:
         raise ValueError("A_log and dt_bias are used only with use_gate_in_kernel=True")
     if disable_recompute:
-        raise NotImplementedError("disable_recompute concerns the backward pass, which is not implemented")
+        raise NotImplementedError("disable_recompute is not implemented: the backward (chunk_kda_bwd) always "
+                                  "recomputes the chunk quantities")
     if cp_context is not None:
         raise NotImplementedError("context parallelism across devices is not implemented; chunk_kda_cp runs "
                                   "its state chaining with the ranks' slices on one device")
@@ -345,6 +351,101 @@ def read_flags(workspace) -> int:
                                                   ctypes.c_void_p(stream), ctypes.byref(flags)),
                "kda_chunk_fwd_flags")
     return int(flags.value)
+
+
+def chunk_kda_bwd(q, k, v, g, beta, d_o, scale: Optional[float] = None, initial_state=None, d_final_state=None,
+                  use_qk_l2norm_in_kernel: bool = False, segment_ids=None, N_max: Optional[int] = None,
+                  want_d_initial_state: bool = True, workspace=None):
+    """Gradients of chunk_kda (g as the log decay) for the loss
+    sum(o * d_o) + sum(final_state * d_final_state): returns fp32
+    (dq, dk, dv, dg, dbeta, d_initial_state or None).  Inputs as for
+    chunk_kda; d_o [B,T,H,V] fp32 or bf16; d_final_state None or fp32 in the
+    state shape."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be a contiguous device tensor of q's dtype")
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if k.shape != q.shape or g.shape != q.shape or tuple(v.shape[:3]) != (B, T, H) or tuple(beta.shape) != (B, T, H):
+        raise ValueError("shape mismatch: q, k, g [B,T,H,K], v [B,T,H,V], beta [B,T,H]")
+    if tuple(d_o.shape) != (B, T, H, V) or not d_o.is_contiguous():
+        raise ValueError("d_o must be a contiguous [B,T,H,V] tensor")
+    n_max = 0
+    if segment_ids is not None:
+        if segment_ids.dtype != torch.int32 or tuple(segment_ids.shape) != (B, T) or not segment_ids.is_contiguous():
+            raise ValueError("segment_ids must be a contiguous int32 [B, T] tensor")
+        if N_max is None or N_max < 1:
+            raise ValueError("packed input (segment_ids) needs a positive N_max (max segments per row)")
+        n_max = int(N_max)
+    state_shape = (B, H, K, V) if segment_ids is None else (B, n_max, H, K, V)
+    for name, t in (("initial_state", initial_state), ("d_final_state", d_final_state)):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != state_shape or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 {state_shape} tensor")
+    desc = make_desc(B, T, H, K, V, _dtype_code(q.dtype), _dtype_code(d_o.dtype), scale, use_qk_l2norm_in_kernel,
+                     False, None, n_max)
+    lib = load_library()
+    n = ctypes.c_size_t(0)
+    _raise_for(lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc), int(segment_ids is not None), ctypes.byref(n)),
+               "kda_chunk_bwd_workspace_size")
+    if workspace is None or workspace.numel() < n.value:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dg = (torch.empty((B, T, H, K), **f32) for _ in range(3))
+    dv = torch.empty((B, T, H, V), **f32)
+    dbeta = torch.empty((B, T, H), **f32)
+    d_init = torch.empty(state_shape, **f32) if want_d_initial_state else None
+    seg_arg = segment_ids
+    if segment_ids is not None and segment_ids.numel() == 0:
+        seg_arg = torch.zeros(4, dtype=torch.int32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+                           _ptr(seg_arg), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                           _ptr(dbeta), _ptr(d_init), _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                           ctypes.c_void_p(stream))
+    _raise_for(st, "kda_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, d_init
+
+
+def _autograd_function():
+    import torch
+
+    class ChunkKDA(torch.autograd.Function):
+        """chunk_kda with its backward (kda_chunk_bwd) for torch autograd.
+        Gradients come back in fp32 and are cast to each input's dtype."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, g, beta, initial_state, scale, use_qk_l2norm_in_kernel, segment_ids, N_max):
+            o, fin = chunk_kda(q, k, v, g, beta, scale=scale, initial_state=initial_state, output_final_state=True,
+                               use_qk_l2norm_in_kernel=use_qk_l2norm_in_kernel, segment_ids=segment_ids,
+                               N_max=N_max)
+            ctx.save_for_backward(q, k, v, g, beta, initial_state, segment_ids)
+            ctx.opts = (scale, use_qk_l2norm_in_kernel, N_max)
+            return o, fin
+
+        @staticmethod
+        def backward(ctx, d_o, d_fin):
+            q, k, v, g, beta, init, seg = ctx.saved_tensors
+            scale, l2, n_max = ctx.opts
+            d_o = torch.zeros_like(q[..., :1].expand(*q.shape[:3], v.shape[-1]), dtype=torch.float32) \
+                if d_o is None else d_o.contiguous()
+            d_fin = None if d_fin is None else d_fin.contiguous().float()
+            dq, dk, dv, dg, db, dinit = chunk_kda_bwd(q, k, v, g, beta, d_o, scale=scale, initial_state=init,
+                                                      d_final_state=d_fin, use_qk_l2norm_in_kernel=l2,
+                                                      segment_ids=seg, N_max=n_max,
+                                                      want_d_initial_state=init is not None)
+            return (dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), dg.to(g.dtype), db.to(beta.dtype), dinit,
+                    None, None, None, None)
+
+    return ChunkKDA
+
+
+def chunk_kda_autograd(q, k, v, g, beta, initial_state=None, scale: Optional[float] = None,
+                       use_qk_l2norm_in_kernel: bool = False, segment_ids=None, N_max: Optional[int] = None):
+    """chunk_kda as a differentiable torch op: returns (o, final_state), and
+    backward() runs kda_chunk_bwd."""
+    return _autograd_function().apply(q, k, v, g, beta, initial_state, scale, use_qk_l2norm_in_kernel,
+                                      segment_ids, N_max)
 
 
 class CpCall:

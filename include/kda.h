@@ -127,6 +127,42 @@ kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc,
                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of kda_chunk_fwd (g taken as the log decay): the gradients of
+ *     L = sum(o * d_o) + sum(final_state * d_final_state)
+ * with respect to q, k, v, g, beta and initial_state, for the forward that
+ * desc, q, k, v, g, beta, initial_state and segment_ids describe (page
+ * "feat(kda): integrate KDA attention with tokamax backend and CP support":
+ * the Delta Rule formulation is the function differentiated; its CP
+ * gradient-equivalence test checks the backward against the unsplit one).
+ * Evaluated in fp32 in 16-token chunks (recomputing the forward's chunk
+ * quantities and states; nothing is kept from a forward call).
+ *   d_o            [B,T,H,V] of desc->o_dtype; rows of padding tokens are ignored.
+ *   d_final_state  NULL (zero) or fp32 in the initial state's shape.
+ *   dq, dk, dg     fp32 [B,T,H,K];  dv fp32 [B,T,H,V];  dbeta fp32 [B,T,H];
+ *                  every element is written (zero for padding tokens and for
+ *                  segments past max_segments).
+ *   d_initial_state NULL (not wanted) or fp32 in the initial state's shape
+ *                  (written also when initial_state is NULL: the gradient
+ *                  with respect to a zero start state); slots of absent
+ *                  segments get zero.
+ *   workspace      at least kda_chunk_bwd_workspace_size() bytes (about
+ *                  (K V / 8 + 4 K + V) * 4 bytes per token and head: the
+ *                  state and its gradient at every 16-token chunk, and the
+ *                  chunk quantities).
+ * desc->use_qk_l2norm differentiates through the in-kernel L2 norm;
+ * safe_gate and lower_bound play no part.  Errors as for kda_chunk_fwd.
+ */
+kda_status_t kda_chunk_bwd_workspace_size(const kda_fwd_desc_t* desc, int has_segment_ids, size_t* bytes);
+kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc,
+                           const void* q, const void* k, const void* v,
+                           const void* g, const void* beta,
+                           const float* initial_state, const int32_t* segment_ids,
+                           const void* d_o, const float* d_final_state,
+                           float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                           float* d_initial_state,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The forward, plus each row's transition: the recurrence is affine in the
  * state the row's first segment starts from, so the state after the row's
  * last token is  M * S_start + (that state for S_start = 0),  with M the
