@@ -199,6 +199,59 @@ def time_call(call, steps: int, warmup: int):
     return dict(step_ms=step_ms, total_ms=total_ms, wall_s=wall, kernel_ms=kern_ms)
 
 
+class _BwdCall:
+    """kda_chunk_bwd on fixed buffers (one enqueue = one backward)."""
+
+    def __init__(self, w):
+        import torch
+        from gated_delta_rule_33_amd import kda
+        inp = make_inputs(w)
+        d = to_device(inp, w.dtype)
+        g = torch.Generator(device="cuda").manual_seed(w.seed + 11)
+        self.d_o = torch.randn(w.B, w.T, w.H, w.V, device="cuda", generator=g)
+        shape = (w.B, w.H, w.K, w.V) if d["segment_ids"] is None else (w.B, inp["max_segments"], w.H, w.K, w.V)
+        self.d_fin = torch.randn(*shape, device="cuda", generator=g) if w.final_state else None
+        self.kw = dict(scale=inp["scale"], initial_state=d["initial_state"], d_final_state=self.d_fin,
+                       use_qk_l2norm_in_kernel=w.l2norm_in_kernel, segment_ids=d["segment_ids"],
+                       N_max=inp["max_segments"] if d["segment_ids"] is not None else None)
+        self.args = (d["q"], d["k"], d["v"], d["g"], d["beta"], self.d_o)
+        self.kda = kda
+        self.out = kda.chunk_kda_bwd(*self.args, **self.kw)
+        torch.cuda.synchronize()
+        self.workspace_bytes = None
+
+    def enqueue(self):
+        self.out = self.kda.chunk_kda_bwd(*self.args, **self.kw, workspace=self._ws())
+
+    def _ws(self):
+        import torch
+        if getattr(self, "ws", None) is None:
+            from gated_delta_rule_33_amd.kda import load_library, make_desc, _dtype_code
+            import ctypes
+            q, v = self.args[0], self.args[2]
+            B, T, H, K = q.shape
+            seg = self.kw["segment_ids"]
+            desc = make_desc(B, T, H, K, v.shape[-1], _dtype_code(q.dtype), _dtype_code(self.d_o.dtype),
+                             self.kw["scale"], self.kw["use_qk_l2norm_in_kernel"], False, None,
+                             self.kw["N_max"] or 0)
+            n = ctypes.c_size_t(0)
+            load_library().kda_chunk_bwd_workspace_size(ctypes.byref(desc), int(seg is not None), ctypes.byref(n))
+            self.workspace_bytes = int(n.value)
+            self.ws = torch.empty(max(self.workspace_bytes, 1), dtype=torch.uint8, device="cuda")
+        return self.ws
+
+
+def time_bwd(w, steps: int, warmup: int):
+    """The backward (kda_chunk_bwd) at the workload's shape with random
+    cotangents: time per call and per kernel."""
+    call = _BwdCall(w)
+    res = time_call(call, steps, warmup)
+    ms = res["total_ms"] / steps
+    kern = {n: round(float(np.mean(v)) * 1e3, 2) for n, v in res["kernel_ms"].items()}
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.B * w.T / (ms * 1e-3), 1),
+            "kernel_avg_us": kern, "workspace_bytes": call.workspace_bytes}
+
+
 def time_cp(w, steps: int, warmup: int, P: int):
     """The workload cut into P context-parallel slices on this one GPU (plan,
     forward with transitions, chain, rerun of the recurrence, state routing):
@@ -310,6 +363,8 @@ def main():
                     help="skip the timing of the short convolution and the gated RMSNorm")
     ap.add_argument("--no-gate-in-kernel", dest="gate_in_kernel", action="store_false",
                     help="skip the timing of the same workload with the gate activated in the kernel")
+    ap.add_argument("--no-bwd", dest="bwd", action="store_false",
+                    help="skip the timing of the backward (kda_chunk_bwd)")
     ap.add_argument("--no-cp", dest="cp", action="store_false",
                     help="skip the timing of the workload cut into 2 and 4 context-parallel slices")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -376,6 +431,12 @@ def main():
                                    "note": "raw N(0,1) gate, A_log = 0, dt_bias = 0, safe gate at -5: "
                                            "the same decay distribution, activated in the kernel"}
         del res3
+    if args.bwd:
+        for wb in (w, WORKLOADS[args.extra] if args.extra else None):
+            if wb is None:
+                continue
+            log(f"[bench] backward of {wb.name}")
+            extra.setdefault("backward", {})[wb.name] = time_bwd(wb, args.steps, args.warmup)
     if args.cp:
         for P in (2, 4):
             log(f"[bench] {w.name} cut into {P} context-parallel slices")

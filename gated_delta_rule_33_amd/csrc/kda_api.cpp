@@ -526,7 +526,9 @@ kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void
     a.hs = reinterpret_cast<float*>(ws + bp.off_hs);
     a.dhs = reinterpret_cast<float*>(ws + bp.off_dhs);
     a.stream = s;
-    if (e == hipSuccess) e = observed("kda_bwd", s, [&] { return kda::launch_bwd(a); });
+    static const char* const names[4] = {"kda_bwd_chunk", "kda_bwd_states", "kda_bwd_dstates", "kda_bwd_local"};
+    for (int stage = 0; stage < 4 && e == hipSuccess; ++stage)
+      e = observed(names[stage], s, [&] { return kda::launch_bwd(a, stage); });
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return KDA_OK;

@@ -431,30 +431,57 @@ __global__ __launch_bounds__(kBThreads) void bwd_dstates_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- bwd_local
-// One workgroup per (chunk, head): every input gradient of the chunk's rows.
-// Thread t owns row r = t / 16 and key channels c = t % 16 + 16 m.
+// fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32).  A 16-deep slab of a
+// product C (16x16) += A (16x16) B (16x16) is four instructions: for the j-th,
+// lane l = 16 g + n supplies A[n][4g + j] and B[4g + j][n], so one f32x4 per
+// operand and lane covers the slab.  The accumulator lane l holds C[4g + i][n]
+// (i = 0..3), which is also the B operand of a 16-deep slab over its rows.
+__device__ __forceinline__ void mma16(f32x4& c, const f32x4& a, const f32x4& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+}
+// A operand of a row-major X (rows m0.., k = k0 + 4g + j); also the B operand
+// of X^T (cols m0..).
+__device__ __forceinline__ f32x4 opa(const float* X, int ld, int m0, int k0, int lane) {
+  return *reinterpret_cast<const f32x4*>(X + (int64_t)(m0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+}
+// B operand of a row-major Y (k = k0 + 4g + j, cols n0..); also the A operand
+// of Y^T (rows n0..).
+__device__ __forceinline__ f32x4 opb(const float* Y, int ld, int k0, int n0, int lane) {
+  const float* q = Y + (int64_t)(k0 + 4 * (lane >> 4)) * ld + n0 + (lane & 15);
+  return f32x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
+}
+
+// One workgroup (four waves) per (chunk, head): every input gradient of the
+// chunk's rows.  Phase A (contraction over K; wave w takes value blocks w,
+// w + 4, ...): Delta = U - W h, dDelta = scale Aqk^T dO + Kt dh, and
+// d Gamma_C = rowsum(dh * h).  Phase B (contraction over V; wave w takes key
+// blocks w, w + 4, ...): dQg = scale dO h^T, dKt = Delta dh^T,
+// dW = -dDelta h^T; besides, wave 0 dAqk = scale dO Delta^T, wave 1
+// dT = dDelta Vb^T, waves 2-3 dVb = T^T dDelta (dv, and dbeta's V part).
+// Phase C: dT += dW Kb^T, dA = -T^T dT T^T.  Phase D (key blocks again): dKb =
+// T^T dW and the exponent-factor sums of A and Aqk, assembled per (row,
+// channel) into dq, dk, dbeta and dG; dg = reverse in-chunk cumsum of dG.
 template <class TI, class TO, int K, int V>
 __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   using R = BRec<K, V>;
-  constexpr int VT = 32;           // value columns per pass over the states
-  constexpr int MC = K / kBC;      // key channels per thread
+  constexpr int NKB = K / 16, NVB = V / 16, MX = K > V ? K : V;
   const int64_t slot = blockIdx.x / p.H, h = blockIdx.x % p.H;
   BSlot si;
   if (!slot_info(p, slot, &si)) return;
   const float* rec = p.rec + (slot * p.H + h) * R::kFloats;
   const float* hS = p.hs + (slot * p.H + h) * K * V;
   const float* dhS = p.dhs + (slot * p.H + h) * K * V;
-  __shared__ float sG[kBC][K], sKt[kBC][K], sQg[kBC][K], sW[kBC][K], sKb[kBC][K];
-  __shared__ float sk[kBC][K], sq[kBC][K], skf[kBC][K], skb[kBC][K], sqf[kBC][K];
-  __shared__ float sU[kBC][V], sv[kBC][V], sdO[kBC][V];
-  __shared__ float sHH[2 * K * VT];   // h and dh tiles; afterwards dW, dKt, dQg and dG
-  __shared__ float sD[kBC][VT], sdD[kBC][VT];
-  __shared__ float sAqk[kBC][kBC + 1], sT[kBC][kBC + 1], sX[kBC][kBC + 1], sdA[kBC][kBC + 1];
-  __shared__ float sdAqk[kBC][kBC + 1], sdT[kBC][kBC + 1], sGc[K], sdgc[K], sbeta[kBC];
-  static_assert(4 * kBC * K <= 2 * K * VT, "dW, dKt, dQg and dG must fit the state tiles");
-  float (*sh)[VT] = reinterpret_cast<float (*)[VT]>(sHH);
-  float (*sdh)[VT] = reinterpret_cast<float (*)[VT]>(sHH + K * VT);
-  const int tid = threadIdx.x, r = tid / kBC, cc = tid % kBC;
+  __shared__ __align__(16) float sG[kBC][K], sk[kBC][K], sq[kBC][K];
+  __shared__ __align__(16) float sVG[kBC * MX];        // v [16][V], later dG [16][K]
+  __shared__ __align__(16) float sBig[3 * kBC * MX];   // dO, Delta, dDelta [16][V]; later dW, dKt, dQg [16][K]
+  __shared__ __align__(16) float sT[kBC][kBC], sAqk[kBC][kBC], sdA[kBC][kBC], sdAqk[kBC][kBC], sdT[kBC][kBC];
+  __shared__ __align__(16) float sX[kBC][kBC];
+  // Per-wave partial sums (one writer each), combined in wave order: no
+  // atomics, so every run adds in the same order.
+  __shared__ float sdgcp[4][K], sred[4][kBC][4], sdTp[4][kBC][kBC];
+  __shared__ float sbeta[kBC], snq[kBC], snk[kBC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = 4 * (lane >> 4), n = lane & 15;
   const TI* q = static_cast<const TI*>(p.q);
   const TI* k = static_cast<const TI*>(p.k);
   const TI* v = static_cast<const TI*>(p.v);
@@ -463,34 +490,33 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   const bool unsafe = rec[R::kInfo] != 0.f;
   const int len = si.len, last = len - 1;
   auto tok = [&](int row) { return (si.b * p.T + si.t0 + row) * p.H + h; };
+  float* sv = sVG;
+  float* sdO = sBig;
+  float* sD = sBig + kBC * V;
+  float* sdD = sBig + 2 * kBC * V;
 
-  // ---- the record and the inputs
+  // ---- inputs
   for (int e = tid; e < kBC * K; e += kBThreads) {
-    const int rr = e / K, c = e % K;
-    sG[rr][c] = rec[R::kG + e];
-    sKt[rr][c] = rec[R::kKt + e];
-    sQg[rr][c] = rec[R::kQg + e];
-    sW[rr][c] = rec[R::kW + e];
-    sk[rr][c] = rr < len ? ld(k, tok(rr) * K + c) : 0.f;
-    sq[rr][c] = rr < len ? ld(q, tok(rr) * K + c) : 0.f;
+    const int r = e / K, c = e % K;
+    sG[r][c] = rec[R::kG + e];
+    sk[r][c] = r < len ? ld(k, tok(r) * K + c) : 0.f;
+    sq[r][c] = r < len ? ld(q, tok(r) * K + c) : 0.f;
   }
   for (int e = tid; e < kBC * V; e += kBThreads) {
-    const int rr = e / V, j = e % V;
-    sU[rr][j] = rec[R::kU + e];
-    sv[rr][j] = rr < len ? ld(v, tok(rr) * V + j) : 0.f;
-    sdO[rr][j] = rr < len ? ld(d_o, tok(rr) * V + j) : 0.f;
+    const int r = e / V, j = e % V;
+    sv[e] = r < len ? ld(v, tok(r) * V + j) : 0.f;
+    sdO[e] = r < len ? ld(d_o, tok(r) * V + j) : 0.f;
   }
-  sAqk[r][cc] = rec[R::kAqk + tid];
-  sT[r][cc] = rec[R::kT + tid];
-  for (int c = tid; c < K; c += kBThreads) {
-    sGc[c] = rec[R::kGc + c];
-    sdgc[c] = 0.f;
-  }
+  sT[tid / kBC][tid % kBC] = rec[R::kT + tid];
+  sAqk[tid / kBC][tid % kBC] = rec[R::kAqk + tid];
+  for (int e = tid; e < 4 * K; e += kBThreads) (&sdgcp[0][0])[e] = 0.f;
+  for (int e = tid; e < 4 * kBC * 4; e += kBThreads) (&sred[0][0][0])[e] = 0.f;
+  for (int e = tid; e < 4 * kBC * kBC; e += kBThreads) (&sdTp[0][0][0])[e] = 0.f;
   if (tid < kBC) sbeta[tid] = tid < len ? ld(beta, tok(tid)) : 0.f;
   __syncthreads();
-  // the L2 norm of q and k, 16 lanes per row (norms kept for the chain rule)
-  float nq = 1.f, nk = 1.f;
   {
+    // the L2 norm of q and k, 16 lanes per row
+    const int r = tid / kBC, cc = tid % kBC;
     float sqq = 0.f, skk = 0.f;
     for (int c = cc; c < K; c += kBC) {
       sqq += sq[r][c] * sq[r][c];
@@ -498,201 +524,253 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
     }
     sqq = sum16(sqq);
     skk = sum16(skk);
-    if (p.l2norm) {
-      nq = sqrtf(sqq + 1e-6f);
-      nk = sqrtf(skk + 1e-6f);
-    }
+    const float nq = p.l2norm ? sqrtf(sqq + 1e-6f) : 1.f, nk = p.l2norm ? sqrtf(skk + 1e-6f) : 1.f;
     for (int c = cc; c < K; c += kBC) {
       sq[r][c] /= nq;
       sk[r][c] /= nk;
     }
+    if (cc == 0) {
+      snq[r] = nq;
+      snk[r] = nk;
+    }
   }
   __syncthreads();
-  for (int e = tid; e < kBC * K; e += kBThreads) {
-    const int rr = e / K, c = e % K;
-    const float G = sG[rr][c], G0 = sG[0][c];
-    skf[rr][c] = sk[rr][c] * __expf(G - G0);
-    skb[rr][c] = unsafe ? 0.f : sk[rr][c] * __expf(G0 - G);
-    sqf[rr][c] = sq[rr][c] * __expf(G - G0);
-    sKb[rr][c] = sbeta[rr] * sk[rr][c] * __expf(G);
-  }
 
-  // ---- passes over the value columns: Delta = U - W h, dDelta = scale Aqk^T dO
-  // + Kt dh, and every product that contracts over V
-  float aQg[MC] = {}, aKt[MC] = {}, aW[MC] = {};
-  float aAqk = 0.f, aT = 0.f, dbv = 0.f;
-  for (int j0 = 0; j0 < V; j0 += VT) {
-    __syncthreads();
-    for (int e = tid; e < K * VT; e += kBThreads) {
-      const int c = e / VT, j = e % VT;
-      sh[c][j] = hS[c * V + j0 + j];
-      sdh[c][j] = dhS[c * V + j0 + j];
-    }
-    __syncthreads();
-    for (int e = tid; e < kBC * VT; e += kBThreads) {
-      const int rr = e / VT, j = e % VT;
-      float d = sU[rr][j0 + j], dd = 0.f;
-      for (int c = 0; c < K; ++c) d -= sW[rr][c] * sh[c][j];
-      for (int i = 0; i < kBC; ++i) dd += sAqk[i][rr] * sdO[i][j0 + j];
-      dd *= p.scale;
-      for (int c = 0; c < K; ++c) dd += sKt[rr][c] * sdh[c][j];
-      sD[rr][j] = d;
-      sdD[rr][j] = dd;
-    }
-    __syncthreads();
+  // ---- phase A: Delta, dDelta, d Gamma_C
+  for (int vb = wave; vb < NVB; vb += 4) {
+    f32x4 cD = {0, 0, 0, 0}, cDD = {0, 0, 0, 0};
+#pragma unroll 2
+    for (int s = 0; s < NKB; ++s) {
+      const f32x4 bh = opb(hS, V, 16 * s, 16 * vb, lane), bdh = opb(dhS, V, 16 * s, 16 * vb, lane);
+      mma16(cD, opa(rec + R::kW, K, 0, 16 * s, lane), bh);
+      mma16(cDD, opa(rec + R::kKt, K, 0, 16 * s, lane), bdh);
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      const int c = cc + kBC * m;
-      float x = 0.f, y = 0.f, z = 0.f;
-      for (int j = 0; j < VT; ++j) {
-        x += sdO[r][j0 + j] * sh[c][j];
-        y += sD[r][j] * sdh[c][j];
-        z += sdD[r][j] * sh[c][j];
+      for (int j = 0; j < 4; ++j) {
+        const float x = sum16(bh[j] * bdh[j]);
+        if (n == 0) sdgcp[wave][16 * s + g4 + j] += x;
       }
-      aQg[m] += p.scale * x;   // dQg = scale dO h^T
-      aKt[m] += y;             // dKt = Delta dh^T
-      aW[m] -= z;              // dW = -dDelta h^T
     }
-    {
-      float x = 0.f, y = 0.f;
-      for (int j = 0; j < VT; ++j) {
-        x += sdO[r][j0 + j] * sD[cc][j];
-        y += sdD[r][j] * sbeta[cc] * sv[cc][j0 + j];
-      }
-      aAqk += p.scale * x;     // dAqk = scale dO Delta^T
-      aT += y;                 // dT  = dDelta Vb^T (+ dW Kb^T below)
-    }
-    // dVb = T^T dDelta: dv = beta dVb, and dbeta gets v . dVb
-    for (int jj = cc; jj < VT; jj += kBC) {
-      float x = 0.f;
-      for (int rr = r; rr < kBC; ++rr) x += sT[rr][r] * sdD[rr][jj];
-      if (r < len) p.dv[tok(r) * V + j0 + jj] = sbeta[r] * x;
-      dbv += sv[r][j0 + jj] * x;
-    }
-    for (int c = tid; c < K; c += kBThreads) {
-      float x = 0.f;
-      for (int j = 0; j < VT; ++j) x += sdh[c][j] * sh[c][j];
-      sdgc[c] += x;            // d Gamma_C = rowsum(dh * h)
-    }
-  }
-  __syncthreads();
-  float* dWl = sHH;                 // [16][K]
-  float* dKtl = sHH + kBC * K;
-  float* dQgl = sHH + 2 * kBC * K;
-  float* dGl = sHH + 3 * kBC * K;
+    f32x4 cq = {0, 0, 0, 0};
+    mma16(cq, opb(&sAqk[0][0], kBC, 0, 0, lane), opb(sdO, V, 0, 16 * vb, lane));
 #pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    const int c = cc + kBC * m;
-    dWl[r * K + c] = aW[m];
-    dKtl[r * K + c] = aKt[m];
-    dQgl[r * K + c] = aQg[m];
+    for (int i = 0; i < 4; ++i) {
+      const int r = g4 + i, j = 16 * vb + n;
+      sD[r * V + j] = rec[R::kU + r * V + j] - cD[i];
+      sdD[r * V + j] = cDD[i] + p.scale * cq[i];
+    }
+  }
+  __syncthreads();
+
+  // ---- phase B: products over V
+  f32x4 cQ[2], cKt[2], cW[2];
+  for (int u = 0; u < 2; ++u) {
+    const int cb = wave + 4 * u;
+    cQ[u] = cKt[u] = cW[u] = f32x4{0, 0, 0, 0};
+    if (cb >= NKB) continue;
+#pragma unroll 2
+    for (int s = 0; s < NVB; ++s) {
+      const f32x4 bh = opa(hS, V, 16 * cb, 16 * s, lane), bdh = opa(dhS, V, 16 * cb, 16 * s, lane);
+      mma16(cQ[u], opa(sdO, V, 0, 16 * s, lane), bh);
+      mma16(cKt[u], opa(sD, V, 0, 16 * s, lane), bdh);
+      mma16(cW[u], opa(sdD, V, 0, 16 * s, lane), bh);
+    }
+  }
+  if (wave == 0) {
+    f32x4 c = {0, 0, 0, 0};
+    for (int s = 0; s < NVB; ++s) mma16(c, opa(sdO, V, 0, 16 * s, lane), opa(sD, V, 0, 16 * s, lane));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sdAqk[g4 + i][n] = g4 + i >= n ? p.scale * c[i] : 0.f;
+  } else if (wave == 1) {
+    f32x4 c = {0, 0, 0, 0};
+    for (int s = 0; s < NVB; ++s) {
+      f32x4 b = opa(sv, V, 0, 16 * s, lane);
+      const float bn = sbeta[n];
+      b = f32x4{b[0] * bn, b[1] * bn, b[2] * bn, b[3] * bn};
+      mma16(c, opa(sdD, V, 0, 16 * s, lane), b);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sdT[g4 + i][n] = c[i];
+  } else {
+    for (int vb = wave - 2; vb < NVB; vb += 2) {
+      f32x4 c = {0, 0, 0, 0};
+      mma16(c, opb(&sT[0][0], kBC, 0, 0, lane), opb(sdD, V, 0, 16 * vb, lane));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = g4 + i, j = 16 * vb + n;
+        if (r < len) p.dv[tok(r) * V + j] = sbeta[r] * c[i];
+        const float x = sum16(sv[r * V + j] * c[i]);
+        if (n == 0) sred[wave][r][3] += x;
+      }
+    }
+  }
+  __syncthreads();
+  float* sdW = sBig;
+  float* sdKt = sBig + kBC * K;
+  float* sdQg = sBig + 2 * kBC * K;
+  for (int u = 0; u < 2; ++u) {
+    const int cb = wave + 4 * u;
+    if (cb >= NKB) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = (g4 + i) * K + 16 * cb + n;
+      sdW[idx] = -cW[u][i];
+      sdKt[idx] = cKt[u][i];
+      sdQg[idx] = p.scale * cQ[u][i];
+    }
+  }
+  __syncthreads();
+
+  // ---- phase C: dT += dW Kb^T (as dT^T = Kb dW^T, summed over the waves' key blocks), dA
+  {
+    f32x4 c = {0, 0, 0, 0};
+    for (int u = 0; u < 2; ++u) {
+      const int cb = wave + 4 * u;
+      if (cb >= NKB) continue;
+      const int i = n, c0 = 16 * cb + g4;
+      f32x4 a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) a[j] = sbeta[i] * sk[i][c0 + j] * __expf(sG[i][c0 + j]);
+      mma16(c, a, opa(sdW, K, 0, 16 * cb, lane));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sdTp[wave][n][g4 + i] = c[i];
   }
   __syncthreads();
   {
-    float x = 0.f;
-    for (int c = 0; c < K; ++c) x += dWl[r * K + c] * sKb[cc][c];
-    sdT[r][cc] = aT + x;
-    sdAqk[r][cc] = r >= cc ? aAqk : 0.f;
+    const int r = tid / kBC, cc = tid % kBC;
+    sX[r][cc] = sdT[r][cc] + sdTp[0][r][cc] + sdTp[1][r][cc] + sdTp[2][r][cc] + sdTp[3][r][cc];
   }
   __syncthreads();
   {
-    // X = T^T dT
+    const int r = tid / kBC, cc = tid % kBC;
     float x = 0.f;
-    for (int a = r; a < kBC; ++a) x += sT[a][r] * sdT[a][cc];
-    sX[r][cc] = x;
+    for (int a = r; a < kBC; ++a) x += sT[a][r] * sX[a][cc];
+    sdT[r][cc] = x;   // now X = T^T dT
   }
   __syncthreads();
   {
-    // dA = -(T^T dT T^T), strictly lower
+    const int r = tid / kBC, cc = tid % kBC;
     float x = 0.f;
-    for (int b = 0; b <= cc; ++b) x += sX[r][b] * sT[cc][b];
+    for (int b = 0; b <= cc; ++b) x += sdT[r][b] * sT[cc][b];
     sdA[r][cc] = cc < r ? -x : 0.f;
   }
   __syncthreads();
 
-  // ---- per (row, channel): the terms of A and Aqk back onto q, k and G
-  const float br = sbeta[r];
-  float dqh[MC], dkh[MC], dbeta_p = 0.f;
-#pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    const int c = cc + kBC * m;
-    const float G = sG[r][c], GC = sG[last][c];
-    float RA = 0.f, RAq = 0.f, CA = 0.f, CAq = 0.f;
+  // ---- phase D: per key block, the terms of A and Aqk back onto q, k and G
+  float* sdG = sVG;
+  float dqh[2][4], dkh[2][4];
+  float pq[4] = {0, 0, 0, 0}, pk[4] = {0, 0, 0, 0}, pb[4] = {0, 0, 0, 0};
+  for (int u = 0; u < 2; ++u) {
+    const int cb = wave + 4 * u;
+    if (cb >= NKB) continue;
+    const int c = 16 * cb + n;                  // this lane's channel in the C layout
+    f32x4 cKb = {0, 0, 0, 0}, RA = {0, 0, 0, 0}, RAq = {0, 0, 0, 0}, CA = {0, 0, 0, 0}, CAq = {0, 0, 0, 0};
+    mma16(cKb, opb(&sT[0][0], kBC, 0, 0, lane), opb(sdW, K, 0, 16 * cb, lane));
     if (!unsafe) {
-      for (int i = 0; i < kBC; ++i) {
-        RA += sdA[r][i] * skb[i][c];
-        RAq += sdAqk[r][i] * skb[i][c];
-        CA += sdA[i][r] * sbeta[i] * skf[i][c];
-        CAq += sdAqk[i][r] * sqf[i][c];
+      // B operands kb[4g+j][c] = k exp(G0 - G), beta kf = beta k exp(G - G0), qf = q exp(G - G0)
+      f32x4 kb, bkf, qf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = g4 + j;
+        const float d = sG[r][c] - sG[0][c];
+        kb[j] = sk[r][c] * __expf(-d);
+        bkf[j] = sbeta[r] * sk[r][c] * __expf(d);
+        qf[j] = sq[r][c] * __expf(d);
       }
-      const float fr = __expf(G - sG[0][c]), bk = __expf(sG[0][c] - G);
-      RA *= fr;
-      RAq *= fr;
-      CA *= bk;
-      CAq *= bk;
+      mma16(RA, opa(&sdA[0][0], kBC, 0, 0, lane), kb);
+      mma16(RAq, opa(&sdAqk[0][0], kBC, 0, 0, lane), kb);
+      mma16(CA, opb(&sdA[0][0], kBC, 0, 0, lane), bkf);
+      mma16(CAq, opb(&sdAqk[0][0], kBC, 0, 0, lane), qf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float d = sG[g4 + i][c] - sG[0][c];
+        const float fr = __expf(d), bk = __expf(-d);
+        RA[i] *= fr;
+        RAq[i] *= fr;
+        CA[i] *= bk;
+        CAq[i] *= bk;
+      }
     } else {
-      for (int i = 0; i < kBC; ++i) {
-        const float e = __expf(G - sG[i][c]), ei = __expf(sG[i][c] - G);
-        if (i <= r) {
-          RA += sdA[r][i] * sk[i][c] * e;
-          RAq += sdAqk[r][i] * sk[i][c] * e;
-        }
-        if (i >= r) {
-          CA += sdA[i][r] * sbeta[i] * sk[i][c] * ei;
-          CAq += sdAqk[i][r] * sq[i][c] * ei;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = g4 + i;
+        for (int x = 0; x < kBC; ++x) {
+          const float e = __expf(sG[r][c] - sG[x][c]), ei = __expf(sG[x][c] - sG[r][c]);
+          if (x <= r) {
+            RA[i] += sdA[r][x] * sk[x][c] * e;
+            RAq[i] += sdAqk[r][x] * sk[x][c] * e;
+          }
+          if (x >= r) {
+            CA[i] += sdA[x][r] * sbeta[x] * sk[x][c] * ei;
+            CAq[i] += sdAqk[x][r] * sq[x][c] * ei;
+          }
         }
       }
     }
-    float dKb = 0.f;
-    for (int i = r; i < kBC; ++i) dKb += sT[i][r] * dWl[i * K + c];
-    const float e = __expf(G), ec = __expf(GC - G), kh = sk[r][c], qh = sq[r][c];
-    const float dQg = dQgl[r * K + c], dKt = dKtl[r * K + c];
-    dqh[m] = dQg * e + RAq;
-    dkh[m] = dKb * br * e + dKt * ec + br * RA + CA + CAq;
-    dbeta_p += kh * e * dKb + kh * RA;
-    float dG = dQg * qh * e + dKb * br * kh * e - dKt * kh * ec + br * kh * RA - kh * CA + qh * RAq - kh * CAq;
-    if (r == last) {
-      float x = 0.f;
-      for (int i = 0; i < kBC; ++i) x += dKtl[i * K + c] * sKt[i][c];
-      dG += x + sdgc[c] * sGc[c];
+    const float GC = sG[last][c];
+    float lastx = 0.f;
+    if (last >= g4 && last < g4 + 4) {
+      for (int x = 0; x < kBC; ++x) lastx += sdKt[x * K + c] * rec[R::kKt + x * K + c];
+      lastx += (sdgcp[0][c] + sdgcp[1][c] + sdgcp[2][c] + sdgcp[3][c]) * __expf(GC);
     }
-    dGl[r * K + c] = r < len ? dG : 0.f;
-  }
-  // dbeta: the V part and the K part, summed over the row's 16 lanes
-  const float db = sum16(dbv + dbeta_p);
-  if (cc == 0 && r < len) p.dbeta[tok(r)] = db;
-  // dq, dk through the L2 norm: dx = (dx^ - x^ (x^ . dx^)) / n
-  float pq = 0.f, pk = 0.f;
 #pragma unroll
-  for (int m = 0; m < MC; ++m) {
-    pq += sq[r][cc + kBC * m] * dqh[m];
-    pk += sk[r][cc + kBC * m] * dkh[m];
+    for (int i = 0; i < 4; ++i) {
+      const int r = g4 + i;
+      const float G = sG[r][c], e = __expf(G), ec = __expf(GC - G), kh = sk[r][c], qh = sq[r][c], br = sbeta[r];
+      const float dQg = sdQg[r * K + c], dKt = sdKt[r * K + c], dKb = cKb[i];
+      dqh[u][i] = dQg * e + RAq[i];
+      dkh[u][i] = dKb * br * e + dKt * ec + br * RA[i] + CA[i] + CAq[i];
+      pb[i] += kh * e * dKb + kh * RA[i];
+      float dG = dQg * qh * e + dKb * br * kh * e - dKt * kh * ec + br * kh * RA[i] - kh * CA[i] + qh * RAq[i] -
+                 kh * CAq[i];
+      if (r == last) dG += lastx;
+      sdG[r * K + c] = r < len ? dG : 0.f;
+      pq[i] += qh * dqh[u][i];
+      pk[i] += kh * dkh[u][i];
+    }
   }
-  pq = sum16(pq);
-  pk = sum16(pk);
-  if (r < len) {
 #pragma unroll
-    for (int m = 0; m < MC; ++m) {
-      const int c = cc + kBC * m;
-      const float dq = p.l2norm ? (dqh[m] - sq[r][c] * pq) / nq : dqh[m];
-      const float dk = p.l2norm ? (dkh[m] - sk[r][c] * pk) / nk : dkh[m];
+  for (int i = 0; i < 4; ++i) {
+    const float a = sum16(pq[i]), b = sum16(pk[i]), c = sum16(pb[i]);
+    if (n == 0) {
+      sred[wave][g4 + i][0] = a;
+      sred[wave][g4 + i][1] = b;
+      sred[wave][g4 + i][2] = c;
+    }
+  }
+  __syncthreads();
+  for (int u = 0; u < 2; ++u) {
+    const int cb = wave + 4 * u;
+    if (cb >= NKB) continue;
+    const int c = 16 * cb + n;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = g4 + i;
+      if (r >= len) continue;
+      const float pqr = sred[0][r][0] + sred[1][r][0] + sred[2][r][0] + sred[3][r][0];
+      const float pkr = sred[0][r][1] + sred[1][r][1] + sred[2][r][1] + sred[3][r][1];
+      const float dq = p.l2norm ? (dqh[u][i] - sq[r][c] * pqr) / snq[r] : dqh[u][i];
+      const float dk = p.l2norm ? (dkh[u][i] - sk[r][c] * pkr) / snk[r] : dkh[u][i];
       p.dq[tok(r) * K + c] = dq;
       p.dk[tok(r) * K + c] = dk;
     }
   }
-  __syncthreads();
-  // dg = reverse in-chunk cumsum of dG
+  if (tid < len) {
+    float x = 0.f;
+    for (int w = 0; w < 4; ++w) x += sred[w][tid][2] + sred[w][tid][3];
+    p.dbeta[tok(tid)] = x;
+  }
   for (int c = tid; c < K; c += kBThreads) {
     float run = 0.f;
-    for (int rr = last; rr >= 0; --rr) {
-      run += dGl[rr * K + c];
-      p.dg[tok(rr) * K + c] = run;
+    for (int r = last; r >= 0; --r) {
+      run += sdG[r * K + c];
+      p.dg[tok(r) * K + c] = run;
     }
   }
 }
 
 template <class TI, class TO, int K, int V>
-hipError_t launch_bwd_t(const BwdArgs& a) {
+hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   BwdParams p{};
   p.B = a.B; p.T = a.T; p.H = a.H;
   p.nc64 = a.nc_fixed;
@@ -707,20 +785,23 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
   p.rec = a.rec; p.hs = a.hs; p.dhs = a.dhs;
   const int64_t slots = 4 * a.cmax;
   const dim3 blk(kBThreads);
-  hipLaunchKernelGGL((bwd_chunk_kernel<TI, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p);
   const int64_t seqs = (p.packed ? a.smax : a.B) * a.H * (V / kBC);
-  hipLaunchKernelGGL((bwd_states_kernel<K, V>), dim3((unsigned)seqs), blk, 0, a.stream, p);
-  hipLaunchKernelGGL((bwd_dstates_kernel<TO, K, V>), dim3((unsigned)seqs), blk, 0, a.stream, p);
-  hipLaunchKernelGGL((bwd_local_kernel<TI, TO, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p);
+  switch (stage) {
+    case 0: hipLaunchKernelGGL((bwd_chunk_kernel<TI, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p); break;
+    case 1: hipLaunchKernelGGL((bwd_states_kernel<K, V>), dim3((unsigned)seqs), blk, 0, a.stream, p); break;
+    case 2: hipLaunchKernelGGL((bwd_dstates_kernel<TO, K, V>), dim3((unsigned)seqs), blk, 0, a.stream, p); break;
+    case 3: hipLaunchKernelGGL((bwd_local_kernel<TI, TO, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <class TI, class TO>
-hipError_t launch_bwd_kv(const BwdArgs& a) {
-  if (a.K == 64 && a.V == 64) return launch_bwd_t<TI, TO, 64, 64>(a);
-  if (a.K == 64 && a.V == 128) return launch_bwd_t<TI, TO, 64, 128>(a);
-  if (a.K == 128 && a.V == 64) return launch_bwd_t<TI, TO, 128, 64>(a);
-  if (a.K == 128 && a.V == 128) return launch_bwd_t<TI, TO, 128, 128>(a);
+hipError_t launch_bwd_kv(const BwdArgs& a, int stage) {
+  if (a.K == 64 && a.V == 64) return launch_bwd_t<TI, TO, 64, 64>(a, stage);
+  if (a.K == 64 && a.V == 128) return launch_bwd_t<TI, TO, 64, 128>(a, stage);
+  if (a.K == 128 && a.V == 64) return launch_bwd_t<TI, TO, 128, 64>(a, stage);
+  if (a.K == 128 && a.V == 128) return launch_bwd_t<TI, TO, 128, 128>(a, stage);
   return hipErrorInvalidValue;
 }
 
@@ -733,10 +814,10 @@ int64_t bwd_record_floats(int64_t K, int64_t V) {
   return BRec<128, 128>::kFloats;
 }
 
-hipError_t launch_bwd(const BwdArgs& a) {
+hipError_t launch_bwd(const BwdArgs& a, int stage) {
   if (a.in == InType::BF16)
-    return a.do_bf16 ? launch_bwd_kv<uint16_t, uint16_t>(a) : launch_bwd_kv<uint16_t, float>(a);
-  return a.do_bf16 ? launch_bwd_kv<float, uint16_t>(a) : launch_bwd_kv<float, float>(a);
+    return a.do_bf16 ? launch_bwd_kv<uint16_t, uint16_t>(a, stage) : launch_bwd_kv<uint16_t, float>(a, stage);
+  return a.do_bf16 ? launch_bwd_kv<float, uint16_t>(a, stage) : launch_bwd_kv<float, float>(a, stage);
 }
 
 }  // namespace kda

@@ -109,7 +109,9 @@ hipError_t launch_zero_states(const CallArgs& a);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);
 hipError_t launch_short_conv(const ConvArgs& a);
 hipError_t launch_gated_rmsnorm(const NormArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// stage 0: chunk quantities, 1: forward states, 2: reverse state recurrence,
+// 3: per-chunk input gradients (launched in that order).
+hipError_t launch_bwd(const BwdArgs& a, int stage);
 hipError_t launch_cp_plan(const CpArgs& a);
 hipError_t launch_cp_gather(const CpArgs& a);
 hipError_t launch_cp_chain(const CpArgs& a);
