@@ -40,6 +40,8 @@ namespace {
 
 constexpr int kBC = 16;            // rows per backward chunk
 constexpr int kBThreads = 256;
+constexpr int kRecThreads = 320;   // the recurrences: four compute waves and an L2 prefetch wave
+constexpr int kBAhead = 4;         // chunks the prefetch wave runs ahead
 constexpr float kSpanMax = 64.f;   // exp(64) ~ 6e27: room for sums of O(1e10) below FLT_MAX
 
 // Chunk record (floats) per (slot, head).
@@ -262,175 +264,6 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   if (tid == 0) rec[R::kInfo] = unsafe ? 1.f : 0.f;
 }
 
-// ---------------------------------------------------- recurrences (helpers)
-// Per-chunk operands of one 16-column state tile, staged through registers
-// one chunk ahead and stored into the LDS buffer of the next chunk.
-template <int K, int V, bool kRev>
-struct Stage {
-  static constexpr int NW = kBC * K / 4 / kBThreads;   // float4 of W (and Kt, Qg) per thread
-  f32x4 w[NW], kt[NW], qg[NW];
-  float u, aq, gc, dout;
-  __device__ void fetch(const float* rec, int tid, int tile, const float* dorow_f, const uint16_t* dorow_b,
-                        int64_t do_stride, int len) {
-    using R = BRec<K, V>;
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      w[i] = reinterpret_cast<const f32x4*>(rec + R::kW)[tid + i * kBThreads];
-      kt[i] = reinterpret_cast<const f32x4*>(rec + R::kKt)[tid + i * kBThreads];
-      if (kRev) qg[i] = reinterpret_cast<const f32x4*>(rec + R::kQg)[tid + i * kBThreads];
-    }
-    const int r = tid / kBC, j = tid % kBC;
-    u = kRev ? 0.f : rec[R::kU + r * V + tile * kBC + j];
-    aq = kRev ? rec[R::kAqk + tid] : 0.f;
-    gc = tid < K ? rec[R::kGc + tid] : 0.f;
-    dout = 0.f;
-    if (kRev && r < len) dout = dorow_f ? dorow_f[r * do_stride + tile * kBC + j]
-                                        : bits_to_f32(dorow_b[r * do_stride + tile * kBC + j]);
-  }
-  __device__ void store(float (*sW)[K], float (*sKt)[K], float (*sQg)[K], float (*sX)[kBC], float (*sAq)[kBC],
-                        float* sGc, float (*sdO)[kBC], int tid) const {
-#pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      reinterpret_cast<f32x4*>(&sW[0][0])[tid + i * kBThreads] = w[i];
-      reinterpret_cast<f32x4*>(&sKt[0][0])[tid + i * kBThreads] = kt[i];
-      if (kRev) reinterpret_cast<f32x4*>(&sQg[0][0])[tid + i * kBThreads] = qg[i];
-    }
-    const int r = tid / kBC, j = tid % kBC;
-    if (!kRev) sX[r][j] = u;
-    if (kRev) {
-      sAq[r][j] = aq;
-      sdO[r][j] = dout;
-    }
-    if (tid < K) sGc[tid] = gc;
-  }
-};
-
-// ---------------------------------------------------------------- bwd_states
-// One workgroup per (sequence, head, 16 value columns): S from the initial
-// state through every chunk, writing the state entering each chunk.
-template <int K, int V>
-__global__ __launch_bounds__(kBThreads) void bwd_states_kernel(BwdParams p) {
-  using R = BRec<K, V>;
-  constexpr int NV = V / kBC;
-  const int64_t id = blockIdx.x;
-  const int tile = (int)(id % NV);
-  const int64_t sh = id / NV, h = sh % p.H, sq = sh / p.H;
-  BSeq s;
-  if (!seq_info(p, sq, h, &s)) return;
-  __shared__ float S[K][kBC];
-  __shared__ float sW[2][kBC][K], sKt[2][kBC][K], sU[2][kBC][kBC], sGc[2][K], sD[kBC][kBC];
-  const int tid = threadIdx.x;
-  const int cr = tid / 2, j0 = (tid % 2) * 8;   // state rows owned in the update (K = 128; K = 64 uses tid < 128)
-  for (int e = tid; e < K * kBC; e += kBThreads) {
-    const int c = e / kBC, j = e % kBC;
-    S[c][j] = p.init ? p.init[s.state * K * V + c * V + tile * kBC + j] : 0.f;
-  }
-  auto rec = [&](int64_t n) { return p.rec + ((s.slot0 + n) * p.H + h) * R::kFloats; };
-  Stage<K, V, false> st;
-  st.fetch(rec(0), tid, tile, nullptr, nullptr, 0, 0);
-  st.store(sW[0], sKt[0], nullptr, sU[0], nullptr, sGc[0], nullptr, tid);
-  __syncthreads();
-  for (int64_t n = 0; n < s.n16; ++n) {
-    const int cur = (int)(n & 1);
-    if (n + 1 < s.n16) st.fetch(rec(n + 1), tid, tile, nullptr, nullptr, 0, 0);
-    float* hs = p.hs + ((s.slot0 + n) * p.H + h) * K * V + tile * kBC;
-    for (int e = tid; e < K * kBC; e += kBThreads) hs[(e / kBC) * V + e % kBC] = S[e / kBC][e % kBC];
-    {
-      const int r = tid / kBC, j = tid % kBC;
-      float d = sU[cur][r][j];
-      for (int c = 0; c < K; ++c) d -= sW[cur][r][c] * S[c][j];
-      sD[r][j] = d;
-    }
-    __syncthreads();
-    if (cr < K) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float x = sGc[cur][cr] * S[cr][j0 + jj];
-        for (int r = 0; r < kBC; ++r) x += sKt[cur][r][cr] * sD[r][j0 + jj];
-        S[cr][j0 + jj] = x;
-      }
-    }
-    if (n + 1 < s.n16) st.store(sW[cur ^ 1], sKt[cur ^ 1], nullptr, sU[cur ^ 1], nullptr, sGc[cur ^ 1], nullptr, tid);
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------- bwd_dstates
-// One workgroup per (sequence, head, 16 value columns): dS' from the final
-// state's gradient back through every chunk, writing dS' of each chunk and
-// the gradient of the sequence's initial state.
-template <class TO, int K, int V>
-__global__ __launch_bounds__(kBThreads) void bwd_dstates_kernel(BwdParams p) {
-  using R = BRec<K, V>;
-  constexpr int NV = V / kBC;
-  const int64_t id = blockIdx.x;
-  const int tile = (int)(id % NV);
-  const int64_t sh = id / NV, h = sh % p.H, sq = sh / p.H;
-  BSeq s;
-  if (!seq_info(p, sq, h, &s)) return;
-  __shared__ float S[K][kBC];   // dS'
-  __shared__ float sW[2][kBC][K], sKt[2][kBC][K], sQg[2][kBC][K];
-  __shared__ float sAq[2][kBC][kBC], sdO[2][kBC][kBC], sGc[2][K], sD[kBC][kBC];
-  const int tid = threadIdx.x;
-  const int cr = tid / 2, j0 = (tid % 2) * 8;
-  const TO* d_o = static_cast<const TO*>(p.d_o);
-  for (int e = tid; e < K * kBC; e += kBThreads) {
-    const int c = e / kBC, j = e % kBC;
-    S[c][j] = p.d_final ? p.d_final[s.state * K * V + c * V + tile * kBC + j] : 0.f;
-  }
-  auto rec = [&](int64_t n) { return p.rec + ((s.slot0 + n) * p.H + h) * R::kFloats; };
-  auto fetch = [&](Stage<K, V, true>& st, int64_t n) {
-    const int64_t t0 = s.t0 + n * kBC;
-    const int len = (int)min<int64_t>(kBC, (p.packed ? p.segs[sq].len : p.T) - n * kBC);
-    const TO* row = d_o + ((s.b * p.T + t0) * p.H + h) * V;
-    if constexpr (sizeof(TO) == 4)
-      st.fetch(rec(n), tid, tile, reinterpret_cast<const float*>(row), nullptr, p.H * V, len);
-    else
-      st.fetch(rec(n), tid, tile, nullptr, reinterpret_cast<const uint16_t*>(row), p.H * V, len);
-  };
-  Stage<K, V, true> st;
-  fetch(st, s.n16 - 1);
-  st.store(sW[0], sKt[0], sQg[0], nullptr, sAq[0], sGc[0], sdO[0], tid);
-  __syncthreads();
-  for (int64_t m = 0; m < s.n16; ++m) {
-    const int64_t n = s.n16 - 1 - m;
-    const int cur = (int)(m & 1);
-    if (n > 0) fetch(st, n - 1);
-    float* dhs = p.dhs + ((s.slot0 + n) * p.H + h) * K * V + tile * kBC;
-    for (int e = tid; e < K * kBC; e += kBThreads) dhs[(e / kBC) * V + e % kBC] = S[e / kBC][e % kBC];
-    {
-      // dDelta = scale Aqk^T dO + Kt dS'
-      const int i = tid / kBC, j = tid % kBC;
-      float d = 0.f;
-      for (int r = 0; r < kBC; ++r) d += sAq[cur][r][i] * sdO[cur][r][j];
-      d *= p.scale;
-      for (int c = 0; c < K; ++c) d += sKt[cur][i][c] * S[c][j];
-      sD[i][j] = d;
-    }
-    __syncthreads();
-    if (cr < K) {
-      // dS = diag(Gamma_C) dS' + scale Qg^T dO - W^T dDelta
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        float a = 0.f, b = 0.f;
-        for (int r = 0; r < kBC; ++r) {
-          a += sQg[cur][r][cr] * sdO[cur][r][j0 + jj];
-          b += sW[cur][r][cr] * sD[r][j0 + jj];
-        }
-        S[cr][j0 + jj] = sGc[cur][cr] * S[cr][j0 + jj] + p.scale * a - b;
-      }
-    }
-    if (n > 0) st.store(sW[cur ^ 1], sKt[cur ^ 1], sQg[cur ^ 1], nullptr, sAq[cur ^ 1], sGc[cur ^ 1], sdO[cur ^ 1], tid);
-    __syncthreads();
-  }
-  if (p.d_init)
-    for (int e = tid; e < K * kBC; e += kBThreads) {
-      const int c = e / kBC, j = e % kBC;
-      p.d_init[s.state * K * V + c * V + tile * kBC + j] = S[c][j];
-    }
-}
-
-// ---------------------------------------------------------------- bwd_local
 // fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32).  A 16-deep slab of a
 // product C (16x16) += A (16x16) B (16x16) is four instructions: for the j-th,
 // lane l = 16 g + n supplies A[n][4g + j] and B[4g + j][n], so one f32x4 per
@@ -452,6 +285,248 @@ __device__ __forceinline__ f32x4 opb(const float* Y, int ld, int k0, int n0, int
   return f32x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
 }
 
+// ---------------------------------------------------------------- bwd_states
+// One workgroup (four waves) per (sequence, head, 16 value columns): the
+// state from the initial state through every chunk, writing the state that
+// enters each chunk.  The 16-column state is K/16 accumulator tiles; wave w
+// holds tiles w, w + 4 (rows 16 cb ..), which are also the B operands of its
+// slabs of W S.  Per chunk: each wave's partial W S goes through LDS (double
+// buffered, one barrier), every wave sums the four in the same order into
+// Delta = U - W S, and updates its tiles S <- diag(Gamma_C) S + Kt^T Delta.
+// The chunk record's operands are loaded one chunk ahead.
+template <int K, int V>
+struct StatesOps {
+  static constexpr int TPW = K / 64;   // state tiles per wave
+  f32x4 w[TPW], kt[TPW], gc[TPW], u;
+  __device__ void load(const float* rec, int wave, int lane, int tile) {
+    using R = BRec<K, V>;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int cb = wave + 4 * t;
+      w[t] = opa(rec + R::kW, K, 0, 16 * cb, lane);      // W[r][16 cb + 4g + j]
+      kt[t] = opb(rec + R::kKt, K, 0, 16 * cb, lane);    // (Kt^T)[16 cb + n][4g + j]
+      gc[t] = *reinterpret_cast<const f32x4*>(rec + R::kGc + 16 * cb + 4 * (lane >> 4));
+    }
+    const float* up = rec + R::kU + (int64_t)(4 * (lane >> 4)) * V + tile * kBC + (lane & 15);
+    u = f32x4{up[0], up[V], up[2 * V], up[3 * V]};
+  }
+};
+
+// The fifth wave of a recurrence workgroup touches this workgroup's 1/NV
+// share of the record kBAhead chunks ahead (one 16-byte direct-to-LDS load
+// per 64-byte segment, into a sink), so that the compute waves' loads find
+// it in L2.  It meets the compute waves at every barrier.
+template <int K, int V, class RecFn, class ExtraFn>
+__device__ void prefetch_wave(RecFn rec, ExtraFn extra, int64_t n16, bool reverse, int tile, int lane, char* sink) {
+  using R = BRec<K, V>;
+  constexpr int NV = V / kBC;
+  constexpr int SEGS = (int)(R::kFloats * 4 / 64), SHARE = (SEGS + NV - 1) / NV;
+  auto touch = [&](int64_t c) {
+    const char* r = reinterpret_cast<const char*>(rec(reverse ? n16 - 1 - c : c));
+#pragma unroll
+    for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
+      const int e = i * kWave + lane, seg = tile * SHARE + e;
+      if (e < SHARE && seg < SEGS) dma16(sink, r + 64 * (int64_t)seg);
+    }
+    extra(reverse ? n16 - 1 - c : c);
+  };
+  for (int64_t c = 0; c < kBAhead && c < n16; ++c) touch(c);
+  for (int64_t c = 0; c < n16; ++c) {
+    if (c + kBAhead < n16) touch(c + kBAhead);
+    block_sync();
+  }
+  vm_wait<0>();
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
+  using R = BRec<K, V>;
+  using Ops = StatesOps<K, V>;
+  constexpr int NV = V / kBC, TPW = Ops::TPW;
+  // The NV workgroups of one (sequence, head) get ids of equal id % 8, which
+  // the dispatcher places on one XCD: they share its L2 copy of the records.
+  const int64_t id = blockIdx.x;
+  const int tile = (int)((id / 8) % NV);
+  const int64_t sh = (id / (8 * NV)) * 8 + id % 8, h = sh % p.H, sq = sh / p.H;
+  BSeq s;
+  if (!seq_info(p, sq, h, &s)) return;
+  __shared__ __align__(16) float sP[2][4][kBC][kBC];
+  __shared__ __align__(16) char s_sink[1024];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = 4 * (lane >> 4), n = lane & 15;
+  auto rec = [&](int64_t c) { return p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats; };
+  if (wave == 4) {
+    prefetch_wave<K, V>(rec, [](int64_t) {}, s.n16, false, tile, lane, s_sink);
+    return;
+  }
+  f32x4 st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      st[t][i] = p.init ? p.init[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n] : 0.f;
+  // Operands two chunks ahead in three register sets that rotate by name
+  // (the loop is unrolled by three), so no set is copied while its loads are
+  // in flight.
+  auto step = [&](int64_t c, const Ops& cur, Ops& fill) {
+    if (c + 2 < s.n16) fill.load(rec(c + 2), wave, lane, tile);
+    float* hs = p.hs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC + n;
+    f32x4 d = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hs[(int64_t)(16 * (wave + 4 * t) + g4 + i) * V] = st[t][i];
+      mma16(d, cur.w[t], st[t]);
+    }
+    const int buf = (int)(c & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sP[buf][wave][g4 + i][n] = d[i];
+    block_sync();
+    f32x4 delta;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      delta[i] = cur.u[i] - (sP[buf][0][g4 + i][n] + sP[buf][1][g4 + i][n] + sP[buf][2][g4 + i][n] +
+                             sP[buf][3][g4 + i][n]);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      f32x4 x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = cur.gc[t][i] * st[t][i];
+      mma16(x, cur.kt[t], delta);
+      st[t] = x;
+    }
+  };
+  Ops o0, o1, o2;
+  o0.load(rec(0), wave, lane, tile);
+  if (s.n16 > 1) o1.load(rec(1), wave, lane, tile);
+  for (int64_t c = 0; c < s.n16; c += 3) {
+    step(c, o0, o2);
+    if (c + 1 < s.n16) step(c + 1, o1, o0);
+    if (c + 2 < s.n16) step(c + 2, o2, o1);
+  }
+}
+
+// ---------------------------------------------------------------- bwd_dstates
+// One workgroup (four waves) per (sequence, head, 16 value columns): dS'
+// from the final state's gradient back through every chunk, writing dS' of
+// each chunk and the gradient of the sequence's initial state.  Same tiling
+// as bwd_states: per chunk the waves' partial Kt dS' (and scale Aqk^T dO,
+// added by wave 0) are summed into dDelta through LDS, then each wave updates
+// its tiles dS = diag(Gamma_C) dS' + scale Qg^T dO - W^T dDelta.
+template <int K, int V>
+struct DStatesOps {
+  static constexpr int TPW = K / 64;
+  f32x4 kt[TPW], qgt[TPW], wt[TPW], gc[TPW], aq, dout;
+  template <class TO>
+  __device__ void load(const float* rec, const TO* dorow, int64_t stride, int len, int wave, int lane, int tile) {
+    using R = BRec<K, V>;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int cb = wave + 4 * t;
+      kt[t] = opa(rec + R::kKt, K, 0, 16 * cb, lane);    // Kt[r][16 cb + 4g + j]
+      qgt[t] = opb(rec + R::kQg, K, 0, 16 * cb, lane);   // (Qg^T)[16 cb + n][4g + j]
+      wt[t] = opb(rec + R::kW, K, 0, 16 * cb, lane);     // (W^T)[16 cb + n][4g + j]
+      gc[t] = *reinterpret_cast<const f32x4*>(rec + R::kGc + 16 * cb + 4 * (lane >> 4));
+    }
+    aq = opb(rec + R::kAqk, kBC, 0, 0, lane);              // (Aqk^T)[n][4g + j]
+    const int g4 = 4 * (lane >> 4), n = lane & 15;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dout[j] = g4 + j < len ? ld(dorow, (g4 + j) * stride + tile * kBC + n) : 0.f;
+  }
+};
+
+template <class TO, int K, int V>
+__global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
+  using R = BRec<K, V>;
+  using Ops = DStatesOps<K, V>;
+  constexpr int NV = V / kBC, TPW = Ops::TPW;
+  // The NV workgroups of one (sequence, head) get ids of equal id % 8, which
+  // the dispatcher places on one XCD: they share its L2 copy of the records.
+  const int64_t id = blockIdx.x;
+  const int tile = (int)((id / 8) % NV);
+  const int64_t sh = (id / (8 * NV)) * 8 + id % 8, h = sh % p.H, sq = sh / p.H;
+  BSeq s;
+  if (!seq_info(p, sq, h, &s)) return;
+  __shared__ __align__(16) float sP[2][4][kBC][kBC];
+  __shared__ __align__(16) char s_sink[1024];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g4 = 4 * (lane >> 4), n = lane & 15;
+  const TO* d_o = static_cast<const TO*>(p.d_o);
+  const int64_t seq_len = p.packed ? p.segs[sq].len : p.T;
+  if (wave == 4) {
+    // records, and this workgroup's 16 columns of the chunk's d_o rows
+    auto rec = [&](int64_t c) { return p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats; };
+    auto rows = [&](int64_t c) {
+      if (lane < kBC && c * kBC + lane < seq_len)
+        dma16(s_sink, d_o + ((s.b * p.T + s.t0 + c * kBC + lane) * p.H + h) * V + tile * kBC);
+    };
+    prefetch_wave<K, V>(rec, rows, s.n16, true, tile, lane, s_sink);
+    return;
+  }
+  f32x4 st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      st[t][i] = p.d_final ? p.d_final[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n]
+                           : 0.f;
+  auto load = [&](Ops& o, int64_t c) {
+    const int len = (int)min<int64_t>(kBC, seq_len - c * kBC);
+    const TO* row = d_o + ((s.b * p.T + s.t0 + c * kBC) * p.H + h) * V;
+    o.load(p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats, row, p.H * V, len, wave, lane, tile);
+  };
+  // Operands two chunks ahead in three rotating register sets, as above.
+  auto step = [&](int64_t m, const Ops& cur, Ops& fill) {
+    const int64_t c = s.n16 - 1 - m;
+    if (c > 1) load(fill, c - 2);
+    float* dhs = p.dhs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC + n;
+    f32x4 d = {0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dhs[(int64_t)(16 * (wave + 4 * t) + g4 + i) * V] = st[t][i];
+      mma16(d, cur.kt[t], st[t]);
+    }
+    if (wave == 0) {
+      f32x4 e = {0, 0, 0, 0};
+      mma16(e, cur.aq, cur.dout);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] += p.scale * e[i];
+    }
+    const int buf = (int)(m & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sP[buf][wave][g4 + i][n] = d[i];
+    block_sync();
+    f32x4 dd;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dd[i] = sP[buf][0][g4 + i][n] + sP[buf][1][g4 + i][n] + sP[buf][2][g4 + i][n] + sP[buf][3][g4 + i][n];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      f32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
+      mma16(a, cur.qgt[t], cur.dout);
+      mma16(b, cur.wt[t], dd);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[t][i] = cur.gc[t][i] * st[t][i] + p.scale * a[i] - b[i];
+    }
+  };
+  Ops o0, o1, o2;
+  load(o0, s.n16 - 1);
+  if (s.n16 > 1) load(o1, s.n16 - 2);
+  for (int64_t m = 0; m < s.n16; m += 3) {
+    step(m, o0, o2);
+    if (m + 1 < s.n16) step(m + 1, o1, o0);
+    if (m + 2 < s.n16) step(m + 2, o2, o1);
+  }
+  if (p.d_init)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.d_init[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n] = st[t][i];
+}
+
+// ---------------------------------------------------------------- bwd_local
 // One workgroup (four waves) per (chunk, head): every input gradient of the
 // chunk's rows.  Phase A (contraction over K; wave w takes value blocks w,
 // w + 4, ...): Delta = U - W h, dDelta = scale Aqk^T dO + Kt dh, and
@@ -785,11 +860,13 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   p.rec = a.rec; p.hs = a.hs; p.dhs = a.dhs;
   const int64_t slots = 4 * a.cmax;
   const dim3 blk(kBThreads);
-  const int64_t seqs = (p.packed ? a.smax : a.B) * a.H * (V / kBC);
+  const int64_t seqs = ((p.packed ? a.smax : a.B) * a.H + 7) / 8 * 8 * (V / kBC);
   switch (stage) {
     case 0: hipLaunchKernelGGL((bwd_chunk_kernel<TI, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p); break;
-    case 1: hipLaunchKernelGGL((bwd_states_kernel<K, V>), dim3((unsigned)seqs), blk, 0, a.stream, p); break;
-    case 2: hipLaunchKernelGGL((bwd_dstates_kernel<TO, K, V>), dim3((unsigned)seqs), blk, 0, a.stream, p); break;
+    case 1: hipLaunchKernelGGL((bwd_states_kernel<K, V>), dim3((unsigned)seqs), dim3(kRecThreads), 0, a.stream, p); break;
+    case 2:
+      hipLaunchKernelGGL((bwd_dstates_kernel<TO, K, V>), dim3((unsigned)seqs), dim3(kRecThreads), 0, a.stream, p);
+      break;
     case 3: hipLaunchKernelGGL((bwd_local_kernel<TI, TO, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p); break;
     default: return hipErrorInvalidValue;
   }
