@@ -419,7 +419,7 @@ namespace {
 
 struct BwdPlan {
   Plan t;                      // tables (the forward's layout up to its records)
-  size_t off_rec = 0, off_hs = 0, off_dhs = 0, total = 0;
+  size_t off_rec = 0, off_hs = 0, off_dhs = 0, off_ds = 0, off_dds = 0, total = 0;
 };
 
 kda_status_t bwd_validate(const kda_fwd_desc_t* d, bool has_seg, BwdPlan* bp) {
@@ -432,7 +432,11 @@ kda_status_t bwd_validate(const kda_fwd_desc_t* d, bool has_seg, BwdPlan* bp) {
   b.off_hs = off;
   off = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
   b.off_dhs = off;
-  b.total = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
+  off = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
+  b.off_ds = off;
+  off = align_up(off + slots * H * (size_t)(16 * d->V) * sizeof(float));
+  b.off_dds = off;
+  b.total = align_up(off + slots * H * (size_t)(16 * d->V) * sizeof(float));
   *bp = b;
   return KDA_OK;
 }
@@ -525,6 +529,8 @@ kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void
     a.rec = reinterpret_cast<float*>(ws + bp.off_rec);
     a.hs = reinterpret_cast<float*>(ws + bp.off_hs);
     a.dhs = reinterpret_cast<float*>(ws + bp.off_dhs);
+    a.ds = reinterpret_cast<float*>(ws + bp.off_ds);
+    a.dds = reinterpret_cast<float*>(ws + bp.off_dds);
     a.stream = s;
     static const char* const names[4] = {"kda_bwd_chunk", "kda_bwd_states", "kda_bwd_dstates", "kda_bwd_local"};
     for (int stage = 0; stage < 4 && e == hipSuccess; ++stage)

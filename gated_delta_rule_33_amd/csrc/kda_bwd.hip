@@ -73,6 +73,8 @@ struct BwdParams {
   float* rec;                   // [slots][H][BRec::kFloats]
   float* hs;                    // [slots][H][K][V] state entering each chunk
   float* dhs;                   // [slots][H][K][V] dL/d(state leaving each chunk)
+  float* ds;                    // [slots][H][16][V] Delta of each chunk
+  float* dds;                   // [slots][H][16][V] dDelta of each chunk
 };
 
 // A 16-row chunk: slot s is sub-chunk s % 4 of 64-token chunk s / 4.
@@ -387,6 +389,11 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
       delta[i] = cur.u[i] - (sP[buf][0][g4 + i][n] + sP[buf][1][g4 + i][n] + sP[buf][2][g4 + i][n] +
                              sP[buf][3][g4 + i][n]);
+    if (wave == 0) {
+      float* dst = p.ds + ((s.slot0 + c) * p.H + h) * kBC * V + tile * kBC + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(g4 + i) * V] = delta[i];
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       f32x4 x;
@@ -501,6 +508,11 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       dd[i] = sP[buf][0][g4 + i][n] + sP[buf][1][g4 + i][n] + sP[buf][2][g4 + i][n] + sP[buf][3][g4 + i][n];
+    if (wave == 0) {
+      float* dst = p.dds + ((s.slot0 + c) * p.H + h) * kBC * V + tile * kBC + n;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(g4 + i) * V] = dd[i];
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       f32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
@@ -528,11 +540,10 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_local
 // One workgroup (four waves) per (chunk, head): every input gradient of the
-// chunk's rows.  Phase A (contraction over K; wave w takes value blocks w,
-// w + 4, ...): Delta = U - W h, dDelta = scale Aqk^T dO + Kt dh, and
-// d Gamma_C = rowsum(dh * h).  Phase B (contraction over V; wave w takes key
-// blocks w, w + 4, ...): dQg = scale dO h^T, dKt = Delta dh^T,
-// dW = -dDelta h^T; besides, wave 0 dAqk = scale dO Delta^T, wave 1
+// chunk's rows.  Delta and dDelta come from the recurrences.  Phase B
+// (contraction over V; wave w takes key blocks w, w + 4, ...): dQg =
+// scale dO h^T, dKt = Delta dh^T, dW = -dDelta h^T and d Gamma_C =
+// rowsum(dh * h); besides, wave 0 dAqk = scale dO Delta^T, wave 1
 // dT = dDelta Vb^T, waves 2-3 dVb = T^T dDelta (dv, and dbeta's V part).
 // Phase C: dT += dW Kb^T, dA = -T^T dT T^T.  Phase D (key blocks again): dKb =
 // T^T dW and the exponent-factor sums of A and Aqk, assembled per (row,
@@ -554,7 +565,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   __shared__ __align__(16) float sX[kBC][kBC];
   // Per-wave partial sums (one writer each), combined in wave order: no
   // atomics, so every run adds in the same order.
-  __shared__ float sdgcp[4][K], sred[4][kBC][4], sdTp[4][kBC][kBC];
+  __shared__ float sdgc[K], sred[4][kBC][4], sdTp[4][kBC][kBC];
   __shared__ float sbeta[kBC], snq[kBC], snk[kBC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = 4 * (lane >> 4), n = lane & 15;
   const TI* q = static_cast<const TI*>(p.q);
@@ -584,7 +595,6 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   }
   sT[tid / kBC][tid % kBC] = rec[R::kT + tid];
   sAqk[tid / kBC][tid % kBC] = rec[R::kAqk + tid];
-  for (int e = tid; e < 4 * K; e += kBThreads) (&sdgcp[0][0])[e] = 0.f;
   for (int e = tid; e < 4 * kBC * 4; e += kBThreads) (&sred[0][0][0])[e] = 0.f;
   for (int e = tid; e < 4 * kBC * kBC; e += kBThreads) (&sdTp[0][0][0])[e] = 0.f;
   if (tid < kBC) sbeta[tid] = tid < len ? ld(beta, tok(tid)) : 0.f;
@@ -611,44 +621,37 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   }
   __syncthreads();
 
-  // ---- phase A: Delta, dDelta, d Gamma_C
-  for (int vb = wave; vb < NVB; vb += 4) {
-    f32x4 cD = {0, 0, 0, 0}, cDD = {0, 0, 0, 0};
-#pragma unroll 2
-    for (int s = 0; s < NKB; ++s) {
-      const f32x4 bh = opb(hS, V, 16 * s, 16 * vb, lane), bdh = opb(dhS, V, 16 * s, 16 * vb, lane);
-      mma16(cD, opa(rec + R::kW, K, 0, 16 * s, lane), bh);
-      mma16(cDD, opa(rec + R::kKt, K, 0, 16 * s, lane), bdh);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = sum16(bh[j] * bdh[j]);
-        if (n == 0) sdgcp[wave][16 * s + g4 + j] += x;
-      }
-    }
-    f32x4 cq = {0, 0, 0, 0};
-    mma16(cq, opb(&sAqk[0][0], kBC, 0, 0, lane), opb(sdO, V, 0, 16 * vb, lane));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = g4 + i, j = 16 * vb + n;
-      sD[r * V + j] = rec[R::kU + r * V + j] - cD[i];
-      sdD[r * V + j] = cDD[i] + p.scale * cq[i];
+  // ---- Delta and dDelta of the chunk, as the recurrences left them
+  {
+    const float* gD = p.ds + (slot * p.H + h) * kBC * V;
+    const float* gdD = p.dds + (slot * p.H + h) * kBC * V;
+    for (int e = tid; e < kBC * V / 4; e += kBThreads) {
+      reinterpret_cast<f32x4*>(sD)[e] = reinterpret_cast<const f32x4*>(gD)[e];
+      reinterpret_cast<f32x4*>(sdD)[e] = reinterpret_cast<const f32x4*>(gdD)[e];
     }
   }
   __syncthreads();
 
   // ---- phase B: products over V
+  // d Gamma_C = rowsum(dh * h) comes along: lane (g, n) holds h and dh of
+  // channel 16 cb + n, columns 16 s + 4g .. +3.
   f32x4 cQ[2], cKt[2], cW[2];
   for (int u = 0; u < 2; ++u) {
     const int cb = wave + 4 * u;
     cQ[u] = cKt[u] = cW[u] = f32x4{0, 0, 0, 0};
     if (cb >= NKB) continue;
+    float gsum = 0.f;
 #pragma unroll 2
     for (int s = 0; s < NVB; ++s) {
       const f32x4 bh = opa(hS, V, 16 * cb, 16 * s, lane), bdh = opa(dhS, V, 16 * cb, 16 * s, lane);
       mma16(cQ[u], opa(sdO, V, 0, 16 * s, lane), bh);
       mma16(cKt[u], opa(sD, V, 0, 16 * s, lane), bdh);
       mma16(cW[u], opa(sdD, V, 0, 16 * s, lane), bh);
+      gsum += bh[0] * bdh[0] + bh[1] * bdh[1] + bh[2] * bdh[2] + bh[3] * bdh[3];
     }
+    gsum += __shfl_xor(gsum, 16);
+    gsum += __shfl_xor(gsum, 32);
+    if (lane < 16) sdgc[16 * cb + n] = gsum;
   }
   if (wave == 0) {
     f32x4 c = {0, 0, 0, 0};
@@ -786,7 +789,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
     float lastx = 0.f;
     if (last >= g4 && last < g4 + 4) {
       for (int x = 0; x < kBC; ++x) lastx += sdKt[x * K + c] * rec[R::kKt + x * K + c];
-      lastx += (sdgcp[0][c] + sdgcp[1][c] + sdgcp[2][c] + sdgcp[3][c]) * __expf(GC);
+      lastx += sdgc[c] * __expf(GC);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -857,7 +860,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.d_o = a.d_o;
   p.init = a.init; p.d_final = a.d_final;
   p.dq = a.dq; p.dk = a.dk; p.dv = a.dv; p.dg = a.dg; p.dbeta = a.dbeta; p.d_init = a.d_init;
-  p.rec = a.rec; p.hs = a.hs; p.dhs = a.dhs;
+  p.rec = a.rec; p.hs = a.hs; p.dhs = a.dhs; p.ds = a.ds; p.dds = a.dds;
   const int64_t slots = 4 * a.cmax;
   const dim3 blk(kBThreads);
   const int64_t seqs = ((p.packed ? a.smax : a.B) * a.H + 7) / 8 * 8 * (V / kBC);

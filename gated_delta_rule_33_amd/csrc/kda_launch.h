@@ -96,6 +96,7 @@ struct BwdArgs {
   SegEntry* segs;
   ChunkEntry* chunks;
   float *rec, *hs, *dhs;      // chunk records, states entering and gradients leaving each 16-row chunk
+  float *ds, *dds;            // Delta and dDelta of each 16-row chunk
   hipStream_t stream;
 };
 
