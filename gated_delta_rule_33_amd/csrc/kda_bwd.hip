@@ -139,18 +139,47 @@ __device__ __forceinline__ float sum16(float x) {
   return x;
 }
 
+// fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32).  A 16-deep slab of a
+// product C (16x16) += A (16x16) B (16x16) is four instructions: for the j-th,
+// lane l = 16 g + n supplies A[n][4g + j] and B[4g + j][n], so one f32x4 per
+// operand and lane covers the slab.  The accumulator lane l holds C[4g + i][n]
+// (i = 0..3), which is also the B operand of a 16-deep slab over its rows.
+__device__ __forceinline__ void mma16(f32x4& c, const f32x4& a, const f32x4& b) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
+}
+// A operand of a row-major X (rows m0.., k = k0 + 4g + j); also the B operand
+// of X^T (cols m0..).
+__device__ __forceinline__ f32x4 opa(const float* X, int ld, int m0, int k0, int lane) {
+  return *reinterpret_cast<const f32x4*>(X + (int64_t)(m0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
+}
+// B operand of a row-major Y (k = k0 + 4g + j, cols n0..); also the A operand
+// of Y^T (rows n0..).
+__device__ __forceinline__ f32x4 opb(const float* Y, int ld, int k0, int n0, int lane) {
+  const float* q = Y + (int64_t)(k0 + 4 * (lane >> 4)) * ld + n0 + (lane & 15);
+  return f32x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
+}
+
 // ---------------------------------------------------------------- bwd_chunk
+// One workgroup (four waves) per (chunk, head): the chunk quantities into
+// the chunk record.  A = beta (kf kb^T) and Aqk = qf kb^T with kf = k exp(G -
+// G_0), kb = k exp(G_0 - G), qf = q exp(G - G_0) (or exp(G_r - G_i) per
+// element past the span limit), T = (I + A)^-1 = (I - A)(I + A^2)(I + A^4)
+// (I + A^8) (A is strictly lower, so A^16 = 0), W = T Kb, U = T Vb: all on
+// fp32 matrix-core tiles, 16x16 intermediates through LDS.
 template <class TI, int K, int V>
 __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   using R = BRec<K, V>;
+  constexpr int NKB = K / 16, NVB = V / 16;
   const int64_t slot = blockIdx.x / p.H, h = blockIdx.x % p.H;
   BSlot si;
   if (!slot_info(p, slot, &si)) return;
-  __shared__ float sk[kBC][K], sq[kBC][K], sG[kBC][K], sv[kBC][V];
-  __shared__ float skf[kBC][K], skb[kBC][K], sqf[kBC][K];
-  __shared__ float sA[kBC][kBC + 1], sT[kBC][kBC + 1], sbeta[kBC];
+  __shared__ __align__(16) float sk[kBC][K], sq[kBC][K], sG[kBC][K], sv[kBC][V];
+  __shared__ __align__(16) float skf[kBC][K], skb[kBC][K], sqf[kBC][K];
+  __shared__ __align__(16) float sA[kBC][kBC], sP1[kBC][kBC], sP2[kBC][kBC], sT[kBC][kBC];
+  __shared__ float sbeta[kBC];
   __shared__ int s_unsafe;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = 4 * (lane >> 4), n = lane & 15;
   const TI* q = static_cast<const TI*>(p.q);
   const TI* k = static_cast<const TI*>(p.k);
   const TI* v = static_cast<const TI*>(p.v);
@@ -212,79 +241,99 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
     if (r == 0) rec[R::kGc + c] = __expf(GC);
   }
   __syncthreads();
-  {
-    // A and Aqk, one (r, i) pair per thread
-    const int r = tid / kBC, i = tid % kBC;
-    float a = 0.f, aq = 0.f;
-    if (i <= r) {
-      if (!unsafe) {
-        for (int c = 0; c < K; ++c) {
-          a += skf[r][c] * skb[i][c];
-          aq += sqf[r][c] * skb[i][c];
-        }
-      } else {
-        for (int c = 0; c < K; ++c) {
-          const float e = __expf(sG[r][c] - sG[i][c]);
-          a += sk[r][c] * sk[i][c] * e;
-          aq += sq[r][c] * sk[i][c] * e;
-        }
+  if (wave < 2) {
+    // wave 0: A, wave 1: Aqk (contraction over K)
+    f32x4 c = {0, 0, 0, 0};
+    if (!unsafe) {
+      const float* left = wave == 0 ? &skf[0][0] : &sqf[0][0];
+#pragma unroll 4
+      for (int s = 0; s < NKB; ++s) mma16(c, opa(left, K, 0, 16 * s, lane), opa(&skb[0][0], K, 0, 16 * s, lane));
+    } else {
+      const float* left = wave == 0 ? &sk[0][0] : &sq[0][0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = g4 + i;
+        float x = 0.f;
+        if (n <= r)
+          for (int cc = 0; cc < K; ++cc) x += left[r * K + cc] * sk[n][cc] * __expf(sG[r][cc] - sG[n][cc]);
+        c[i] = x;
       }
     }
-    sA[r][i] = i < r ? sbeta[r] * a : 0.f;
-    rec[R::kAqk + r * kBC + i] = aq;
-  }
-  __syncthreads();
-  // T = (I + A)^-1 by forward substitution, one column per thread
-  if (tid < kBC) {
-    const int j = tid;
-    for (int r = 0; r < kBC; ++r) {
-      float t = r == j ? 1.f : 0.f;
-      for (int i = j; i < r; ++i) t -= sA[r][i] * sT[i][j];
-      sT[r][j] = r >= j ? t : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = g4 + i;
+      if (wave == 0) sA[r][n] = n < r ? sbeta[r] * c[i] : 0.f;
+      else rec[R::kAqk + r * kBC + n] = n <= r ? c[i] : 0.f;
     }
   }
   // Kb = diag(beta) (K * Gamma) in place of q, which A and Aqk no longer need
+  __syncthreads();
   for (int e = tid; e < kBC * K; e += kBThreads) {
     const int r = e / K, c = e % K;
     sq[r][c] = sbeta[r] * sk[r][c] * __expf(sG[r][c]);
   }
+  if (wave == 0) {
+    // T = (I - A)(I + A^2)(I + A^4)(I + A^8): squares and products, one wave
+    auto mul = [&](const float (*X)[kBC], const float (*Y)[kBC]) {
+      f32x4 c = {0, 0, 0, 0};
+      mma16(c, opa(&X[0][0], kBC, 0, 0, lane), opb(&Y[0][0], kBC, 0, 0, lane));
+      return c;
+    };
+    auto put = [&](float (*X)[kBC], const f32x4& c, float diag) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) X[g4 + i][n] = c[i] + (g4 + i == n ? diag : 0.f);
+    };
+    // sP1 = A^2; sT = I - A; sP2 = (I - A)(I + A^2)
+    put(sP1, mul(sA, sA), 0.f);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sT[g4 + i][n] = (g4 + i == n ? 1.f : 0.f) - sA[g4 + i][n];
+    lds_wait();
+    {
+      f32x4 c = mul(sT, sP1);   // (I - A) A^2
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += sT[g4 + i][n];
+      put(sP2, c, 0.f);         // (I - A)(I + A^2)
+    }
+    lds_wait();
+    put(sA, mul(sP1, sP1), 0.f);   // A^4 (A no longer needed)
+    lds_wait();
+    {
+      f32x4 c = mul(sP2, sA);   // X (A^4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += sP2[g4 + i][n];
+      put(sT, c, 0.f);          // X (I + A^4)
+    }
+    lds_wait();
+    put(sP1, mul(sA, sA), 0.f);    // A^8
+    lds_wait();
+    {
+      f32x4 c = mul(sT, sP1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] += sT[g4 + i][n];
+      lds_wait();
+      put(sT, c, 0.f);          // T
+    }
+  }
   __syncthreads();
   rec[R::kT + tid] = sT[tid / kBC][tid % kBC];
-  // W = T Kb, U = T diag(beta) V
-  for (int e = tid; e < kBC * K; e += kBThreads) {
-    const int r = e / K, c = e % K;
-    float w = 0.f;
-    for (int i = 0; i <= r; ++i) w += sT[r][i] * sq[i][c];
-    rec[R::kW + e] = w;
-  }
-  for (int e = tid; e < kBC * V; e += kBThreads) {
-    const int r = e / V, j = e % V;
-    float u = 0.f;
-    for (int i = 0; i <= r; ++i) u += sT[r][i] * sbeta[i] * sv[i][j];
-    rec[R::kU + e] = u;
+  // W = T Kb, U = T Vb: K/16 + V/16 output tiles over the four waves
+  for (int t = wave; t < NKB + NVB; t += 4) {
+    f32x4 c = {0, 0, 0, 0};
+    if (t < NKB) {
+      mma16(c, opa(&sT[0][0], kBC, 0, 0, lane), opb(&sq[0][0], K, 0, 16 * t, lane));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rec[R::kW + (g4 + i) * K + 16 * t + n] = c[i];
+    } else {
+      const int vb = t - NKB;
+      f32x4 b = opb(&sv[0][0], V, 0, 16 * vb, lane);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] *= sbeta[g4 + j];
+      mma16(c, opa(&sT[0][0], kBC, 0, 0, lane), b);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rec[R::kU + (g4 + i) * V + 16 * vb + n] = c[i];
+    }
   }
   if (tid == 0) rec[R::kInfo] = unsafe ? 1.f : 0.f;
-}
-
-// fp32 matrix-core tiles (v_mfma_f32_16x16x4_f32).  A 16-deep slab of a
-// product C (16x16) += A (16x16) B (16x16) is four instructions: for the j-th,
-// lane l = 16 g + n supplies A[n][4g + j] and B[4g + j][n], so one f32x4 per
-// operand and lane covers the slab.  The accumulator lane l holds C[4g + i][n]
-// (i = 0..3), which is also the B operand of a 16-deep slab over its rows.
-__device__ __forceinline__ void mma16(f32x4& c, const f32x4& a, const f32x4& b) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], c, 0, 0, 0);
-}
-// A operand of a row-major X (rows m0.., k = k0 + 4g + j); also the B operand
-// of X^T (cols m0..).
-__device__ __forceinline__ f32x4 opa(const float* X, int ld, int m0, int k0, int lane) {
-  return *reinterpret_cast<const f32x4*>(X + (int64_t)(m0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4));
-}
-// B operand of a row-major Y (k = k0 + 4g + j, cols n0..); also the A operand
-// of Y^T (rows n0..).
-__device__ __forceinline__ f32x4 opb(const float* Y, int ld, int k0, int n0, int lane) {
-  const float* q = Y + (int64_t)(k0 + 4 * (lane >> 4)) * ld + n0 + (lane & 15);
-  return f32x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
 }
 
 // ---------------------------------------------------------------- bwd_states
