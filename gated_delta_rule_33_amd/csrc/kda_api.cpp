@@ -454,11 +454,17 @@ kda_status_t kda_chunk_bwd_workspace_size(const kda_fwd_desc_t* desc, int has_se
   return KDA_OK;
 }
 
-kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
-                           const void* beta, const float* initial_state, const int32_t* segment_ids,
-                           const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
-                           float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The backward; `rerun` keeps the chunk records and states a previous call
+// left in the workspace and runs only the reverse recurrence and the
+// per-chunk gradients again.
+kda_status_t backward(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, const float* initial_state, const int32_t* segment_ids, const void* d_o,
+                      const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                      float* d_initial_state, void* workspace, size_t workspace_bytes, void* stream, bool rerun) {
   const bool has_seg = segment_ids != nullptr;
   BwdPlan bp;
   kda_status_t st = bwd_validate(desc, has_seg, &bp);
@@ -500,7 +506,7 @@ kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void
   if (d.T == 0) {
     zero(d_initial_state, bp.t.smax * slot_elems);
   } else {
-    if (has_seg) {
+    if (has_seg && !rerun) {
       // padding tokens, unrecorded segments and absent state slots keep zero gradients
       e = observed("kda_prep", s, [&] { return kda::launch_prep(t); });
       const int64_t tok = d.B * d.T * d.H;
@@ -533,11 +539,88 @@ kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void
     a.dds = reinterpret_cast<float*>(ws + bp.off_dds);
     a.stream = s;
     static const char* const names[4] = {"kda_bwd_chunk", "kda_bwd_states", "kda_bwd_dstates", "kda_bwd_local"};
-    for (int stage = 0; stage < 4 && e == hipSuccess; ++stage)
+    for (int stage = rerun ? 2 : 0; stage < 4 && e == hipSuccess; ++stage)
       e = observed(names[stage], s, [&] { return kda::launch_bwd(a, stage); });
   }
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const float* initial_state, const int32_t* segment_ids,
+                           const void* d_o, const float* d_final_state, float* dq, float* dk, float* dv, float* dg,
+                           float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return backward(desc, q, k, v, g, beta, initial_state, segment_ids, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                  d_initial_state, workspace, workspace_bytes, stream, false);
+}
+
+kda_status_t kda_chunk_bwd_rerun(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* initial_state,
+                                 const int32_t* segment_ids, const void* d_o, const float* d_final_state, float* dq,
+                                 float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return backward(desc, q, k, v, g, beta, initial_state, segment_ids, d_o, d_final_state, dq, dk, dv, dg, dbeta,
+                  d_initial_state, workspace, workspace_bytes, stream, true);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+kda_status_t kda_cp_gather_final_grads(const kda_cp_desc_t* desc, const int32_t* plan, const float* d_final_state,
+                                       const float* carry_grad, float* local_d_final, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0 || desc->H == 0) return KDA_OK;
+  if (!plan || !local_d_final) return fail(KDA_ERR_INVALID_ARGUMENT, "plan and local_d_final must be non-NULL");
+  if (!all_aligned16({plan, d_final_state, carry_grad, local_d_final}))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.plan = const_cast<int32_t*>(plan);
+  a.init = d_final_state;
+  a.carry = const_cast<float*>(carry_grad);
+  a.local = local_d_final;
+  a.grads = true;
+  return cp_launch("kda_cp_gather", a.stream, kda::launch_cp_gather, a);
+}
+
+kda_status_t kda_cp_chain_bwd(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_d_initial,
+                              const float* transition, float* carry_grad, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0 || desc->H == 0) return KDA_OK;
+  if (!plan || !local_d_initial || !transition || !carry_grad)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "plan, local_d_initial, transition and carry_grad must be non-NULL");
+  if (!all_aligned16({plan, local_d_initial, transition, carry_grad}))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.plan = const_cast<int32_t*>(plan);
+  a.local = const_cast<float*>(local_d_initial);
+  a.trans = transition;
+  a.carry = carry_grad;
+  return cp_launch("kda_cp_chain_bwd", a.stream, kda::launch_cp_chain_bwd, a);
+}
+
+kda_status_t kda_cp_scatter_initial_grads(const kda_cp_desc_t* desc, const int32_t* plan,
+                                          const float* local_d_initial, float* d_initial_state, void* stream) {
+  kda_status_t st = cp_validate(desc);
+  if (st != KDA_OK) return st;
+  if (desc->B == 0 || desc->H == 0) return KDA_OK;
+  if (!plan || !local_d_initial || !d_initial_state)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "plan, local_d_initial and d_initial_state must be non-NULL");
+  if (!all_aligned16({plan, local_d_initial, d_initial_state}))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 16-byte aligned");
+  kda::CpArgs a = cp_args(desc, stream);
+  a.plan = const_cast<int32_t*>(plan);
+  a.local = const_cast<float*>(local_d_initial);
+  a.fin = d_initial_state;
+  a.grads = true;
+  return cp_launch("kda_cp_scatter", a.stream, kda::launch_cp_scatter, a);
 }
 
 }  // extern "C"

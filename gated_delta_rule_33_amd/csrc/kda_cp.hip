@@ -78,20 +78,24 @@ __global__ __launch_bounds__(kPlanThreads) void cp_plan_kernel(const int32_t* __
 
 constexpr int kCopyThreads = 256;
 
-// One workgroup per (slice, local segment, head) state: the start state of
-// the slice's local segment l for a pass.  The carried segment takes the
-// chain's state (zero in pass 1), any other the caller's state of the
-// segment's global index; unused slots get zero.
+// One workgroup per (slice, local segment, head) state.  Start states (not
+// ends): the slice's local segment l starts from the chain's state if the
+// slice continues it (zero when carry is NULL), else from the caller's state
+// of its global segment.  Final-state gradients (ends): the slice's last
+// local segment, when the next slice continues it, takes the chain's
+// gradient (zero when carry is NULL); any other takes the caller's gradient
+// of its global segment.  Unused slots get zero.
 __global__ __launch_bounds__(kCopyThreads) void cp_gather_kernel(const int32_t* __restrict__ plan,
                                                                  const float* __restrict__ init,
                                                                  const float* __restrict__ carry,
                                                                  float* __restrict__ local, int P, int nm, int64_t H,
-                                                                 int64_t KV) {
+                                                                 int64_t KV, int ends) {
   const int64_t id = blockIdx.x;
-  const int64_t h = id % H, l = (id / H) % nm, rho = id / (H * nm), b = rho / P;
+  const int64_t h = id % H, l = (id / H) % nm, rho = id / (H * nm), b = rho / P, r = rho % P;
   const int32_t* e = plan + rho * 4;
   const float* src = nullptr;
-  if (l == 0 && e[0]) {
+  const bool chained = ends ? (l == e[2] - 1 && r + 1 < P && plan[(rho + 1) * 4] != 0) : (l == 0 && e[0] != 0);
+  if (chained) {
     src = carry ? carry + (rho * H + h) * KV : nullptr;
   } else if (l < e[2] && e[1] + l < nm && init != nullptr) {
     src = init + ((b * nm + e[1] + l) * H + h) * KV;
@@ -102,16 +106,18 @@ __global__ __launch_bounds__(kCopyThreads) void cp_gather_kernel(const int32_t* 
 }
 
 // One workgroup per (row, global segment slot, head): the final state of
-// global segment s is the one of the last slice that holds it; slots of
+// global segment s is the one of the last slice that holds it (the gradient
+// of its initial state, with `first`, the one of the first slice); slots of
 // segments that do not occur get zero.
 __global__ __launch_bounds__(kCopyThreads) void cp_scatter_kernel(const int32_t* __restrict__ plan,
                                                                   const float* __restrict__ local,
                                                                   float* __restrict__ fin, int P, int nm, int64_t H,
-                                                                  int64_t KV) {
+                                                                  int64_t KV, int first) {
   const int64_t id = blockIdx.x;
   const int64_t h = id % H, s = (id / H) % nm, b = id / (H * nm);
   const float* src = nullptr;
-  for (int r = P - 1; r >= 0; --r) {
+  for (int i = 0; i < P; ++i) {
+    const int r = first ? i : P - 1 - i;
     const int32_t* e = plan + (b * P + r) * 4;
     if (e[1] <= s && s < e[1] + e[2]) {
       const int64_t l = s - e[1];
@@ -186,6 +192,63 @@ __global__ __launch_bounds__(kChainThreads) void cp_chain_kernel(const int32_t* 
   }
 }
 
+// The reverse chain for the gradients: X_r, the gradient of the state that
+// leaves slice r, is zero for the last slice and, going back,
+//     X_r = [slice r+1 continues] (dInit_{r+1} + M_{r+1}^T X_{r+1}),
+// where dInit_{r+1} is the gradient the slice's own backward found for the
+// state its continued segment starts from (with a zero gradient for the state
+// it hands on) and M_{r+1} its transition.  Same tiling as the forward chain.
+template <int K>
+__global__ __launch_bounds__(kChainThreads) void cp_chain_bwd_kernel(const int32_t* __restrict__ plan,
+                                                                     const float* __restrict__ dinit,
+                                                                     const float* __restrict__ trans,
+                                                                     float* __restrict__ xg, int P, int nm, int64_t H,
+                                                                     int64_t V) {
+  constexpr int OPT = K * kChainCols / kChainThreads;
+  constexpr int TPR = kChainCols / OPT;
+  __shared__ float cur[K][kChainCols];
+  const int64_t ntile = V / kChainCols;
+  const int64_t id = blockIdx.x;
+  const int64_t tile = id % ntile, h = (id / ntile) % H, b = id / (ntile * H);
+  const int tid = threadIdx.x, row = tid / TPR, c0 = (tid % TPR) * OPT;
+  const int64_t v0 = tile * kChainCols;
+  const int64_t KV = (int64_t)K * V;
+  auto x_at = [&](int r) { return xg + ((b * P + r) * H + h) * KV + (int64_t)row * V + v0 + c0; };
+#pragma unroll
+  for (int j = 0; j < OPT; ++j) {
+    cur[row][c0 + j] = 0.f;
+    x_at(P - 1)[j] = 0.f;
+  }
+  __syncthreads();
+  for (int r = P - 2; r >= 0; --r) {
+    const int64_t nx = b * P + r + 1;
+    float acc[OPT];
+    if (plan[nx * 4] != 0) {
+      // dInit of the continued segment (local segment 0 of slice r+1) ...
+      const float* D = dinit + ((nx * nm) * H + h) * KV + (int64_t)row * V + v0 + c0;
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) acc[j] = D[j];
+      // ... plus M^T X_{r+1}: column `row` of M
+      const float* M = trans + (nx * H + h) * (int64_t)K * K + row;
+      for (int k = 0; k < K; ++k) {
+        const float mk = M[(int64_t)k * K];
+#pragma unroll
+        for (int j = 0; j < OPT; ++j) acc[j] += mk * cur[k][c0 + j];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < OPT; ++j) acc[j] = 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OPT; ++j) {
+      cur[row][c0 + j] = acc[j];
+      x_at(r)[j] = acc[j];
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 hipError_t launch_cp_plan(const CpArgs& a) {
@@ -197,14 +260,27 @@ hipError_t launch_cp_plan(const CpArgs& a) {
 hipError_t launch_cp_gather(const CpArgs& a) {
   const int64_t n = a.B * a.P * a.nm * a.H;
   hipLaunchKernelGGL(cp_gather_kernel, dim3((unsigned)n), dim3(kCopyThreads), 0, a.stream, a.plan, a.init, a.carry,
-                     a.local, a.P, a.nm, a.H, a.K * a.V);
+                     a.local, a.P, a.nm, a.H, a.K * a.V, a.grads ? 1 : 0);
   return hipGetLastError();
 }
 
 hipError_t launch_cp_scatter(const CpArgs& a) {
   const int64_t n = a.B * a.nm * a.H;
   hipLaunchKernelGGL(cp_scatter_kernel, dim3((unsigned)n), dim3(kCopyThreads), 0, a.stream, a.plan, a.local, a.fin,
-                     a.P, a.nm, a.H, a.K * a.V);
+                     a.P, a.nm, a.H, a.K * a.V, a.grads ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_cp_chain_bwd(const CpArgs& a) {
+  const dim3 grid((unsigned)(a.B * a.H * (a.V / kChainCols)));
+  if (a.K == 64)
+    hipLaunchKernelGGL(cp_chain_bwd_kernel<64>, grid, dim3(kChainThreads), 0, a.stream, a.plan, a.local, a.trans,
+                       a.carry, a.P, a.nm, a.H, a.V);
+  else if (a.K == 128)
+    hipLaunchKernelGGL(cp_chain_bwd_kernel<128>, grid, dim3(kChainThreads), 0, a.stream, a.plan, a.local, a.trans,
+                       a.carry, a.P, a.nm, a.H, a.V);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

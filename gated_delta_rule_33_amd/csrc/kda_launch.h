@@ -77,6 +77,7 @@ struct CpArgs {
   float* local;               // [B*P,nm,H,K,V] per-slice states (gather: out; chain, scatter: in)
   const float* trans;         // [B*P,H,K,K] (chain)
   float* fin;                 // [B,nm,H,K,V] (scatter: out)
+  bool grads;                 // gather: final-state gradients; scatter: initial-state gradients (first slice)
   hipStream_t stream;
 };
 
@@ -117,6 +118,7 @@ hipError_t launch_cp_plan(const CpArgs& a);
 hipError_t launch_cp_gather(const CpArgs& a);
 hipError_t launch_cp_chain(const CpArgs& a);
 hipError_t launch_cp_scatter(const CpArgs& a);
+hipError_t launch_cp_chain_bwd(const CpArgs& a);
 int cu_count();
 
 }  // namespace kda

@@ -22,7 +22,8 @@ KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 
 EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_transition",
-            "kda_chunk_bwd_workspace_size", "kda_chunk_bwd",
+            "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_chunk_bwd_rerun", "kda_cp_gather_final_grads",
+            "kda_cp_chain_bwd", "kda_cp_scatter_initial_grads",
             "kda_chunk_fwd_rerun", "kda_cp_plan", "kda_cp_gather_states", "kda_cp_chain", "kda_cp_scatter_states",
             "kda_short_conv_fwd", "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer",
             "kda_last_error", "kda_version")
@@ -77,12 +78,18 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(KdaFwdDesc)] + [p] * 16 + [sz, p]
     lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd_rerun.argtypes = lib.kda_chunk_bwd.argtypes
+    lib.kda_chunk_bwd_rerun.restype = ctypes.c_int
     cpd = ctypes.POINTER(KdaCpDesc)
     lib.kda_cp_plan.argtypes = [cpd, p, p, p]
     lib.kda_cp_gather_states.argtypes = [cpd, p, p, p, p, p]
     lib.kda_cp_chain.argtypes = [cpd, p, p, p, p, p]
     lib.kda_cp_scatter_states.argtypes = [cpd, p, p, p, p]
-    for f in (lib.kda_cp_plan, lib.kda_cp_gather_states, lib.kda_cp_chain, lib.kda_cp_scatter_states):
+    lib.kda_cp_gather_final_grads.argtypes = [cpd, p, p, p, p, p]
+    lib.kda_cp_chain_bwd.argtypes = [cpd, p, p, p, p, p]
+    lib.kda_cp_scatter_initial_grads.argtypes = [cpd, p, p, p, p]
+    for f in (lib.kda_cp_plan, lib.kda_cp_gather_states, lib.kda_cp_chain, lib.kda_cp_scatter_states,
+              lib.kda_cp_gather_final_grads, lib.kda_cp_chain_bwd, lib.kda_cp_scatter_initial_grads):
         f.restype = ctypes.c_int
     i64, i32 = ctypes.c_int64, ctypes.c_int32
     lib.kda_short_conv_fwd.argtypes = [i64, i64, i64, i32, i32, p, p, p, p, p]
@@ -502,7 +509,9 @@ class CpCall:
         self.workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         self.views = [t.view((rows, L) + tuple(t.shape[2:])) for t in (q, k, v, g, beta)]
         self.keep = (q, k, v, g, beta, initial_state, segment_ids)
+        self.packed, self.gshape, self.lshape, self.dev = packed, gshape, lshape, dev
         seg_local = segment_ids.view(rows, L) if packed else None
+        self.seg_local = seg_local
         stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
         cp, d, ws = ctypes.byref(self.cp), ctypes.byref(self.desc), (_ptr(self.workspace), ctypes.c_size_t(ws_bytes))
         lib = load_library()
@@ -525,6 +534,56 @@ class CpCall:
     def enqueue(self):
         for fn, args in self.steps:
             _raise_for(fn(*args), fn.__name__)
+
+    def backward(self, d_o, d_final_state=None, want_d_initial_state=True):
+        """The gradients of sum(o * d_o) + sum(final_state * d_final_state)
+        under the same slicing, after enqueue(): each slice's backward, the
+        reverse chain of hand-off gradients, the backward again on the same
+        workspace.  Returns fp32 (dq, dk, dv, dg, dbeta, d_initial_state)."""
+        import torch
+        q, k, v, g, beta, init, _ = self.keep
+        B, T, H, K = q.shape
+        V = v.shape[-1]
+        rows, L = self.desc.B, self.desc.T
+        if tuple(d_o.shape) != (B, T, H, V) or not d_o.is_contiguous():
+            raise ValueError("d_o must be a contiguous [B,T,H,V] tensor")
+        if d_final_state is not None and (d_final_state.dtype != torch.float32 or not d_final_state.is_contiguous()
+                                          or tuple(d_final_state.shape) != self.gshape):
+            raise ValueError(f"d_final_state must be a contiguous float32 {self.gshape} tensor")
+        lib = load_library()
+        stream = ctypes.c_void_p(torch.cuda.current_stream(self.dev).cuda_stream)
+        f32 = dict(dtype=torch.float32, device=self.dev)
+        desc = make_desc(rows, L, H, K, V, self.desc.dtype, _dtype_code(d_o.dtype), self.desc.scale,
+                         bool(self.desc.use_qk_l2norm), False, None, self.desc.max_segments)
+        n = ctypes.c_size_t(0)
+        _raise_for(lib.kda_chunk_bwd_workspace_size(ctypes.byref(desc), int(self.packed), ctypes.byref(n)),
+                   "kda_chunk_bwd_workspace_size")
+        ws = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=self.dev)
+        dq, dk, dg = (torch.empty((B, T, H, K), **f32) for _ in range(3))
+        dv = torch.empty((B, T, H, V), **f32)
+        dbeta = torch.empty((B, T, H), **f32)
+        local_dfin = torch.empty(self.lshape, **f32)
+        local_dinit = torch.empty(self.lshape, **f32)
+        xg = torch.empty((rows, H, K, V), **f32)
+        cp, plan = ctypes.byref(self.cp), _ptr(self.plan)
+        grads = [_ptr(t.view((rows, L) + tuple(t.shape[2:]))) for t in (dq, dk, dv, dg, dbeta)]
+        bwd_args = (ctypes.byref(desc), *[_ptr(t) for t in self.views], _ptr(self.local_init), _ptr(self.seg_local),
+                    _ptr(d_o.view(rows, L, H, V)), _ptr(local_dfin), *grads, _ptr(local_dinit), _ptr(ws),
+                    ctypes.c_size_t(ws.numel()), stream)
+        _raise_for(lib.kda_cp_gather_final_grads(cp, plan, _ptr(d_final_state), None, _ptr(local_dfin), stream),
+                   "kda_cp_gather_final_grads")
+        _raise_for(lib.kda_chunk_bwd(*bwd_args), "kda_chunk_bwd")
+        _raise_for(lib.kda_cp_chain_bwd(cp, plan, _ptr(local_dinit), _ptr(self.transition), _ptr(xg), stream),
+                   "kda_cp_chain_bwd")
+        _raise_for(lib.kda_cp_gather_final_grads(cp, plan, _ptr(d_final_state), _ptr(xg), _ptr(local_dfin), stream),
+                   "kda_cp_gather_final_grads")
+        _raise_for(lib.kda_chunk_bwd_rerun(*bwd_args), "kda_chunk_bwd_rerun")
+        d_init = None
+        if want_d_initial_state:
+            d_init = torch.empty(self.gshape, **f32)
+            _raise_for(lib.kda_cp_scatter_initial_grads(cp, plan, _ptr(local_dinit), _ptr(d_init), stream),
+                       "kda_cp_scatter_initial_grads")
+        return dq, dk, dv, dg, dbeta, d_init
 
 
 def chunk_kda_cp(q, k, v, g, beta, cp_size: int, scale: Optional[float] = None, initial_state=None,

@@ -163,6 +163,23 @@ kda_status_t kda_chunk_bwd(const kda_fwd_desc_t* desc,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_bwd again on a workspace that a kda_chunk_bwd call with the same
+ * desc, inputs and gradient buffers filled: the chunk quantities and the
+ * forward states do not depend on the cotangents, so only the reverse state
+ * recurrence and the per-chunk gradients run, for new d_o / d_final_state.
+ * Positions the first call zeroed (padding tokens, absent slots) are not
+ * written again.  The second backward pass of a context-parallel rank.
+ */
+kda_status_t kda_chunk_bwd_rerun(const kda_fwd_desc_t* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* initial_state, const int32_t* segment_ids,
+                                 const void* d_o, const float* d_final_state,
+                                 float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                                 float* d_initial_state,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * The forward, plus each row's transition: the recurrence is affine in the
  * state the row's first segment starts from, so the state after the row's
  * last token is  M * S_start + (that state for S_start = 0),  with M the
@@ -276,6 +293,47 @@ kda_status_t kda_cp_chain(const kda_cp_desc_t* desc, const int32_t* plan, const 
  */
 kda_status_t kda_cp_scatter_states(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_final,
                                    float* final_state, void* stream);
+
+/*
+ * The backward under the same slicing (the pages' CP gradient equivalence):
+ * each slice's backward (kda_chunk_bwd on the slice rows, with the start
+ * states of the forward's step 5) needs the gradient of the state it hands
+ * on, which the next slice's backward produces.  In order:
+ *   1. kda_cp_gather_final_grads   per-slice final-state gradients, carry_grad
+ *                                  = NULL (a handed-on state gets zero).
+ *   2. kda_chunk_bwd               on the slices: local initial-state gradients.
+ *   3. kda_cp_chain_bwd            X_r = [slice r+1 continues]
+ *                                  (dInit_{r+1} + M_{r+1}^T X_{r+1}), X_{P-1} = 0.
+ *   4. kda_cp_gather_final_grads   with carry_grad = X.
+ *   5. kda_chunk_bwd_rerun         on the same workspace: exact gradients.
+ *   6. kda_cp_scatter_initial_grads  per-segment initial-state gradients,
+ *                                  global layout (from the slice where each
+ *                                  segment starts).
+ * Across GPUs step 3 is P-1 point-to-point hops of one state gradient, from
+ * the last rank back.
+ *
+ * local_d_final [B*P,n_states,H,K,V]: slot l of slice (b, r) gets, for the
+ * slice's last local segment when slice r+1 continues it, carry_grad[b*P + r]
+ * (zero if carry_grad is NULL), else d_final_state of its global segment
+ * (zero if d_final_state is NULL); unused slots get zero.
+ */
+kda_status_t kda_cp_gather_final_grads(const kda_cp_desc_t* desc, const int32_t* plan, const float* d_final_state,
+                                       const float* carry_grad, float* local_d_final, void* stream);
+/*
+ * carry_grad [B*P,H,K,V]: X_r above (zero for the last slice and for slices
+ * whose last token does not continue into the next).  local_d_initial
+ * [B*P,n_states,H,K,V] is the d_initial_state of step 2 and transition
+ * [B*P,H,K,K] the forward's.  Accumulates in fp32.
+ */
+kda_status_t kda_cp_chain_bwd(const kda_cp_desc_t* desc, const int32_t* plan, const float* local_d_initial,
+                              const float* transition, float* carry_grad, void* stream);
+/*
+ * d_initial_state [B,n_states,H,K,V]: each segment's initial-state gradient,
+ * taken from the first slice that holds it; slots of segments that do not
+ * occur get zero.  local_d_initial is the d_initial_state of step 5.
+ */
+kda_status_t kda_cp_scatter_initial_grads(const kda_cp_desc_t* desc, const int32_t* plan,
+                                          const float* local_d_initial, float* d_initial_state, void* stream);
 
 /*
  * Short convolution, the layer step that q, k and v each pass through before

@@ -176,6 +176,40 @@ def test_cp_steps_reject_before_any_launch():
         kda.KDA_ERR_INVALID_ARGUMENT
     assert lib.kda_cp_scatter_states(ctypes.byref(cp(V=32)), fake, fake, fake, None) == kda.KDA_ERR_NOT_IMPLEMENTED
     assert lib.kda_cp_scatter_states(ctypes.byref(d), fake, None, fake, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    # the backward's glue
+    assert lib.kda_cp_gather_final_grads(ctypes.byref(d), fake, None, None, None, None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_cp_gather_final_grads(ctypes.byref(cp(P=3)), fake, None, None, fake, None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT                                   # T not a multiple of P
+    assert lib.kda_cp_chain_bwd(ctypes.byref(d), fake, fake, None, fake, None) == kda.KDA_ERR_INVALID_ARGUMENT
+    assert lib.kda_cp_scatter_initial_grads(ctypes.byref(cp(K=32)), fake, fake, fake, None) == \
+        kda.KDA_ERR_NOT_IMPLEMENTED
+    assert lib.kda_cp_scatter_initial_grads(ctypes.byref(d), fake, fake, ctypes.c_void_p(0x1004), None) == \
+        kda.KDA_ERR_INVALID_ARGUMENT
+
+
+def test_backward_rejects_before_any_launch():
+    lib = kda.load_library()
+    d = _desc()
+    fake = ctypes.c_void_p(0x1000)
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(d), 0, ctypes.byref(n)) == kda.KDA_OK and n.value > 0
+    assert lib.kda_chunk_bwd_workspace_size(ctypes.byref(_desc(K=96)), 0, ctypes.byref(n)) == \
+        kda.KDA_ERR_NOT_IMPLEMENTED
+    args = lambda **kw: [kw.get(x, fake) for x in ("q", "k", "v", "g", "beta")] + \
+        [kw.get("init"), kw.get("seg"), kw.get("d_o", fake), kw.get("d_fin")] + \
+        [kw.get(x, fake) for x in ("dq", "dk", "dv", "dg", "dbeta")] + [kw.get("d_init")]
+    for fn in (lib.kda_chunk_bwd, lib.kda_chunk_bwd_rerun):
+        # a missing gradient buffer
+        assert fn(ctypes.byref(d), *args(dg=None), fake, ctypes.c_size_t(1 << 40), None) == kda.KDA_ERR_INVALID_ARGUMENT
+        # a misaligned cotangent
+        assert fn(ctypes.byref(d), *args(d_o=ctypes.c_void_p(0x1008)), fake, ctypes.c_size_t(1 << 40), None) == \
+            kda.KDA_ERR_INVALID_ARGUMENT
+        # too small a workspace
+        assert fn(ctypes.byref(d), *args(), fake, ctypes.c_size_t(64), None) == kda.KDA_ERR_WORKSPACE_TOO_SMALL
+        # packed without a segment bound
+        assert fn(ctypes.byref(d), *args(seg=fake), fake, ctypes.c_size_t(1 << 40), None) == \
+            kda.KDA_ERR_INVALID_ARGUMENT
 
 
 def test_python_wrapper_rejects_unsupported_options():

@@ -206,3 +206,59 @@ def test_cp_full_size_sampled_heads(P):
     _say(f"[cp] full P={P} o rel err (heads {heads}) {e:.3e}")
     e = check(f"full P={P} final", fin[:, heads], fin_ref, TOL_BF16)
     _say(f"[cp] full P={P} final rel err {e:.3e}")
+
+
+def _cp_backward(inp, w, P, seed):
+    """Forward and backward through CpCall; returns (grads, oracle grads)."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    d = to_device(inp, w.dtype)
+    call = kda.CpCall(d["q"], d["k"], d["v"], d["g"], d["beta"], P, scale=inp["scale"],
+                      initial_state=d["initial_state"], output_final_state=True,
+                      use_qk_l2norm_in_kernel=w.l2norm_in_kernel, safe_gate=w.safe_gate, lower_bound=w.lower_bound,
+                      segment_ids=d["segment_ids"],
+                      N_max=inp["max_segments"] if d["segment_ids"] is not None else None)
+    call.enqueue()
+    rng = np.random.default_rng(seed)
+    d_o = rng.standard_normal((w.B, w.T, w.H, w.V)).astype(np.float32)
+    shape = call.gshape
+    d_fin = rng.standard_normal(shape).astype(np.float32)
+    out = call.backward(torch.from_numpy(d_o).cuda(), torch.from_numpy(d_fin).cuda())
+    torch.cuda.synchronize()
+    names = ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state")
+    got = {n: t.cpu().numpy().astype(np.float64) for n, t in zip(names, out)}
+    ref = oracle.kda_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], d_o, scale=inp["scale"],
+                              initial_state=inp["initial_state"], d_final_state=d_fin,
+                              use_qk_l2norm=w.l2norm_in_kernel, segment_ids=inp["segment_ids"],
+                              max_segments=inp["max_segments"])
+    return got, ref
+
+
+@pytest.mark.parametrize("P", [2, 4])
+@pytest.mark.parametrize("case", [FIXED[0], FIXED[2]], ids=lambda c: c[0].name)
+def test_cp_backward_fixed_rows_match_the_unsplit_oracle(case, P):
+    """CP gradient equivalence (the pages' CP gradient test): the gradients
+    through P slices equal the unsplit backward."""
+    w, g_scale = case
+    _say(f"[cp-bwd] {w.name} P={P}")
+    got, ref = _cp_backward(_inputs(w, g_scale), w, P, 120 + P)
+    for n in got:
+        e = check(f"{w.name} P={P} {n}", got[n], ref[n], _tol(w))
+        _say(f"[cp-bwd] {w.name} P={P} {n} rel err {e:.3e}")
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_cp_backward_packed_segments_match_the_unsplit_oracle(P):
+    """Segments crossing cuts, beginning at a cut, spanning every slice."""
+    T = 1024
+    w = Workload("cp_bwd_bf16_packed", "bf16", 3, T, 2, 128, 128, initial_state=True, final_state=True,
+                 max_segments=8, seed=130 + P)
+    seg = _packed_ids(P, T)
+    _say(f"[cp-bwd] {w.name} P={P}")
+    got, ref = _cp_backward(_inputs(w, 0.02, segment_ids=seg), w, P, 140 + P)
+    pad = seg == 0
+    for n in got:
+        if n != "d_initial_state":
+            assert np.all(got[n][pad] == 0.0)
+        e = check(f"{w.name} P={P} {n}", got[n], ref[n], TOL_BF16)
+        _say(f"[cp-bwd] {w.name} P={P} {n} rel err {e:.3e}")

@@ -197,3 +197,83 @@ def test_chaining_reproduces_the_unsplit_run(P):
     # the oracle takes start states in fp32, so each carried state is rounded once
     assert oracle.rel_err(oc, o) < 1e-6
     assert oracle.rel_err(fc, fin) < 1e-6
+
+
+def _cp_bwd_run(q, k, v, g, beta, seg, S0, d_o, d_fin, n_states, P):
+    """The gradient chaining written out with the oracle alone: the slices'
+    start states come from the forward chain; each slice's backward first
+    runs with a zero gradient for the state it hands on, the reverse chain
+    X_r = [r+1 continues] (dInit_{r+1} + M_{r+1}^T X_{r+1}) gives the true
+    hand-off gradients, and a second backward of each slice uses them."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    L = T // P
+    plan = cp.cp_plan(seg, B, T, P, n_states)
+    out = {n: np.zeros(a.shape) for n, a in (("dq", q), ("dk", k), ("dv", v), ("dg", g), ("dbeta", beta))}
+    d_init = np.zeros((B, n_states, H, K, V))
+    for b in range(B):
+        # forward chain: the state each continued slice starts from
+        carries = [np.zeros((H, K, V)) for _ in range(P)]
+        for r in range(P - 1):
+            cont, first, count, _ = plan[b, r]
+            sl = slice(r * L, (r + 1) * L)
+            local = np.zeros((1, max(count, 1), H, K, V))
+            for l in range(count):
+                local[0, l] = carries[r] if (l == 0 and cont) else (S0[b, first + l] if S0 is not None else 0.0)
+            args = [a[b:b + 1, sl] for a in (q, k, v, g, beta)]
+            _, fl = oracle.kda_forward(*args, initial_state=local.astype(np.float32), output_final_state=True,
+                                       segment_ids=seg[b:b + 1, sl], max_segments=max(count, 1))
+            if plan[b, r + 1, 0]:
+                carries[r + 1] = fl[0, count - 1]
+
+        def slice_bwd(r, x_out):
+            cont, first, count, _ = plan[b, r]
+            sl = slice(r * L, (r + 1) * L)
+            local = np.zeros((1, max(count, 1), H, K, V))
+            dfl = np.zeros((1, max(count, 1), H, K, V))
+            for l in range(count):
+                local[0, l] = carries[r] if (l == 0 and cont) else (S0[b, first + l] if S0 is not None else 0.0)
+                handed_on = l == count - 1 and r + 1 < P and plan[b, r + 1, 0]
+                dfl[0, l] = x_out if handed_on else d_fin[b, first + l]
+            args = [a[b:b + 1, sl] for a in (q, k, v, g, beta)]
+            gr = oracle.kda_backward(*args, d_o[b:b + 1, sl], initial_state=local.astype(np.float32),
+                                     d_final_state=dfl, segment_ids=seg[b:b + 1, sl], max_segments=max(count, 1))
+            M = cp.transition(args[1], args[3], args[4], segment_ids=seg[b:b + 1, sl])[0]
+            return gr, M, sl, first, count, cont
+
+        # pass 1 and the reverse chain
+        X = [np.zeros((H, K, V)) for _ in range(P)]
+        for r in range(P - 1, 0, -1):
+            gr, M, _, _, _, cont = slice_bwd(r, np.zeros((H, K, V)))   # pass 1: nothing handed on
+            if cont:
+                X[r - 1] = gr["d_initial_state"][0, 0] + np.swapaxes(M, -1, -2) @ X[r]
+        # pass 2
+        for r in range(P):
+            gr, _, sl, first, count, cont = slice_bwd(r, X[r])
+            for n in out:
+                out[n][b, sl] = gr[n][0]
+            for l in range(count):
+                if not (l == 0 and cont):
+                    d_init[b, first + l] = gr["d_initial_state"][0, l]
+    out["d_initial_state"] = d_init
+    return out
+
+
+@pytest.mark.parametrize("P", [2, 4])
+def test_gradient_chaining_reproduces_the_unsplit_backward(P):
+    """CP gradient equivalence, the pages' check, on the oracle."""
+    B, T, H, K, V = 2, 32, 2, 6, 5
+    q, k, v, g, beta = _case(B, T, H, K, V, 70)
+    seg = np.zeros((B, T), np.int32)
+    seg[0, 0:5], seg[0, 5:19], seg[0, 19:24], seg[0, 24:31] = 1, 2, 3, 4
+    seg[1, 0:8], seg[1, 9:32] = 1, 2
+    n_states = 5
+    S0 = _rand((B, n_states, H, K, V), 71, 0.5).astype(np.float32)
+    d_o = _rand((B, T, H, V), 72)
+    d_fin = _rand((B, n_states, H, K, V), 73)
+    ref = oracle.kda_backward(q, k, v, g, beta, d_o, initial_state=S0, d_final_state=d_fin, segment_ids=seg,
+                              max_segments=n_states)
+    got = _cp_bwd_run(q, k, v, g, beta, seg, S0, d_o, d_fin, n_states, P)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "d_initial_state"):
+        # the oracle takes start states in fp32, so each carried state is rounded once
+        assert oracle.rel_err(got[n], ref[n]) < 1e-5, n
