@@ -25,14 +25,16 @@
 // for any 16-row span up to 64, which leaves a wide margin below FLT_MAX for
 // the sums these factors enter, so every product splits at the chunk's first
 // row; a chunk with a larger span (possible only at the edge of the safe
-// gate's [-5, 0), or without it) takes exp(G_r - G_i) per element.  The result does not depend on
-// the chunk size.  Everything is fp32 (bf16 inputs are exact in fp32).
+// gate's [-5, 0), or without it) takes exp(G_r - G_i) per element.  The
+// result does not depend on the chunk size.  Everything is fp32 (bf16 inputs
+// are exact in fp32), the products on fp32 matrix-core tiles.
 //
 // Kernels, in order: bwd_chunk (one workgroup per chunk and head: G, A, Aqk,
 // T, W, U, Kt, Qg into a chunk record), bwd_states (the forward recurrence
-// again, keeping the state entering every chunk), bwd_dstates (the reverse
-// recurrence, keeping dS' of every chunk and the initial-state gradients),
-// bwd_local (one workgroup per chunk and head: all input gradients).
+// again, keeping the state entering and Delta of every chunk), bwd_dstates
+// (the reverse recurrence, keeping dS' and dDelta of every chunk and the
+// initial-state gradients), bwd_local (one workgroup per chunk and head: all
+// input gradients).
 #include "kda_launch.h"
 
 namespace kda {
