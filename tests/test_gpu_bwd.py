@@ -176,3 +176,50 @@ def test_backward_full_size_sampled_heads(name):
         g = np.take(got[n], heads, axis=ax) if n == "d_initial_state" else got[n][:, :, heads]
         e = check(f"{name} {n}", g, ref[n], TOL_BF16)
         _say(f"[bwd] {name} {n} rel err (heads {heads}) {e:.3e}")
+
+
+def test_backward_empty_and_padding_only_inputs():
+    """T = 0: every initial-state gradient is zero (fixed and packed); a row of
+    padding only gets zero gradients everywhere and zero state gradients."""
+    import torch
+    from gated_delta_rule_33_amd import kda
+    for seg in (None, torch.zeros((1, 0), dtype=torch.int32, device="cuda")):
+        z = torch.zeros((1, 0, 2, 64), dtype=torch.float32, device="cuda")
+        zb = torch.zeros((1, 0, 2), dtype=torch.float32, device="cuda")
+        out = kda.chunk_kda_bwd(z, z, z, z, zb, z, segment_ids=seg, N_max=2 if seg is not None else None)
+        torch.cuda.synchronize()
+        d_init = out[5]
+        assert d_init.shape == ((1, 2, 64, 64) if seg is None else (1, 2, 2, 64, 64)) and torch.all(d_init == 0)
+    w = Workload("bwd_pad_rows", "f32", 2, 40, 2, 64, 64, initial_state=True, final_state=True, max_segments=2,
+                 seed=150)
+    seg = np.zeros((2, 40), np.int32)
+    seg[1, 3:20] = 1
+    seg[1, 20:40] = 2
+    inp = make_inputs(w, segment_ids=seg)
+    d_o, d_fin = _cotangents(inp, w, 12)
+    got = _run_gpu(inp, w, d_o, d_fin)
+    ref = _run_oracle(inp, w, d_o, d_fin)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.all(got[n][0] == 0.0)
+    assert np.all(got["d_initial_state"][0] == 0.0)
+    _compare(w.name, got, ref, w)
+
+
+def test_backward_segments_past_the_bound_get_zero_gradients():
+    """A row with more segments than N_max: the forward gives the excess
+    segments o = 0, so their tokens' gradients are zero; the recorded
+    segments are unaffected (compared with a run that stops at the bound)."""
+    w = Workload("bwd_overflow", "f32", 1, 64, 2, 64, 64, final_state=True, max_segments=2, seed=151)
+    seg = np.repeat(np.arange(1, 5, dtype=np.int32), 16)[None]        # four segments, bound two
+    inp = make_inputs(w, segment_ids=seg)
+    d_o, d_fin = _cotangents(inp, w, 13)
+    got = _run_gpu(inp, w, d_o, d_fin)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert np.all(got[n][:, 32:] == 0.0)
+    sub = {k_: (v_[:, :32] if isinstance(v_, np.ndarray) and v_.ndim >= 2 and v_.shape[:2] == (1, 64) else v_)
+           for k_, v_ in inp.items()}
+    ref = oracle.kda_backward(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], d_o[:, :32], scale=inp["scale"],
+                              d_final_state=d_fin, segment_ids=seg[:, :32], max_segments=2)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        check(f"overflow {n}", got[n][:, :32], ref[n], TOL_F32)
+    check("overflow d_initial_state", got["d_initial_state"], ref["d_initial_state"], TOL_F32)
