@@ -610,13 +610,15 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   const float* hS = p.hs + (slot * p.H + h) * K * V;
   const float* dhS = p.dhs + (slot * p.H + h) * K * V;
   __shared__ __align__(16) float sG[kBC][K], sk[kBC][K], sq[kBC][K];
-  __shared__ __align__(16) float sVG[kBC * MX];        // v [16][V], later dG [16][K]
-  __shared__ __align__(16) float sBig[3 * kBC * MX];   // dO, Delta, dDelta [16][V]; later dW, dKt, dQg [16][K]
+  __shared__ __align__(16) float sVG[kBC * MX];        // v [16][V], then the dT partials, then dG [16][K]
+  __shared__ __align__(16) float sOW[kBC * MX];        // dO [16][V], later dW [16][K]
   __shared__ __align__(16) float sT[kBC][kBC], sAqk[kBC][kBC], sdA[kBC][kBC], sdAqk[kBC][kBC], sdT[kBC][kBC];
   __shared__ __align__(16) float sX[kBC][kBC];
   // Per-wave partial sums (one writer each), combined in wave order: no
   // atomics, so every run adds in the same order.
-  __shared__ float sdgc[K], sred[4][kBC][4], sdTp[4][kBC][kBC];
+  __shared__ float sdgc[K], sred[4][kBC][4];
+  static_assert(4 * kBC * kBC <= kBC * MX, "the dT partials fit v's buffer");
+  float (*sdTp)[kBC][kBC] = reinterpret_cast<float (*)[kBC][kBC]>(sVG);
   __shared__ float sbeta[kBC], snq[kBC], snk[kBC];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = 4 * (lane >> 4), n = lane & 15;
   const TI* q = static_cast<const TI*>(p.q);
@@ -628,9 +630,11 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   const int len = si.len, last = len - 1;
   auto tok = [&](int row) { return (si.b * p.T + si.t0 + row) * p.H + h; };
   float* sv = sVG;
-  float* sdO = sBig;
-  float* sD = sBig + kBC * V;
-  float* sdD = sBig + 2 * kBC * V;
+  float* sdO = sOW;
+  // Delta and dDelta of the chunk, as the recurrences left them (rows past
+  // the chunk are zero), read as operands straight from memory
+  const float* sD = p.ds + (slot * p.H + h) * kBC * V;
+  const float* sdD = p.dds + (slot * p.H + h) * kBC * V;
 
   // ---- inputs
   for (int e = tid; e < kBC * K; e += kBThreads) {
@@ -647,7 +651,6 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
   sT[tid / kBC][tid % kBC] = rec[R::kT + tid];
   sAqk[tid / kBC][tid % kBC] = rec[R::kAqk + tid];
   for (int e = tid; e < 4 * kBC * 4; e += kBThreads) (&sred[0][0][0])[e] = 0.f;
-  for (int e = tid; e < 4 * kBC * kBC; e += kBThreads) (&sdTp[0][0][0])[e] = 0.f;
   if (tid < kBC) sbeta[tid] = tid < len ? ld(beta, tok(tid)) : 0.f;
   __syncthreads();
   {
@@ -668,17 +671,6 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
     if (cc == 0) {
       snq[r] = nq;
       snk[r] = nk;
-    }
-  }
-  __syncthreads();
-
-  // ---- Delta and dDelta of the chunk, as the recurrences left them
-  {
-    const float* gD = p.ds + (slot * p.H + h) * kBC * V;
-    const float* gdD = p.dds + (slot * p.H + h) * kBC * V;
-    for (int e = tid; e < kBC * V / 4; e += kBThreads) {
-      reinterpret_cast<f32x4*>(sD)[e] = reinterpret_cast<const f32x4*>(gD)[e];
-      reinterpret_cast<f32x4*>(sdD)[e] = reinterpret_cast<const f32x4*>(gdD)[e];
     }
   }
   __syncthreads();
@@ -733,19 +725,14 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  float* sdW = sBig;
-  float* sdKt = sBig + kBC * K;
-  float* sdQg = sBig + 2 * kBC * K;
+  // dW goes through LDS (its transposes are needed); dKt and dQg stay in the
+  // registers of the lanes that use them
+  float* sdW = sOW;
   for (int u = 0; u < 2; ++u) {
     const int cb = wave + 4 * u;
     if (cb >= NKB) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int idx = (g4 + i) * K + 16 * cb + n;
-      sdW[idx] = -cW[u][i];
-      sdKt[idx] = cKt[u][i];
-      sdQg[idx] = p.scale * cQ[u][i];
-    }
+    for (int i = 0; i < 4; ++i) sdW[(g4 + i) * K + 16 * cb + n] = -cW[u][i];
   }
   __syncthreads();
 
@@ -837,16 +824,20 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
       }
     }
     const float GC = sG[last][c];
+    // the last row's G_C terms: sum over the chunk's rows of dKt * Kt (this
+    // lane holds rows 4g .. 4g+3 of channel c; the four lane groups add up),
+    // and d Gamma_C Gamma_C
     float lastx = 0.f;
-    if (last >= g4 && last < g4 + 4) {
-      for (int x = 0; x < kBC; ++x) lastx += sdKt[x * K + c] * rec[R::kKt + x * K + c];
-      lastx += sdgc[c] * __expf(GC);
-    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lastx += cKt[u][i] * rec[R::kKt + (g4 + i) * K + c];
+    lastx += __shfl_xor(lastx, 16);
+    lastx += __shfl_xor(lastx, 32);
+    lastx += sdgc[c] * __expf(GC);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = g4 + i;
       const float G = sG[r][c], e = __expf(G), ec = __expf(GC - G), kh = sk[r][c], qh = sq[r][c], br = sbeta[r];
-      const float dQg = sdQg[r * K + c], dKt = sdKt[r * K + c], dKb = cKb[i];
+      const float dQg = p.scale * cQ[u][i], dKt = cKt[u][i], dKb = cKb[i];
       dqh[u][i] = dQg * e + RAq[i];
       dkh[u][i] = dKb * br * e + dKt * ec + br * RA[i] + CA[i] + CAq[i];
       pb[i] += kh * e * dKb + kh * RA[i];
