@@ -177,7 +177,6 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   BSlot si;
   if (!slot_info(p, slot, &si)) return;
   __shared__ __align__(16) float sk[kBC][K], sq[kBC][K], sG[kBC][K], sv[kBC][V];
-  __shared__ __align__(16) float skf[kBC][K], skb[kBC][K], sqf[kBC][K];
   __shared__ __align__(16) float sA[kBC][kBC], sP1[kBC][kBC], sP2[kBC][kBC], sT[kBC][kBC];
   __shared__ float sbeta[kBC];
   __shared__ int s_unsafe;
@@ -233,10 +232,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   const int last = si.len - 1;
   for (int e = tid; e < kBC * K; e += kBThreads) {
     const int r = e / K, c = e % K;
-    const float G = sG[r][c], G0 = sG[0][c], GC = sG[last][c];
-    skf[r][c] = sk[r][c] * __expf(G - G0);
-    skb[r][c] = unsafe ? 0.f : sk[r][c] * __expf(G0 - G);
-    sqf[r][c] = sq[r][c] * __expf(G - G0);
+    const float G = sG[r][c], GC = sG[last][c];
     rec[R::kG + e] = G;
     rec[R::kKt + e] = sk[r][c] * __expf(GC - G);
     rec[R::kQg + e] = sq[r][c] * __expf(G);
@@ -247,9 +243,20 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
     // wave 0: A, wave 1: Aqk (contraction over K)
     f32x4 c = {0, 0, 0, 0};
     if (!unsafe) {
-      const float* left = wave == 0 ? &skf[0][0] : &sqf[0][0];
+      // operands formed on the fly: left = (k | q) exp(G - G_0), right kb = k exp(G_0 - G)
+      const float* left = wave == 0 ? &sk[0][0] : &sq[0][0];
 #pragma unroll 4
-      for (int s = 0; s < NKB; ++s) mma16(c, opa(left, K, 0, 16 * s, lane), opa(&skb[0][0], K, 0, 16 * s, lane));
+      for (int s = 0; s < NKB; ++s) {
+        const f32x4 x = opa(left, K, 0, 16 * s, lane), kk = opa(&sk[0][0], K, 0, 16 * s, lane);
+        const f32x4 gr = opa(&sG[0][0], K, 0, 16 * s, lane), g0 = opa(&sG[0][0], 0, 0, 16 * s, lane);
+        f32x4 a, b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          a[j] = x[j] * __expf(gr[j] - g0[j]);
+          b[j] = kk[j] * __expf(g0[j] - gr[j]);
+        }
+        mma16(c, a, b);
+      }
     } else {
       const float* left = wave == 0 ? &sk[0][0] : &sq[0][0];
 #pragma unroll
