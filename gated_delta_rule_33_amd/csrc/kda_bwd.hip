@@ -42,8 +42,7 @@ namespace {
 
 constexpr int kBC = 16;            // rows per backward chunk
 constexpr int kBThreads = 256;
-constexpr int kRecThreads = 320;   // the recurrences: four compute waves and an L2 prefetch wave
-constexpr int kBAhead = 4;         // chunks the prefetch wave runs ahead
+constexpr int kRecThreads = 320;   // the recurrences: four compute waves and a wave filling their operand ring
 constexpr float kSpanMax = 64.f;   // exp(64) ~ 6e27: room for sums of O(1e10) below FLT_MAX
 
 // Chunk record (floats) per (slot, head).
@@ -345,62 +344,117 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   if (tid == 0) rec[R::kInfo] = unsafe ? 1.f : 0.f;
 }
 
-// ---------------------------------------------------------------- bwd_states
-// One workgroup (four waves) per (sequence, head, 16 value columns): the
-// state from the initial state through every chunk, writing the state that
-// enters each chunk.  The 16-column state is K/16 accumulator tiles; wave w
-// holds tiles w, w + 4 (rows 16 cb ..), which are also the B operands of its
-// slabs of W S.  Per chunk: each wave's partial W S goes through LDS (double
-// buffered, one barrier), every wave sums the four in the same order into
-// Delta = U - W S, and updates its tiles S <- diag(Gamma_C) S + Kt^T Delta.
-// The chunk record's operands are loaded one chunk ahead.
-template <int K, int V>
-struct StatesOps {
-  static constexpr int TPW = K / 64;   // state tiles per wave
-  f32x4 w[TPW], kt[TPW], gc[TPW], u;
-  __device__ void load(const float* rec, int wave, int lane, int tile) {
-    using R = BRec<K, V>;
-#pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int cb = wave + 4 * t;
-      w[t] = opa(rec + R::kW, K, 0, 16 * cb, lane);      // W[r][16 cb + 4g + j]
-      kt[t] = opb(rec + R::kKt, K, 0, 16 * cb, lane);    // (Kt^T)[16 cb + n][4g + j]
-      gc[t] = *reinterpret_cast<const f32x4*>(rec + R::kGc + 16 * cb + 4 * (lane >> 4));
-    }
-    const float* up = rec + R::kU + (int64_t)(4 * (lane >> 4)) * V + tile * kBC + (lane & 15);
-    u = f32x4{up[0], up[V], up[2 * V], up[3 * V]};
-  }
-};
+// ------------------------------------------------- recurrence operand ring
+// The recurrences read each chunk's operands from an LDS image that the
+// workgroup's fifth wave fills with direct-to-LDS loads LEAD chunks ahead,
+// so the compute waves issue no global loads in their loop.  Images of
+// [16][K] operands store 16-byte unit u of row r at unit u ^ (r & 15): the
+// fragment reads (a row of four columns per lane, or four rows of one column
+// per lane group) then fall on distinct banks.
+__device__ __forceinline__ int swz(int r, int u) { return u ^ (r & 15); }
 
-// The fifth wave of a recurrence workgroup touches this workgroup's 1/NV
-// share of the record kBAhead chunks ahead (one 16-byte direct-to-LDS load
-// per 64-byte segment, into a sink), so that the compute waves' loads find
-// it in L2.  It meets the compute waves at every barrier.
-template <int K, int V, class RecFn, class ExtraFn>
-__device__ void prefetch_wave(RecFn rec, ExtraFn extra, int64_t n16, bool reverse, int tile, int lane, char* sink) {
-  using R = BRec<K, V>;
-  constexpr int NV = V / kBC;
-  constexpr int SEGS = (int)(R::kFloats * 4 / 64), SHARE = (SEGS + NV - 1) / NV;
-  auto touch = [&](int64_t c) {
-    const char* r = reinterpret_cast<const char*>(rec(reverse ? n16 - 1 - c : c));
+// One wave: rows 0..15 of a row-major [16][K] fp32 operand into an image.
+template <int K>
+__device__ __forceinline__ void dma_rows(float* dst, const float* src, int lane) {
+  constexpr int UPR = K / 4;   // 16-byte units per row
 #pragma unroll
-    for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
-      const int e = i * kWave + lane, seg = tile * SHARE + e;
-      if (e < SHARE && seg < SEGS) dma16(sink, r + 64 * (int64_t)seg);
-    }
-    extra(reverse ? n16 - 1 - c : c);
-  };
-  for (int64_t c = 0; c < kBAhead && c < n16; ++c) touch(c);
-  for (int64_t c = 0; c < n16; ++c) {
-    if (c + kBAhead < n16) touch(c + kBAhead);
+  for (int i = 0; i < K / 16; ++i) {
+    const int pos = 64 * i + lane, r = pos / UPR;
+    dma16(dst + 256 * i, src + r * K + 4 * swz(r, pos % UPR));
+  }
+}
+// One wave: a [16][16] fp32 block (row stride ld) into a plain [16][16] image.
+__device__ __forceinline__ void dma_block16(float* dst, const float* src, int ld, int lane) {
+  dma16(dst, src + (lane >> 2) * ld + 4 * (lane & 3));
+}
+// Fragments of an image: A operand of X (16 x K image), rows 0..15, k = 16 cb
+// + 4g + j; and B operand of X (k = 4g + j, columns 16 cb ..), i.e. the A
+// operand of X^T.
+template <int K>
+__device__ __forceinline__ f32x4 img_opa(const float* X, int cb, int lane) {
+  const int n = lane & 15;
+  return *reinterpret_cast<const f32x4*>(X + n * K + 4 * swz(n, 4 * cb + (lane >> 4)));
+}
+template <int K>
+__device__ __forceinline__ f32x4 img_opb(const float* X, int cb, int lane) {
+  const int n = lane & 15, g4 = 4 * (lane >> 4);
+  f32x4 x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) x[j] = X[(g4 + j) * K + 4 * swz(g4 + j, 4 * cb + (n >> 2)) + (n & 3)];
+  return x;
+}
+
+// Allow n (0 .. LEAD - 1, wave-uniform) chunks of PER direct loads each to
+// stay outstanding.
+template <int PER, int LEAD>
+__device__ __forceinline__ void wait_chunks(int64_t n) {
+  static_assert(LEAD >= 2 && LEAD <= 4 && (LEAD - 1) * PER < 64, "vmcnt is six bits");
+  if constexpr (LEAD >= 4) {
+    if (n >= 3) return vm_wait<3 * PER>();
+  }
+  if constexpr (LEAD >= 3) {
+    if (n >= 2) return vm_wait<2 * PER>();
+  }
+  if (n >= 1) vm_wait<PER>();
+  else vm_wait<0>();
+}
+
+// The fifth wave: issue(c) loads chunk c's image into slot c % LEAD.  Chunk
+// c + 1 is complete before barrier c (the compute waves read it right after),
+// and chunk c + LEAD is issued after it, into the slot of chunk c, which no
+// wave reads past barrier c.  One barrier precedes the loop (chunk 0 ready).
+template <int PER, int LEAD, class IssueFn>
+__device__ void ring_fill(IssueFn issue, int64_t n) {
+  for (int64_t c = 0; c < LEAD && c < n; ++c) issue(c);
+  wait_chunks<PER, LEAD>(min<int64_t>(LEAD, n) - 1);
+  block_sync();
+  for (int64_t c = 0; c < n; ++c) {
+    wait_chunks<PER, LEAD>(max<int64_t>(0, min<int64_t>(c + LEAD, n) - (c + 2)));
     block_sync();
+    if (c + LEAD < n) issue(c + LEAD);
   }
   vm_wait<0>();
 }
 
+// ---------------------------------------------------------------- bwd_states
+// One workgroup (four compute waves and the ring's wave) per (sequence, head,
+// 16 value columns): the state from the initial state through every chunk,
+// writing the state that enters each chunk.  The 16-column state is K/16
+// accumulator tiles; wave w holds tiles w, w + 4 (rows 16 cb ..), which are
+// also the B operands of its slabs of W S.  Per chunk: each wave's partial
+// W S goes through LDS (double buffered, one barrier), every wave sums the
+// four in the same order into Delta = U - W S, and updates its tiles
+// S <- diag(Gamma_C) S + Kt^T Delta.  Operands of chunk c + 1 are read from
+// the ring into registers right after barrier c.
+template <int K, int V>
+struct StatesImg {
+  float w[kBC * K], kt[kBC * K], gc[K], u[kBC * kBC];
+  static constexpr int kPer = 2 * (K / 16) + 2;   // direct loads per image
+  static constexpr int kLead = 4;                 // images in flight (ring slots)
+};
+
+template <int K, int V>
+struct StatesOps {
+  static constexpr int TPW = K / 64;   // state tiles per wave
+  f32x4 w[TPW], kt[TPW], gc[TPW], u;
+  __device__ void load(const StatesImg<K, V>& m, int wave, int lane) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int cb = wave + 4 * t;
+      w[t] = img_opa<K>(m.w, cb, lane);                  // W[n][16 cb + 4g + j]
+      kt[t] = img_opb<K>(m.kt, cb, lane);                // (Kt^T)[16 cb + n][4g + j]
+      gc[t] = *reinterpret_cast<const f32x4*>(m.gc + 16 * cb + 4 * (lane >> 4));
+    }
+    const int g4 = 4 * (lane >> 4), n = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = m.u[(g4 + i) * kBC + n];
+  }
+};
+
 template <int K, int V>
 __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
   using R = BRec<K, V>;
+  using Img = StatesImg<K, V>;
   using Ops = StatesOps<K, V>;
   constexpr int NV = V / kBC, TPW = Ops::TPW;
   // The NV workgroups of one (sequence, head) get ids of equal id % 8, which
@@ -410,13 +464,21 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
   const int64_t sh = (id / (8 * NV)) * 8 + id % 8, h = sh % p.H, sq = sh / p.H;
   BSeq s;
   if (!seq_info(p, sq, h, &s)) return;
+  __shared__ __align__(16) Img ring[Img::kLead];
   __shared__ __align__(16) float sP[2][4][kBC][kBC];
-  __shared__ __align__(16) char s_sink[1024];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
-  auto rec = [&](int64_t c) { return p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats; };
   if (wave == 4) {
-    prefetch_wave<K, V>(rec, [](int64_t) {}, s.n16, false, tile, lane, s_sink);
+    ring_fill<Img::kPer, Img::kLead>(
+        [&](int64_t c) {
+          Img& m = ring[c % Img::kLead];
+          const float* r = p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats;
+          dma_rows<K>(m.w, r + R::kW, lane);
+          dma_rows<K>(m.kt, r + R::kKt, lane);
+          if (lane < K / 4) dma16(m.gc, r + R::kGc + 4 * lane);   // lane 0 always issues: kPer loads
+          dma_block16(m.u, r + R::kU + tile * kBC, V, lane);
+        },
+        s.n16);
     return;
   }
   f32x4 st[TPW];
@@ -425,11 +487,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       st[t][i] = p.init ? p.init[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n] : 0.f;
-  // Operands two chunks ahead in three register sets that rotate by name
-  // (the loop is unrolled by three), so no set is copied while its loads are
-  // in flight.
-  auto step = [&](int64_t c, const Ops& cur, Ops& fill) {
-    if (c + 2 < s.n16) fill.load(rec(c + 2), wave, lane, tile);
+  auto step = [&](int64_t c, const Ops& cur, Ops& next) {
     float* hs = p.hs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC + n;
     f32x4 d = {0, 0, 0, 0};
 #pragma unroll
@@ -447,6 +505,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
       delta[i] = cur.u[i] - (sP[buf][0][g4 + i][n] + sP[buf][1][g4 + i][n] + sP[buf][2][g4 + i][n] +
                              sP[buf][3][g4 + i][n]);
+    if (c + 1 < s.n16) next.load(ring[(c + 1) % Img::kLead], wave, lane);
     if (wave == 0) {
       float* dst = p.ds + ((s.slot0 + c) * p.H + h) * kBC * V + tile * kBC + n;
 #pragma unroll
@@ -461,48 +520,59 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
       st[t] = x;
     }
   };
-  Ops o0, o1, o2;
-  o0.load(rec(0), wave, lane, tile);
-  if (s.n16 > 1) o1.load(rec(1), wave, lane, tile);
-  for (int64_t c = 0; c < s.n16; c += 3) {
-    step(c, o0, o2);
+  Ops o0, o1;
+  block_sync();
+  if (s.n16 > 0) o0.load(ring[0], wave, lane);
+  for (int64_t c = 0; c < s.n16; c += 2) {
+    step(c, o0, o1);
     if (c + 1 < s.n16) step(c + 1, o1, o0);
-    if (c + 2 < s.n16) step(c + 2, o2, o1);
   }
 }
 
 // ---------------------------------------------------------------- bwd_dstates
-// One workgroup (four waves) per (sequence, head, 16 value columns): dS'
-// from the final state's gradient back through every chunk, writing dS' of
-// each chunk and the gradient of the sequence's initial state.  Same tiling
-// as bwd_states: per chunk the waves' partial Kt dS' (and scale Aqk^T dO,
-// added by wave 0) are summed into dDelta through LDS, then each wave updates
-// its tiles dS = diag(Gamma_C) dS' + scale Qg^T dO - W^T dDelta.
+// One workgroup (four compute waves and the ring's wave) per (sequence, head,
+// 16 value columns): dS' from the final state's gradient back through every
+// chunk, writing dS' of each chunk and the gradient of the sequence's
+// initial state.  Same tiling as bwd_states: per chunk the waves' partial
+// Kt dS' (and scale Aqk^T dO, added by wave 0) are summed into dDelta through
+// LDS, then each wave updates its tiles dS = diag(Gamma_C) dS' + scale Qg^T dO
+// - W^T dDelta.  The ring holds the chunk's Kt, Qg, W, Gamma_C, Aqk and the
+// workgroup's 16 columns of the chunk's dO rows.
+template <class TO, int K, int V>
+struct DStatesImg {
+  float kt[kBC * K], qg[kBC * K], w[kBC * K], gc[K], aq[kBC * kBC];
+  TO dout[kBC * kBC];
+  static constexpr int kPer = 3 * (K / 16) + 3;
+  static constexpr int kLead = 3;
+};
+
 template <int K, int V>
 struct DStatesOps {
   static constexpr int TPW = K / 64;
   f32x4 kt[TPW], qgt[TPW], wt[TPW], gc[TPW], aq, dout;
   template <class TO>
-  __device__ void load(const float* rec, const TO* dorow, int64_t stride, int len, int wave, int lane, int tile) {
-    using R = BRec<K, V>;
+  __device__ void load(const DStatesImg<TO, K, V>& m, int len, int wave, int lane) {
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int cb = wave + 4 * t;
-      kt[t] = opa(rec + R::kKt, K, 0, 16 * cb, lane);    // Kt[r][16 cb + 4g + j]
-      qgt[t] = opb(rec + R::kQg, K, 0, 16 * cb, lane);   // (Qg^T)[16 cb + n][4g + j]
-      wt[t] = opb(rec + R::kW, K, 0, 16 * cb, lane);     // (W^T)[16 cb + n][4g + j]
-      gc[t] = *reinterpret_cast<const f32x4*>(rec + R::kGc + 16 * cb + 4 * (lane >> 4));
+      kt[t] = img_opa<K>(m.kt, cb, lane);                // Kt[n][16 cb + 4g + j]
+      qgt[t] = img_opb<K>(m.qg, cb, lane);               // (Qg^T)[16 cb + n][4g + j]
+      wt[t] = img_opb<K>(m.w, cb, lane);                 // (W^T)[16 cb + n][4g + j]
+      gc[t] = *reinterpret_cast<const f32x4*>(m.gc + 16 * cb + 4 * (lane >> 4));
     }
-    aq = opb(rec + R::kAqk, kBC, 0, 0, lane);              // (Aqk^T)[n][4g + j]
     const int g4 = 4 * (lane >> 4), n = lane & 15;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dout[j] = g4 + j < len ? ld(dorow, (g4 + j) * stride + tile * kBC + n) : 0.f;
+    for (int j = 0; j < 4; ++j) {
+      aq[j] = m.aq[(g4 + j) * kBC + n];                    // (Aqk^T)[n][4g + j]
+      dout[j] = g4 + j < len ? ld(m.dout, (g4 + j) * kBC + n) : 0.f;
+    }
   }
 };
 
 template <class TO, int K, int V>
 __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
   using R = BRec<K, V>;
+  using Img = DStatesImg<TO, K, V>;
   using Ops = DStatesOps<K, V>;
   constexpr int NV = V / kBC, TPW = Ops::TPW;
   // The NV workgroups of one (sequence, head) get ids of equal id % 8, which
@@ -512,20 +582,33 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
   const int64_t sh = (id / (8 * NV)) * 8 + id % 8, h = sh % p.H, sq = sh / p.H;
   BSeq s;
   if (!seq_info(p, sq, h, &s)) return;
+  __shared__ __align__(16) Img ring[Img::kLead];
   __shared__ __align__(16) float sP[2][4][kBC][kBC];
-  __shared__ __align__(16) char s_sink[1024];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
   const TO* d_o = static_cast<const TO*>(p.d_o);
   const int64_t seq_len = p.packed ? p.segs[sq].len : p.T;
+  // Step m handles chunk n16 - 1 - m.
+  auto chunk_len = [&](int64_t c) { return (int)min<int64_t>(kBC, seq_len - c * kBC); };
   if (wave == 4) {
-    // records, and this workgroup's 16 columns of the chunk's d_o rows
-    auto rec = [&](int64_t c) { return p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats; };
-    auto rows = [&](int64_t c) {
-      if (lane < kBC && c * kBC + lane < seq_len)
-        dma16(s_sink, d_o + ((s.b * p.T + s.t0 + c * kBC + lane) * p.H + h) * V + tile * kBC);
-    };
-    prefetch_wave<K, V>(rec, rows, s.n16, true, tile, lane, s_sink);
+    ring_fill<Img::kPer, Img::kLead>(
+        [&](int64_t m) {
+          Img& im = ring[m % Img::kLead];
+          const int64_t c = s.n16 - 1 - m;
+          const float* r = p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats;
+          dma_rows<K>(im.kt, r + R::kKt, lane);
+          dma_rows<K>(im.qg, r + R::kQg, lane);
+          dma_rows<K>(im.w, r + R::kW, lane);
+          if (lane < K / 4) dma16(im.gc, r + R::kGc + 4 * lane);
+          dma_block16(im.aq, r + R::kAqk, kBC, lane);
+          // 16 columns of each present dO row: 64 / (16 B per lane) lanes a row
+          constexpr int LPR = kBC * (int)sizeof(TO) / 16;
+          const int row = lane / LPR;
+          if (row < chunk_len(c))   // row 0 always present: every chunk issues kPer loads
+            dma16(im.dout, d_o + ((s.b * p.T + s.t0 + c * kBC + row) * p.H + h) * V + tile * kBC +
+                               (lane % LPR) * (16 / (int)sizeof(TO)));
+        },
+        s.n16);
     return;
   }
   f32x4 st[TPW];
@@ -535,15 +618,8 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
       st[t][i] = p.d_final ? p.d_final[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n]
                            : 0.f;
-  auto load = [&](Ops& o, int64_t c) {
-    const int len = (int)min<int64_t>(kBC, seq_len - c * kBC);
-    const TO* row = d_o + ((s.b * p.T + s.t0 + c * kBC) * p.H + h) * V;
-    o.load(p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats, row, p.H * V, len, wave, lane, tile);
-  };
-  // Operands two chunks ahead in three rotating register sets, as above.
-  auto step = [&](int64_t m, const Ops& cur, Ops& fill) {
+  auto step = [&](int64_t m, const Ops& cur, Ops& next) {
     const int64_t c = s.n16 - 1 - m;
-    if (c > 1) load(fill, c - 2);
     float* dhs = p.dhs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC + n;
     f32x4 d = {0, 0, 0, 0};
 #pragma unroll
@@ -566,6 +642,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       dd[i] = sP[buf][0][g4 + i][n] + sP[buf][1][g4 + i][n] + sP[buf][2][g4 + i][n] + sP[buf][3][g4 + i][n];
+    if (m + 1 < s.n16) next.load(ring[(m + 1) % Img::kLead], chunk_len(c - 1), wave, lane);
     if (wave == 0) {
       float* dst = p.dds + ((s.slot0 + c) * p.H + h) * kBC * V + tile * kBC + n;
 #pragma unroll
@@ -580,13 +657,12 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
       for (int i = 0; i < 4; ++i) st[t][i] = cur.gc[t][i] * st[t][i] + p.scale * a[i] - b[i];
     }
   };
-  Ops o0, o1, o2;
-  load(o0, s.n16 - 1);
-  if (s.n16 > 1) load(o1, s.n16 - 2);
-  for (int64_t m = 0; m < s.n16; m += 3) {
-    step(m, o0, o2);
+  Ops o0, o1;
+  block_sync();
+  if (s.n16 > 0) o0.load(ring[0], chunk_len(s.n16 - 1), wave, lane);
+  for (int64_t m = 0; m < s.n16; m += 2) {
+    step(m, o0, o1);
     if (m + 1 < s.n16) step(m + 1, o1, o0);
-    if (m + 2 < s.n16) step(m + 2, o2, o1);
   }
   if (p.d_init)
 #pragma unroll
