@@ -429,8 +429,8 @@ kda_status_t bwd_validate(const kda_fwd_desc_t* d, bool has_seg, BwdPlan* bp) {
   const size_t slots = 4 * (size_t)b.t.cmax, H = (size_t)d->H;
   b.off_rec = b.t.off_records;
   size_t off = align_up(b.off_rec + slots * H * (size_t)kda::bwd_record_floats(d->K, d->V) * sizeof(float));
-  b.off_hs = off;
-  off = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
+  b.off_hs = off;   // the state entering every 64-token chunk
+  off = align_up(off + (size_t)b.t.cmax * H * (size_t)(d->K * d->V) * sizeof(float));
   b.off_dhs = off;
   off = align_up(off + slots * H * (size_t)(d->K * d->V) * sizeof(float));
   b.off_ds = off;

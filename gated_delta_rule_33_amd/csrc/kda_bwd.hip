@@ -35,6 +35,7 @@
 // (the reverse recurrence, keeping dS' and dDelta of every chunk and the
 // initial-state gradients), bwd_local (one workgroup per chunk and head: all
 // input gradients).
+#include <type_traits>
 #include "kda_launch.h"
 
 namespace kda {
@@ -72,7 +73,7 @@ struct BwdParams {
   const float *init, *d_final;
   float *dq, *dk, *dv, *dg, *dbeta, *d_init;
   float* rec;                   // [slots][H][BRec::kFloats]
-  float* hs;                    // [slots][H][K][V] state entering each chunk
+  float* hs;                    // [slots / 4][H][K][V] state entering each 64-token chunk
   float* dhs;                   // [slots][H][K][V] dL/d(state leaving each chunk)
   float* ds;                    // [slots][H][16][V] Delta of each chunk
   float* dds;                   // [slots][H][16][V] dDelta of each chunk
@@ -98,7 +99,7 @@ __device__ bool slot_info(const BwdParams& p, int64_t slot, BSlot* s) {
     const int64_t per_row = 4 * p.nc64;
     s->b = slot / per_row;
     s->t0 = kBC * (slot % per_row);
-    if (s->t0 >= p.T) return false;
+    if (s->b >= p.B || s->t0 >= p.T) return false;
     s->len = (int)min<int64_t>(kBC, p.T - s->t0);
   }
   return true;
@@ -419,7 +420,8 @@ __device__ void ring_fill(IssueFn issue, int64_t n) {
 // ---------------------------------------------------------------- bwd_states
 // One workgroup (four compute waves and the ring's wave) per (sequence, head,
 // 16 value columns): the state from the initial state through every chunk,
-// writing the state that enters each chunk.  The 16-column state is K/16
+// writing the state that enters each 64-token chunk (the local kernel
+// rebuilds the three after it) and Delta of every chunk.  The 16-column state is K/16
 // accumulator tiles; wave w holds tiles w, w + 4 (rows 16 cb ..), which are
 // also the B operands of its slabs of W S.  Per chunk: each wave's partial
 // W S goes through LDS (double buffered, one barrier), every wave sums the
@@ -488,14 +490,16 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
       st[t][i] = p.init ? p.init[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n] : 0.f;
   auto step = [&](int64_t c, const Ops& cur, Ops& next) {
-    float* hs = p.hs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC + n;
+    if ((c & 3) == 0) {   // checkpoint: the state entering a 64-token chunk (slot0 is a multiple of 4)
+      float* hs = p.hs + (((s.slot0 + c) >> 2) * p.H + h) * K * V + tile * kBC + n;
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hs[(int64_t)(16 * (wave + 4 * t) + g4 + i) * V] = st[t][i];
+    }
     f32x4 d = {0, 0, 0, 0};
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) hs[(int64_t)(16 * (wave + 4 * t) + g4 + i) * V] = st[t][i];
-      mma16(d, cur.w[t], st[t]);
-    }
+    for (int t = 0; t < TPW; ++t) mma16(d, cur.w[t], st[t]);
     const int buf = (int)(c & 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sP[buf][wave][g4 + i][n] = d[i];
@@ -674,8 +678,10 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- bwd_local
 // One workgroup (four waves) per (chunk, head): every input gradient of the
-// chunk's rows.  Delta and dDelta come from the recurrences.  Phase B
-// (contraction over V; wave w takes key blocks w, w + 4, ...): dQg =
+// chunk's rows.  Delta and dDelta come from the recurrences; the state h
+// entering the chunk is rebuilt per 16x16 tile from the state entering its
+// 64-token chunk and the updates of the 16-token chunks before it there.
+// Phase B (contraction over V; wave w takes key blocks w, w + 4, ...): dQg =
 // scale dO h^T, dKt = Delta dh^T, dW = -dDelta h^T and d Gamma_C =
 // rowsum(dh * h); besides, wave 0 dAqk = scale dO Delta^T, wave 1
 // dT = dDelta Vb^T, waves 2-3 dVb = T^T dDelta (dv, and dbeta's V part).
@@ -683,14 +689,19 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
 // T^T dW and the exponent-factor sums of A and Aqk, assembled per (row,
 // channel) into dq, dk, dbeta and dG; dg = reverse in-chunk cumsum of dG.
 template <class TI, class TO, int K, int V>
-__global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
+__global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_local_kernel(BwdParams p) {
   using R = BRec<K, V>;
   constexpr int NKB = K / 16, NVB = V / 16, MX = K > V ? K : V;
+  // Chunk-major ids: the heads of one chunk are neighbours (their input rows
+  // are contiguous), and with H a multiple of 8 the four 16-token chunks of
+  // a (64-token chunk, head) land on one XCD, sharing the state they start
+  // from in its L2.
   const int64_t slot = blockIdx.x / p.H, h = blockIdx.x % p.H;
+  const int sub = (int)(slot & 3);   // the chunk's place in its 64-token chunk
   BSlot si;
   if (!slot_info(p, slot, &si)) return;
   const float* rec = p.rec + (slot * p.H + h) * R::kFloats;
-  const float* hS = p.hs + (slot * p.H + h) * K * V;
+  const float* hS = p.hs + ((slot >> 2) * p.H + h) * K * V;
   const float* dhS = p.dhs + (slot * p.H + h) * K * V;
   __shared__ __align__(16) float sG[kBC][K], sk[kBC][K], sq[kBC][K];
   __shared__ __align__(16) float sVG[kBC * MX];        // v [16][V], then the dT partials, then dG [16][K]
@@ -760,24 +771,77 @@ __global__ __launch_bounds__(kBThreads) void bwd_local_kernel(BwdParams p) {
 
   // ---- phase B: products over V
   // d Gamma_C = rowsum(dh * h) comes along: lane (g, n) holds h and dh of
-  // channel 16 cb + n, columns 16 s + 4g .. +3.
+  // channel 16 cb + n, columns 16 s + 4g .. +3.  That is also the
+  // accumulator layout of the h^T tile, so h is rebuilt there as
+  // h^T <- h^T diag(Gamma_C) + Delta^T Kt for each earlier 16-token chunk
+  // of the 64-token chunk, as the states kernel advanced it.
   f32x4 cQ[2], cKt[2], cW[2];
-  for (int u = 0; u < 2; ++u) {
-    const int cb = wave + 4 * u;
-    cQ[u] = cKt[u] = cW[u] = f32x4{0, 0, 0, 0};
-    if (cb >= NKB) continue;
-    float gsum = 0.f;
-#pragma unroll 2
-    for (int s = 0; s < NVB; ++s) {
-      const f32x4 bh = opa(hS, V, 16 * cb, 16 * s, lane), bdh = opa(dhS, V, 16 * cb, 16 * s, lane);
-      mma16(cQ[u], opa(sdO, V, 0, 16 * s, lane), bh);
-      mma16(cKt[u], opa(sD, V, 0, 16 * s, lane), bdh);
-      mma16(cW[u], opa(sdD, V, 0, 16 * s, lane), bh);
-      gsum += bh[0] * bdh[0] + bh[1] * bdh[1] + bh[2] * bdh[2] + bh[3] * bdh[3];
+  // One instance per number NE of earlier 16-token chunks in the 64-token
+  // chunk (0..3, wave-uniform), so each loads exactly the operands it uses
+  // and no branch sits between a load and its use.
+  auto phase_b = [&](auto ne_tag) {
+    constexpr int NE = decltype(ne_tag)::value, NA = NE > 0 ? NE : 1;
+    for (int u = 0; u < 2; ++u) {
+      const int cb = wave + 4 * u;
+      cQ[u] = cKt[u] = cW[u] = f32x4{0, 0, 0, 0};
+      if (cb >= NKB) continue;
+      // the earlier chunks' Kt and Gamma_C of this key block
+      f32x4 ktp[NA];
+      float gcp[NA];
+      const float* dsp[NA];
+#pragma unroll
+      for (int e = 0; e < NE; ++e) {
+        const int64_t se = slot - NE + e;
+        const float* r = p.rec + (se * p.H + h) * R::kFloats;
+        ktp[e] = opb(r + R::kKt, K, 0, 16 * cb, lane);      // Kt[4g + j][16 cb + n]
+        gcp[e] = r[R::kGc + 16 * cb + n];
+        dsp[e] = p.ds + (se * p.H + h) * kBC * V;
+      }
+      struct VOps {
+        f32x4 bh, bdh, d, dd, dl[NA];
+      };
+      auto load_v = [&](int s, VOps& o) {
+        o.bh = opa(hS, V, 16 * cb, 16 * s, lane);
+        o.bdh = opa(dhS, V, 16 * cb, 16 * s, lane);
+        o.d = opa(sD, V, 0, 16 * s, lane);
+        o.dd = opa(sdD, V, 0, 16 * s, lane);
+#pragma unroll
+        for (int e = 0; e < NE; ++e) o.dl[e] = opb(dsp[e], V, 0, 16 * s, lane);   // (Delta^T)[16 s + n][4g + j]
+      };
+      float gsum = 0.f;
+      auto use_v = [&](int s, const VOps& o) {
+        f32x4 bh = o.bh;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bh[i] *= gcp[e];
+          mma16(bh, o.dl[e], ktp[e]);
+        }
+        mma16(cQ[u], opa(sdO, V, 0, 16 * s, lane), bh);
+        mma16(cKt[u], o.d, o.bdh);
+        mma16(cW[u], o.dd, bh);
+        gsum += bh[0] * o.bdh[0] + bh[1] * o.bdh[1] + bh[2] * o.bdh[2] + bh[3] * o.bdh[3];
+      };
+      // value blocks in pairs, the next block's operands in flight (NVB is even)
+      VOps va, vb;
+      load_v(0, va);
+#pragma unroll 1
+      for (int s = 0; s < NVB; s += 2) {
+        load_v(s + 1, vb);
+        use_v(s, va);
+        if (s + 2 < NVB) load_v(s + 2, va);
+        use_v(s + 1, vb);
+      }
+      gsum += __shfl_xor(gsum, 16);
+      gsum += __shfl_xor(gsum, 32);
+      if (lane < 16) sdgc[16 * cb + n] = gsum;
     }
-    gsum += __shfl_xor(gsum, 16);
-    gsum += __shfl_xor(gsum, 32);
-    if (lane < 16) sdgc[16 * cb + n] = gsum;
+  };
+  switch (sub) {
+    case 0: phase_b(std::integral_constant<int, 0>{}); break;
+    case 1: phase_b(std::integral_constant<int, 1>{}); break;
+    case 2: phase_b(std::integral_constant<int, 2>{}); break;
+    default: phase_b(std::integral_constant<int, 3>{}); break;
   }
   if (wave == 0) {
     f32x4 c = {0, 0, 0, 0};

@@ -146,9 +146,9 @@ kda_status_t kda_chunk_fwd_gated(const kda_fwd_desc_t* desc,
  *                  with respect to a zero start state); slots of absent
  *                  segments get zero.
  *   workspace      at least kda_chunk_bwd_workspace_size() bytes (about
- *                  (K V / 8 + 4 K + 3 V) * 4 bytes per token and head: the
- *                  state and its gradient at every 16-token chunk, and the
- *                  chunk quantities).
+ *                  (5 K V / 64 + 4 K + 3 V) * 4 bytes per token and head: the
+ *                  state entering every 64-token chunk, its gradient at every
+ *                  16-token chunk, and the chunk quantities).
  * desc->use_qk_l2norm differentiates through the in-kernel L2 norm;
  * safe_gate and lower_bound play no part.  Errors as for kda_chunk_fwd.
  */
