@@ -417,6 +417,21 @@ __device__ void ring_fill(IssueFn issue, int64_t n) {
   vm_wait<0>();
 }
 
+// A wave stores an accumulator tile (lane (g, n) holding rows 4g + i, column
+// n) to a row-major matrix with row stride ld: through a padded LDS tile of
+// its own, so that each lane writes one 16-byte piece of a row (one
+// instruction instead of four).  Row stride 20 keeps both the scattered
+// writes and the 16-byte reads free of bank conflicts.
+constexpr int kTileLd = 20;
+__device__ __forceinline__ void store_tile(float* dst, int64_t ld, const f32x4& c, float* lds, int lane) {
+  const int g4 = 4 * (lane >> 4), n = lane & 15;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lds[(g4 + i) * kTileLd + n] = c[i];
+  const int r = lane >> 2, q4 = 4 * (lane & 3);
+  const f32x4 x = *reinterpret_cast<const f32x4*>(lds + r * kTileLd + q4);
+  *reinterpret_cast<f32x4*>(dst + r * ld + q4) = x;
+}
+
 // ---------------------------------------------------------------- bwd_states
 // One workgroup (four compute waves and the ring's wave) per (sequence, head,
 // 16 value columns): the state from the initial state through every chunk,
@@ -468,6 +483,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
   if (!seq_info(p, sq, h, &s)) return;
   __shared__ __align__(16) Img ring[Img::kLead];
   __shared__ __align__(16) float sP[2][4][kBC][kBC];
+  __shared__ __align__(16) float sX[4][TPW][kBC * kTileLd];   // per-wave store staging
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
   if (wave == 4) {
@@ -491,11 +507,9 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
       st[t][i] = p.init ? p.init[s.state * K * V + (int64_t)(16 * (wave + 4 * t) + g4 + i) * V + tile * kBC + n] : 0.f;
   auto step = [&](int64_t c, const Ops& cur, Ops& next) {
     if ((c & 3) == 0) {   // checkpoint: the state entering a 64-token chunk (slot0 is a multiple of 4)
-      float* hs = p.hs + (((s.slot0 + c) >> 2) * p.H + h) * K * V + tile * kBC + n;
+      float* hs = p.hs + (((s.slot0 + c) >> 2) * p.H + h) * K * V + tile * kBC;
 #pragma unroll
-      for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) hs[(int64_t)(16 * (wave + 4 * t) + g4 + i) * V] = st[t][i];
+      for (int t = 0; t < TPW; ++t) store_tile(hs + (int64_t)16 * (wave + 4 * t) * V, V, st[t], sX[wave][t], lane);
     }
     f32x4 d = {0, 0, 0, 0};
 #pragma unroll
@@ -588,6 +602,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
   if (!seq_info(p, sq, h, &s)) return;
   __shared__ __align__(16) Img ring[Img::kLead];
   __shared__ __align__(16) float sP[2][4][kBC][kBC];
+  __shared__ __align__(16) float sX[4][TPW][kBC * kTileLd];   // per-wave store staging
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
   const TO* d_o = static_cast<const TO*>(p.d_o);
@@ -624,12 +639,11 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
                            : 0.f;
   auto step = [&](int64_t m, const Ops& cur, Ops& next) {
     const int64_t c = s.n16 - 1 - m;
-    float* dhs = p.dhs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC + n;
+    float* dhs = p.dhs + ((s.slot0 + c) * p.H + h) * K * V + tile * kBC;
     f32x4 d = {0, 0, 0, 0};
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dhs[(int64_t)(16 * (wave + 4 * t) + g4 + i) * V] = st[t][i];
+      store_tile(dhs + (int64_t)16 * (wave + 4 * t) * V, V, st[t], sX[wave][t], lane);
       mma16(d, cur.kt[t], st[t]);
     }
     if (wave == 0) {
