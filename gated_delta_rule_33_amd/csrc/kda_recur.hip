@@ -111,6 +111,25 @@ __device__ __forceinline__ void store_out(uint16_t* o, int64_t i, float x) {
   const __bf16 h = to_bf16(x);
   __builtin_nontemporal_store(*reinterpret_cast<const uint16_t*>(&h), o + i);
 }
+// Four consecutive outputs o[i .. i + 3] (i a multiple of 4).
+__device__ __forceinline__ void store_out4(float* o, int64_t i, const f32x4& x) {
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(o + i));
+}
+__device__ __forceinline__ void store_out4(uint16_t* o, int64_t i, const f32x4& x) {
+  uint32_t w[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const __bf16 a = to_bf16(x[2 * j]), b = to_bf16(x[2 * j + 1]);
+    w[j] = (uint32_t)*reinterpret_cast<const uint16_t*>(&a) | ((uint32_t)*reinterpret_cast<const uint16_t*>(&b) << 16);
+  }
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(o + i));
+}
+// The output tile of a wave (lane (g, n) holding token rows 4g + i, column n)
+// goes through a padded LDS tile of its own, so each lane stores four
+// consecutive columns of one row; row stride 20 keeps both sides free of
+// bank conflicts.
+constexpr int kOutLd = 20;
 
 // The record operands compute wave w uses in one chunk, staged in its own LDS
 // block by its producer wave with direct-to-LDS loads.
@@ -461,6 +480,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   __shared__ __align__(16) char s_state[KB * TS];
   __shared__ __align__(16) char s_delta[2 * TD];
   __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
+  __shared__ __align__(16) float s_out[kComputeWaves][kChunk / kComputeWaves * kOutLd];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -630,16 +650,12 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
       mma(o1, aq[0], dd[0]);
       if (w >= 2) mma(o0, aq[1], dd[1]);
       load_q(rn1);
-      const int rw = 16 * w + 4 * gq;
-      const int64_t ob = ((b * p.T + t0 + rw) * H + h) * V + v0 + m, rs = H * V;
-      if (len == kChunk) {
+      float* tl = s_out[w];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) store_out(out, ob + i * rs, o0[i] + o1[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (rw + i < len) store_out(out, ob + i * rs, o0[i] + o1[i]);
-      }
+      for (int i = 0; i < 4; ++i) tl[(4 * gq + i) * kOutLd + m] = o0[i] + o1[i];
+      const int r = lane >> 2, q4 = 4 * (lane & 3);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * kOutLd + q4);
+      if (16 * w + r < len) store_out4(out, ((b * p.T + t0 + 16 * w + r) * H + h) * V + v0 + q4, x);
     }
     block_sync();   // B2
   }
