@@ -31,7 +31,8 @@
 //
 // Kernels, in order: bwd_chunk (one workgroup per chunk and head: G, A, Aqk,
 // T, W, U, Kt, Qg into a chunk record), bwd_states (the forward recurrence
-// again, keeping the state entering and Delta of every chunk), bwd_dstates
+// again, keeping the state entering every 64-token chunk and Delta of every
+// chunk), bwd_dstates
 // (the reverse recurrence, keeping dS' and dDelta of every chunk and the
 // initial-state gradients), bwd_local (one workgroup per chunk and head: all
 // input gradients).
@@ -436,9 +437,9 @@ __device__ __forceinline__ void store_tile(float* dst, int64_t ld, const f32x4& 
 // One workgroup (four compute waves and the ring's wave) per (sequence, head,
 // 16 value columns): the state from the initial state through every chunk,
 // writing the state that enters each 64-token chunk (the local kernel
-// rebuilds the three after it) and Delta of every chunk.  The 16-column state is K/16
-// accumulator tiles; wave w holds tiles w, w + 4 (rows 16 cb ..), which are
-// also the B operands of its slabs of W S.  Per chunk: each wave's partial
+// rebuilds the three after it) and Delta of every chunk.  The 16-column
+// state is K/16 accumulator tiles; wave w holds tiles w, w + 4 (rows
+// 16 cb ..), which are also the B operands of its slabs of W S.  Per chunk: each wave's partial
 // W S goes through LDS (double buffered, one barrier), every wave sums the
 // four in the same order into Delta = U - W S, and updates its tiles
 // S <- diag(Gamma_C) S + Kt^T Delta.  Operands of chunk c + 1 are read from
