@@ -46,6 +46,7 @@ constexpr int kBC = 16;            // rows per backward chunk
 constexpr int kBThreads = 256;
 constexpr int kRecThreads = 320;   // the recurrences: four compute waves and a wave filling their operand ring
 constexpr float kSpanMax = 64.f;   // exp(64) ~ 6e27: room for sums of O(1e10) below FLT_MAX
+constexpr int kTP = 20;            // LDS row stride of 16x16 tiles (bank-conflict free fragment reads)
 
 // Chunk record (floats) per (slot, head).
 template <int K, int V>
@@ -174,11 +175,15 @@ template <class TI, int K, int V>
 __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   using R = BRec<K, V>;
   constexpr int NKB = K / 16, NVB = V / 16;
+  // Rows padded by four floats, 16x16 tiles to a stride of 20: the fragment
+  // reads (one row per lane, or four rows per lane group) then fall on
+  // distinct banks.
+  constexpr int KP = K + 4, VP = V + 4, TP = kTP;
   const int64_t slot = blockIdx.x / p.H, h = blockIdx.x % p.H;
   BSlot si;
   if (!slot_info(p, slot, &si)) return;
-  __shared__ __align__(16) float sk[kBC][K], sq[kBC][K], sG[kBC][K], sv[kBC][V];
-  __shared__ __align__(16) float sA[kBC][kBC], sP1[kBC][kBC], sP2[kBC][kBC], sT[kBC][kBC];
+  __shared__ __align__(16) float sk[kBC][KP], sq[kBC][KP], sG[kBC][KP], sv[kBC][VP];
+  __shared__ __align__(16) float sA[kBC][TP], sP1[kBC][TP], sP2[kBC][TP], sT[kBC][TP];
   __shared__ float sbeta[kBC];
   __shared__ int s_unsafe;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = 4 * (lane >> 4), n = lane & 15;
@@ -248,8 +253,8 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
       const float* left = wave == 0 ? &sk[0][0] : &sq[0][0];
 #pragma unroll 4
       for (int s = 0; s < NKB; ++s) {
-        const f32x4 x = opa(left, K, 0, 16 * s, lane), kk = opa(&sk[0][0], K, 0, 16 * s, lane);
-        const f32x4 gr = opa(&sG[0][0], K, 0, 16 * s, lane), g0 = opa(&sG[0][0], 0, 0, 16 * s, lane);
+        const f32x4 x = opa(left, KP, 0, 16 * s, lane), kk = opa(&sk[0][0], KP, 0, 16 * s, lane);
+        const f32x4 gr = opa(&sG[0][0], KP, 0, 16 * s, lane), g0 = opa(&sG[0][0], 0, 0, 16 * s, lane);
         f32x4 a, b;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
         const int r = g4 + i;
         float x = 0.f;
         if (n <= r)
-          for (int cc = 0; cc < K; ++cc) x += left[r * K + cc] * sk[n][cc] * __expf(sG[r][cc] - sG[n][cc]);
+          for (int cc = 0; cc < K; ++cc) x += left[r * KP + cc] * sk[n][cc] * __expf(sG[r][cc] - sG[n][cc]);
         c[i] = x;
       }
     }
@@ -284,12 +289,12 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   }
   if (wave == 0) {
     // T = (I - A)(I + A^2)(I + A^4)(I + A^8): squares and products, one wave
-    auto mul = [&](const float (*X)[kBC], const float (*Y)[kBC]) {
+    auto mul = [&](const float (*X)[TP], const float (*Y)[TP]) {
       f32x4 c = {0, 0, 0, 0};
-      mma16(c, opa(&X[0][0], kBC, 0, 0, lane), opb(&Y[0][0], kBC, 0, 0, lane));
+      mma16(c, opa(&X[0][0], TP, 0, 0, lane), opb(&Y[0][0], TP, 0, 0, lane));
       return c;
     };
-    auto put = [&](float (*X)[kBC], const f32x4& c, float diag) {
+    auto put = [&](float (*X)[TP], const f32x4& c, float diag) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) X[g4 + i][n] = c[i] + (g4 + i == n ? diag : 0.f);
     };
@@ -330,15 +335,15 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   for (int t = wave; t < NKB + NVB; t += 4) {
     f32x4 c = {0, 0, 0, 0};
     if (t < NKB) {
-      mma16(c, opa(&sT[0][0], kBC, 0, 0, lane), opb(&sq[0][0], K, 0, 16 * t, lane));
+      mma16(c, opa(&sT[0][0], TP, 0, 0, lane), opb(&sq[0][0], KP, 0, 16 * t, lane));
 #pragma unroll
       for (int i = 0; i < 4; ++i) rec[R::kW + (g4 + i) * K + 16 * t + n] = c[i];
     } else {
       const int vb = t - NKB;
-      f32x4 b = opb(&sv[0][0], V, 0, 16 * vb, lane);
+      f32x4 b = opb(&sv[0][0], VP, 0, 16 * vb, lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] *= sbeta[g4 + j];
-      mma16(c, opa(&sT[0][0], kBC, 0, 0, lane), b);
+      mma16(c, opa(&sT[0][0], TP, 0, 0, lane), b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) rec[R::kU + (g4 + i) * V + 16 * vb + n] = c[i];
     }
@@ -365,9 +370,13 @@ __device__ __forceinline__ void dma_rows(float* dst, const float* src, int lane)
     dma16(dst + 256 * i, src + r * K + 4 * swz(r, pos % UPR));
   }
 }
-// One wave: a [16][16] fp32 block (row stride ld) into a plain [16][16] image.
+// Images of [16][16] blocks hold row r at position 4 (r & 3) + (r >> 2): a
+// lane group's four rows 4g + i then lie 16 banks apart.
+__device__ __forceinline__ int blk_pos(int r) { return 4 * (r & 3) + (r >> 2); }
+// One wave: a [16][16] fp32 block (row stride ld) into such an image (lane l
+// fills position l / 4, the inverse of blk_pos being the same permutation).
 __device__ __forceinline__ void dma_block16(float* dst, const float* src, int ld, int lane) {
-  dma16(dst, src + (lane >> 2) * ld + 4 * (lane & 3));
+  dma16(dst, src + blk_pos(lane >> 2) * ld + 4 * (lane & 3));
 }
 // Fragments of an image: A operand of X (16 x K image), rows 0..15, k = 16 cb
 // + 4g + j; and B operand of X (k = 4g + j, columns 16 cb ..), i.e. the A
@@ -423,7 +432,7 @@ __device__ void ring_fill(IssueFn issue, int64_t n) {
 // its own, so that each lane writes one 16-byte piece of a row (one
 // instruction instead of four).  Row stride 20 keeps both the scattered
 // writes and the 16-byte reads free of bank conflicts.
-constexpr int kTileLd = 20;
+constexpr int kTileLd = kTP;
 __device__ __forceinline__ void store_tile(float* dst, int64_t ld, const f32x4& c, float* lds, int lane) {
   const int g4 = 4 * (lane >> 4), n = lane & 15;
 #pragma unroll
@@ -465,7 +474,7 @@ struct StatesOps {
     }
     const int g4 = 4 * (lane >> 4), n = lane & 15;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) u[i] = m.u[(g4 + i) * kBC + n];
+    for (int i = 0; i < 4; ++i) u[i] = m.u[blk_pos(g4 + i) * kBC + n];
   }
 };
 
@@ -483,7 +492,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
   BSeq s;
   if (!seq_info(p, sq, h, &s)) return;
   __shared__ __align__(16) Img ring[Img::kLead];
-  __shared__ __align__(16) float sP[2][4][kBC][kBC];
+  __shared__ __align__(16) float sP[2][4][kBC][kTP];
   __shared__ __align__(16) float sX[4][TPW][kBC * kTileLd];   // per-wave store staging
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
@@ -582,8 +591,8 @@ struct DStatesOps {
     const int g4 = 4 * (lane >> 4), n = lane & 15;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      aq[j] = m.aq[(g4 + j) * kBC + n];                    // (Aqk^T)[n][4g + j]
-      dout[j] = g4 + j < len ? ld(m.dout, (g4 + j) * kBC + n) : 0.f;
+      aq[j] = m.aq[blk_pos(g4 + j) * kBC + n];             // (Aqk^T)[n][4g + j]
+      dout[j] = g4 + j < len ? ld(m.dout, blk_pos(g4 + j) * kBC + n) : 0.f;
     }
   }
 };
@@ -602,7 +611,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
   BSeq s;
   if (!seq_info(p, sq, h, &s)) return;
   __shared__ __align__(16) Img ring[Img::kLead];
-  __shared__ __align__(16) float sP[2][4][kBC][kBC];
+  __shared__ __align__(16) float sP[2][4][kBC][kTP];
   __shared__ __align__(16) float sX[4][TPW][kBC * kTileLd];   // per-wave store staging
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
@@ -621,10 +630,11 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
           dma_rows<K>(im.w, r + R::kW, lane);
           if (lane < K / 4) dma16(im.gc, r + R::kGc + 4 * lane);
           dma_block16(im.aq, r + R::kAqk, kBC, lane);
-          // 16 columns of each present dO row: 64 / (16 B per lane) lanes a row
+          // 16 columns of each present dO row, LPR lanes of 16 bytes a row,
+          // rows permuted as in every [16][16] image
           constexpr int LPR = kBC * (int)sizeof(TO) / 16;
-          const int row = lane / LPR;
-          if (row < chunk_len(c))   // row 0 always present: every chunk issues kPer loads
+          const int row = lane / LPR < kBC ? blk_pos(lane / LPR) : kBC;
+          if (row < chunk_len(c))   // row 0 (position 0) always present: every chunk issues kPer loads
             dma16(im.dout, d_o + ((s.b * p.T + s.t0 + c * kBC + row) * p.H + h) * V + tile * kBC +
                                (lane % LPR) * (16 / (int)sizeof(TO)));
         },
