@@ -164,6 +164,40 @@ __device__ __forceinline__ f32x4 opb(const float* Y, int ld, int k0, int n0, int
   return f32x4{q[0], q[ld], q[2 * ld], q[3 * ld]};
 }
 
+// Rows 0..15 of a [rows][W] input (row r at src + r * row_stride elements)
+// into fp32 LDS rows of stride LD, zero past len: 16-byte loads (eight bf16
+// or four fp32 per lane) instead of one element per lane.
+__device__ __forceinline__ void cvt16(const uint16_t* src, float* x) {
+  const uint4 u = *reinterpret_cast<const uint4*>(src);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void cvt16(const float* src, float* x) {
+  const f32x4 u = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) x[i] = u[i];
+}
+template <int W, int LD, class T>
+__device__ __forceinline__ void load_rows(float* dst, const T* src, int64_t row_stride, int len, int tid) {
+  constexpr int E = 16 / (int)sizeof(T), PER_ROW = W / E;
+  for (int e = tid; e < kBC * PER_ROW; e += kBThreads) {
+    const int r = e / PER_ROW, c = (e % PER_ROW) * E;
+    float x[E];
+    if (r < len) {
+      cvt16(src + r * row_stride + c, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) x[i] = 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < E; i += 4) *reinterpret_cast<f32x4*>(dst + r * LD + c + i) = f32x4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+  }
+}
+
 // ---------------------------------------------------------------- bwd_chunk
 // One workgroup (four waves) per (chunk, head): the chunk quantities into
 // the chunk record.  A = beta (kf kb^T) and Aqk = qf kb^T with kf = k exp(G -
@@ -194,17 +228,12 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   const TI* beta = static_cast<const TI*>(p.beta);
   float* rec = p.rec + (slot * p.H + h) * R::kFloats;
   if (tid == 0) s_unsafe = 0;
-  for (int e = tid; e < kBC * K; e += kBThreads) {
-    const int r = e / K, c = e % K;
-    const int64_t off = ((si.b * p.T + si.t0 + r) * p.H + h) * K + c;
-    const bool live = r < si.len;
-    sk[r][c] = live ? ld(k, off) : 0.f;
-    sq[r][c] = live ? ld(q, off) : 0.f;
-    sG[r][c] = live ? ld(g, off) : 0.f;
-  }
-  for (int e = tid; e < kBC * V; e += kBThreads) {
-    const int r = e / V, j = e % V;
-    sv[r][j] = r < si.len ? ld(v, ((si.b * p.T + si.t0 + r) * p.H + h) * V + j) : 0.f;
+  {
+    const int64_t t0 = (si.b * p.T + si.t0) * p.H + h;   // first row's token index (times H, plus h)
+    load_rows<K, KP>(&sk[0][0], k + t0 * K, p.H * K, si.len, tid);
+    load_rows<K, KP>(&sq[0][0], q + t0 * K, p.H * K, si.len, tid);
+    load_rows<K, KP>(&sG[0][0], g + t0 * K, p.H * K, si.len, tid);
+    load_rows<V, VP>(&sv[0][0], v + t0 * V, p.H * V, si.len, tid);
   }
   if (tid < kBC) sbeta[tid] = tid < si.len ? ld(beta, (si.b * p.T + si.t0 + tid) * p.H + h) : 0.f;
   __syncthreads();
@@ -331,21 +360,40 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
   }
   __syncthreads();
   rec[R::kT + tid] = sT[tid / kBC][tid % kBC];
-  // W = T Kb, U = T Vb: K/16 + V/16 output tiles over the four waves
-  for (int t = wave; t < NKB + NVB; t += 4) {
-    f32x4 c = {0, 0, 0, 0};
-    if (t < NKB) {
-      mma16(c, opa(&sT[0][0], TP, 0, 0, lane), opb(&sq[0][0], KP, 0, 16 * t, lane));
+  // W = T Kb, U = T Vb: K/16 + V/16 output tiles, taken by the waves in
+  // pairs of adjacent column blocks and stored through an LDS tile of 16 x 32
+  // (k's and G's buffers are free by now; row stride 36 keeps both sides free
+  // of bank conflicts), so that each lane stores 16 bytes and each
+  // instruction whole 128-byte lines.  Stored straight from the accumulator
+  // layout, each wave wrote half lines that another wave completed, which
+  // cost this kernel about a third of its time.
+  constexpr int NP = (NKB + NVB) / 2, SL = 2 * kBC + 4;
+  constexpr bool kAlias = 2 * kBC * SL <= kBC * KP;
+  __shared__ __align__(16) float sStage[kAlias ? 4 : 4 * kBC * SL];
+  float* stage = kAlias ? (wave < 2 ? &sk[0][0] : &sG[0][0]) + (wave & 1) * (kBC * SL) : sStage + wave * (kBC * SL);
+  for (int pr = wave; pr < NP; pr += 4) {
+    const bool isW = pr < NKB / 2;
+    const int t0 = isW ? 2 * pr : 2 * (pr - NKB / 2);   // first column block of the pair
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rec[R::kW + (g4 + i) * K + 16 * t + n] = c[i];
-    } else {
-      const int vb = t - NKB;
-      f32x4 b = opb(&sv[0][0], VP, 0, 16 * vb, lane);
+    for (int h2 = 0; h2 < 2; ++h2) {
+      f32x4 c = {0, 0, 0, 0};
+      if (isW) {
+        mma16(c, opa(&sT[0][0], TP, 0, 0, lane), opb(&sq[0][0], KP, 0, 16 * (t0 + h2), lane));
+      } else {
+        f32x4 b = opb(&sv[0][0], VP, 0, 16 * (t0 + h2), lane);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] *= sbeta[g4 + j];
-      mma16(c, opa(&sT[0][0], TP, 0, 0, lane), b);
+        for (int j = 0; j < 4; ++j) b[j] *= sbeta[g4 + j];
+        mma16(c, opa(&sT[0][0], TP, 0, 0, lane), b);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rec[R::kU + (g4 + i) * V + 16 * vb + n] = c[i];
+      for (int i = 0; i < 4; ++i) stage[(g4 + i) * SL + 16 * h2 + n] = c[i];
+    }
+    float* dst = rec + (isW ? R::kW : R::kU) + 16 * t0;
+    const int ldr = isW ? K : V;
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int r = (lane >> 3) + 8 * hh, c4 = 4 * (lane & 7);
+      *reinterpret_cast<f32x4*>(dst + r * ldr + c4) = *reinterpret_cast<const f32x4*>(stage + r * SL + c4);
     }
   }
   if (tid == 0) rec[R::kInfo] = unsafe ? 1.f : 0.f;
@@ -756,16 +804,13 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3))) 
   const float* sdD = p.dds + (slot * p.H + h) * kBC * V;
 
   // ---- inputs
-  for (int e = tid; e < kBC * K; e += kBThreads) {
-    const int r = e / K, c = e % K;
-    sG[r][c] = rec[R::kG + e];
-    sk[r][c] = r < len ? ld(k, tok(r) * K + c) : 0.f;
-    sq[r][c] = r < len ? ld(q, tok(r) * K + c) : 0.f;
-  }
-  for (int e = tid; e < kBC * V; e += kBThreads) {
-    const int r = e / V, j = e % V;
-    sv[e] = r < len ? ld(v, tok(r) * V + j) : 0.f;
-    sdO[e] = r < len ? ld(d_o, tok(r) * V + j) : 0.f;
+  {
+    const int64_t t0 = tok(0);
+    load_rows<K, K>(&sG[0][0], rec + R::kG, K, kBC, tid);
+    load_rows<K, K>(&sk[0][0], k + t0 * K, p.H * K, len, tid);
+    load_rows<K, K>(&sq[0][0], q + t0 * K, p.H * K, len, tid);
+    load_rows<V, V>(sv, v + t0 * V, p.H * V, len, tid);
+    load_rows<V, V>(sdO, d_o + t0 * V, p.H * V, len, tid);
   }
   sT[tid / kBC][tid % kBC] = rec[R::kT + tid];
   sAqk[tid / kBC][tid % kBC] = rec[R::kAqk + tid];
