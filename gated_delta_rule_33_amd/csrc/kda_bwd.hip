@@ -44,7 +44,11 @@ namespace {
 
 constexpr int kBC = 16;            // rows per backward chunk
 constexpr int kBThreads = 256;
-constexpr int kRecThreads = 320;   // the recurrences: four compute waves and a wave filling their operand ring
+// The recurrences: four compute waves and the waves filling their operand
+// ring (two for the states, three for their gradients).  One wave moves
+// about 10 bytes per clock from L2 into LDS, so a single one set the pace of
+// every chunk.
+constexpr int kStatesThreads = 6 * kWave, kDStatesThreads = 7 * kWave;
 constexpr float kSpanMax = 64.f;   // exp(64) ~ 6e27: room for sums of O(1e10) below FLT_MAX
 constexpr int kTP = 20;            // LDS row stride of 16x16 tiles (bank-conflict free fragment reads)
 
@@ -401,7 +405,7 @@ __global__ __launch_bounds__(kBThreads) void bwd_chunk_kernel(BwdParams p) {
 
 // ------------------------------------------------- recurrence operand ring
 // The recurrences read each chunk's operands from an LDS image that the
-// workgroup's fifth wave fills with direct-to-LDS loads LEAD chunks ahead,
+// workgroup's fill waves load with direct-to-LDS loads LEAD chunks ahead,
 // so the compute waves issue no global loads in their loop.  Images of
 // [16][K] operands store 16-byte unit u of row r at unit u ^ (r & 15): the
 // fragment reads (a row of four columns per lane, or four rows of one column
@@ -458,7 +462,8 @@ __device__ __forceinline__ void wait_chunks(int64_t n) {
   else vm_wait<0>();
 }
 
-// The fifth wave: issue(c) loads chunk c's image into slot c % LEAD.  Chunk
+// A fill wave: issue(c) loads its part of chunk c's image (PER direct loads)
+// into slot c % LEAD.  Chunk
 // c + 1 is complete before barrier c (the compute waves read it right after),
 // and chunk c + LEAD is issued after it, into the slot of chunk c, which no
 // wave reads past barrier c.  One barrier precedes the loop (chunk 0 ready).
@@ -491,7 +496,7 @@ __device__ __forceinline__ void store_tile(float* dst, int64_t ld, const f32x4& 
 }
 
 // ---------------------------------------------------------------- bwd_states
-// One workgroup (four compute waves and the ring's wave) per (sequence, head,
+// One workgroup (four compute waves and the ring's fill waves) per (sequence, head,
 // 16 value columns): the state from the initial state through every chunk,
 // writing the state that enters each 64-token chunk (the local kernel
 // rebuilds the three after it) and Delta of every chunk.  The 16-column
@@ -504,7 +509,6 @@ __device__ __forceinline__ void store_tile(float* dst, int64_t ld, const f32x4& 
 template <int K, int V>
 struct StatesImg {
   float w[kBC * K], kt[kBC * K], gc[K], u[kBC * kBC];
-  static constexpr int kPer = 2 * (K / 16) + 2;   // direct loads per image
   static constexpr int kLead = 4;                 // images in flight (ring slots)
 };
 
@@ -527,7 +531,7 @@ struct StatesOps {
 };
 
 template <int K, int V>
-__global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
+__global__ __launch_bounds__(kStatesThreads) void bwd_states_kernel(BwdParams p) {
   using R = BRec<K, V>;
   using Img = StatesImg<K, V>;
   using Ops = StatesOps<K, V>;
@@ -544,15 +548,23 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
   __shared__ __align__(16) float sX[4][TPW][kBC * kTileLd];   // per-wave store staging
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = 4 * (lane >> 4), n = lane & 15;
-  if (wave == 4) {
-    ring_fill<Img::kPer, Img::kLead>(
+  auto rec = [&](int64_t c) { return p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats; };
+  if (wave == 4) {   // W and exp(G_C): K/16 + 1 loads a chunk (lane 0 always issues)
+    ring_fill<K / 16 + 1, Img::kLead>(
         [&](int64_t c) {
           Img& m = ring[c % Img::kLead];
-          const float* r = p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats;
-          dma_rows<K>(m.w, r + R::kW, lane);
-          dma_rows<K>(m.kt, r + R::kKt, lane);
-          if (lane < K / 4) dma16(m.gc, r + R::kGc + 4 * lane);   // lane 0 always issues: kPer loads
-          dma_block16(m.u, r + R::kU + tile * kBC, V, lane);
+          dma_rows<K>(m.w, rec(c) + R::kW, lane);
+          if (lane < K / 4) dma16(m.gc, rec(c) + R::kGc + 4 * lane);
+        },
+        s.n16);
+    return;
+  }
+  if (wave == 5) {   // Kt and the workgroup's 16 columns of U: K/16 + 1 loads a chunk
+    ring_fill<K / 16 + 1, Img::kLead>(
+        [&](int64_t c) {
+          Img& m = ring[c % Img::kLead];
+          dma_rows<K>(m.kt, rec(c) + R::kKt, lane);
+          dma_block16(m.u, rec(c) + R::kU + tile * kBC, V, lane);
         },
         s.n16);
     return;
@@ -606,7 +618,7 @@ __global__ __launch_bounds__(kRecThreads) void bwd_states_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- bwd_dstates
-// One workgroup (four compute waves and the ring's wave) per (sequence, head,
+// One workgroup (four compute waves and the ring's fill waves) per (sequence, head,
 // 16 value columns): dS' from the final state's gradient back through every
 // chunk, writing dS' of each chunk and the gradient of the sequence's
 // initial state.  Same tiling as bwd_states: per chunk the waves' partial
@@ -618,8 +630,7 @@ template <class TO, int K, int V>
 struct DStatesImg {
   float kt[kBC * K], qg[kBC * K], w[kBC * K], gc[K], aq[kBC * kBC];
   TO dout[kBC * kBC];
-  static constexpr int kPer = 3 * (K / 16) + 3;
-  static constexpr int kLead = 3;
+  static constexpr int kLead = 4;
 };
 
 template <int K, int V>
@@ -646,7 +657,7 @@ struct DStatesOps {
 };
 
 template <class TO, int K, int V>
-__global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDStatesThreads) void bwd_dstates_kernel(BwdParams p) {
   using R = BRec<K, V>;
   using Img = DStatesImg<TO, K, V>;
   using Ops = DStatesOps<K, V>;
@@ -667,22 +678,32 @@ __global__ __launch_bounds__(kRecThreads) void bwd_dstates_kernel(BwdParams p) {
   const int64_t seq_len = p.packed ? p.segs[sq].len : p.T;
   // Step m handles chunk n16 - 1 - m.
   auto chunk_len = [&](int64_t c) { return (int)min<int64_t>(kBC, seq_len - c * kBC); };
-  if (wave == 4) {
-    ring_fill<Img::kPer, Img::kLead>(
+  // step m's image holds chunk n16 - 1 - m
+  auto rec = [&](int64_t m) { return p.rec + ((s.slot0 + s.n16 - 1 - m) * p.H + h) * R::kFloats; };
+  if (wave == 4) {   // Kt: K/16 loads a chunk
+    ring_fill<K / 16, Img::kLead>([&](int64_t m) { dma_rows<K>(ring[m % Img::kLead].kt, rec(m) + R::kKt, lane); },
+                                  s.n16);
+    return;
+  }
+  if (wave == 5) {   // Qg: K/16 loads a chunk
+    ring_fill<K / 16, Img::kLead>([&](int64_t m) { dma_rows<K>(ring[m % Img::kLead].qg, rec(m) + R::kQg, lane); },
+                                  s.n16);
+    return;
+  }
+  if (wave == 6) {   // W, exp(G_C), Aqk and the dO columns: K/16 + 3 loads a chunk
+    ring_fill<K / 16 + 3, Img::kLead>(
         [&](int64_t m) {
           Img& im = ring[m % Img::kLead];
           const int64_t c = s.n16 - 1 - m;
-          const float* r = p.rec + ((s.slot0 + c) * p.H + h) * R::kFloats;
-          dma_rows<K>(im.kt, r + R::kKt, lane);
-          dma_rows<K>(im.qg, r + R::kQg, lane);
+          const float* r = rec(m);
           dma_rows<K>(im.w, r + R::kW, lane);
-          if (lane < K / 4) dma16(im.gc, r + R::kGc + 4 * lane);
+          if (lane < K / 4) dma16(im.gc, r + R::kGc + 4 * lane);   // lane 0 always issues
           dma_block16(im.aq, r + R::kAqk, kBC, lane);
           // 16 columns of each present dO row, LPR lanes of 16 bytes a row,
           // rows permuted as in every [16][16] image
           constexpr int LPR = kBC * (int)sizeof(TO) / 16;
           const int row = lane / LPR < kBC ? blk_pos(lane / LPR) : kBC;
-          if (row < chunk_len(c))   // row 0 (position 0) always present: every chunk issues kPer loads
+          if (row < chunk_len(c))   // row 0 (position 0) always present: every chunk issues its loads
             dma16(im.dout, d_o + ((s.b * p.T + s.t0 + c * kBC + row) * p.H + h) * V + tile * kBC +
                                (lane % LPR) * (16 / (int)sizeof(TO)));
         },
@@ -1125,9 +1146,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stage) {
   const int64_t seqs = ((p.packed ? a.smax : a.B) * a.H + 7) / 8 * 8 * (V / kBC);
   switch (stage) {
     case 0: hipLaunchKernelGGL((bwd_chunk_kernel<TI, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p); break;
-    case 1: hipLaunchKernelGGL((bwd_states_kernel<K, V>), dim3((unsigned)seqs), dim3(kRecThreads), 0, a.stream, p); break;
+    case 1: hipLaunchKernelGGL((bwd_states_kernel<K, V>), dim3((unsigned)seqs), dim3(kStatesThreads), 0, a.stream, p); break;
     case 2:
-      hipLaunchKernelGGL((bwd_dstates_kernel<TO, K, V>), dim3((unsigned)seqs), dim3(kRecThreads), 0, a.stream, p);
+      hipLaunchKernelGGL((bwd_dstates_kernel<TO, K, V>), dim3((unsigned)seqs), dim3(kDStatesThreads), 0, a.stream, p);
       break;
     case 3: hipLaunchKernelGGL((bwd_local_kernel<TI, TO, K, V>), dim3((unsigned)(slots * a.H)), blk, 0, a.stream, p); break;
     default: return hipErrorInvalidValue;
