@@ -186,13 +186,17 @@ __device__ __forceinline__ void cvt16(const float* src, float* x) {
   for (int i = 0; i < 4; ++i) x[i] = u[i];
 }
 template <int W, int LD, class T>
-__device__ __forceinline__ void load_rows(float* dst, const T* src, int64_t row_stride, int len, int tid) {
+__device__ __forceinline__ void load_rows(float* dst, const T* src, int64_t row_stride, int len, int tid,
+                                          const float* div = nullptr) {
   constexpr int E = 16 / (int)sizeof(T), PER_ROW = W / E;
   for (int e = tid; e < kBC * PER_ROW; e += kBThreads) {
     const int r = e / PER_ROW, c = (e % PER_ROW) * E;
     float x[E];
     if (r < len) {
       cvt16(src + r * row_stride + c, x);
+      if (div)   // each row divided by its own factor
+#pragma unroll
+        for (int i = 0; i < E; ++i) x[i] /= div[r];
     } else {
 #pragma unroll
       for (int i = 0; i < E; ++i) x[i] = 0.f;
@@ -820,9 +824,14 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3))) 
   float* sv = sVG;
   float* sdO = sOW;
   // Delta and dDelta of the chunk, as the recurrences left them (rows past
-  // the chunk are zero), read as operands straight from memory
-  const float* sD = p.ds + (slot * p.H + h) * kBC * V;
-  const float* sdD = p.dds + (slot * p.H + h) * kBC * V;
+  // the chunk are zero).  Every wave reads them for each of its key blocks:
+  // with V <= K they are staged for phase B in the buffers of k and q, which
+  // phase B does not use (both are loaded again, normalised, after it).
+  constexpr bool kStageD = V <= K;
+  const float* gD = p.ds + (slot * p.H + h) * kBC * V;
+  const float* gdD = p.dds + (slot * p.H + h) * kBC * V;
+  const float* sD = kStageD ? &sk[0][0] : gD;
+  const float* sdD = kStageD ? &sq[0][0] : gdD;
 
   // ---- inputs
   {
@@ -849,9 +858,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     sqq = sum16(sqq);
     skk = sum16(skk);
     const float nq = p.l2norm ? sqrtf(sqq + 1e-6f) : 1.f, nk = p.l2norm ? sqrtf(skk + 1e-6f) : 1.f;
-    for (int c = cc; c < K; c += kBC) {
-      sq[r][c] /= nq;
-      sk[r][c] /= nk;
+    if constexpr (!kStageD) {
+      for (int c = cc; c < K; c += kBC) {
+        sq[r][c] /= nq;
+        sk[r][c] /= nk;
+      }
     }
     if (cc == 0) {
       snq[r] = nq;
@@ -859,6 +870,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     }
   }
   __syncthreads();
+  if constexpr (kStageD) {
+    load_rows<V, V>(&sk[0][0], gD, V, kBC, tid);
+    load_rows<V, V>(&sq[0][0], gdD, V, kBC, tid);
+    __syncthreads();
+  }
 
   // ---- phase B: products over V
   // d Gamma_C = rowsum(dh * h) comes along: lane (g, n) holds h and dh of
@@ -963,6 +979,11 @@ __global__ __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3))) 
     }
   }
   __syncthreads();
+  if constexpr (kStageD) {   // k and q again, normalised as before
+    const int64_t t0 = tok(0);
+    load_rows<K, K>(&sk[0][0], k + t0 * K, p.H * K, len, tid, p.l2norm ? snk : nullptr);
+    load_rows<K, K>(&sq[0][0], q + t0 * K, p.H * K, len, tid, p.l2norm ? snq : nullptr);
+  }
   // dW goes through LDS (its transposes are needed); dKt and dQg stay in the
   // registers of the lanes that use them
   float* sdW = sOW;
