@@ -18,6 +18,7 @@ namespace kda {
 namespace {
 
 constexpr int kPrepThreads = 1024;
+constexpr int kPrepTok = 8;   // tokens per thread in the segment scan
 
 // Inclusive prefix sum over the 1024 threads of the block; *total gets the sum.
 __device__ int block_scan(int x, int* wave_sums, int* total) {
@@ -83,22 +84,42 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
   uint32_t flags = 0;
   for (int64_t b = 0; b < p.B; ++b) {
     const int32_t* row = p.ids + b * T;
-    // Pass 1: segment starts and ends.
+    // Pass 1: segment starts and ends.  Each thread takes kPrepTok
+    // consecutive tokens (all their ids loaded at once), counts the starts
+    // among them, and one block scan per kPrepThreads * kPrepTok tokens
+    // numbers the segments.
     int row_segs = 0;
-    for (int64_t t0 = 0; t0 < T; t0 += kPrepThreads) {
-      const int64_t t = t0 + tid;
-      const int id = t < T ? row[t] : 0;
-      const int prev = (t > 0 && t < T) ? row[t - 1] : 0;
-      const int next = (t + 1 < T) ? row[t + 1] : 0;
-      const int start = (id != 0) && (t == 0 || id != prev);
-      const int end = (id != 0) && (t == T - 1 || next != id);
+    for (int64_t t0 = 0; t0 < T; t0 += (int64_t)kPrepThreads * kPrepTok) {
+      const int64_t tb = t0 + (int64_t)tid * kPrepTok;
+      int ids[kPrepTok + 2];   // tokens tb - 1 .. tb + kPrepTok (0 outside the row)
+#pragma unroll
+      for (int i = 0; i < kPrepTok + 2; ++i) {
+        const int64_t t = tb - 1 + i;
+        ids[i] = (t >= 0 && t < T) ? row[t] : 0;
+      }
+      int starts = 0;
+#pragma unroll
+      for (int i = 1; i <= kPrepTok; ++i) {
+        const int64_t t = tb + i - 1;
+        starts += (t < T && ids[i] != 0 && (t == 0 || ids[i] != ids[i - 1])) ? 1 : 0;
+      }
       int total;
-      const int incl = block_scan(start, wave_sums, &total);
-      const int local = row_segs + incl - 1;
-      if (id != 0 && local < p.n_max) {
-        SegEntry* se = p.segs + seg_base + local;
-        if (start) { se->b = (int)b; se->t0 = (int)t; se->local = local; }
-        if (end) se->len = (int)(t + 1);   // end for now; turned into a length below
+      const int incl = block_scan(starts, wave_sums, &total);
+      int seen = row_segs + incl - starts;   // segments started before this thread's first token
+#pragma unroll
+      for (int i = 1; i <= kPrepTok; ++i) {
+        const int64_t t = tb + i - 1;
+        if (t >= T) break;
+        const int id = ids[i];
+        const bool start = id != 0 && (t == 0 || id != ids[i - 1]);
+        const bool end = id != 0 && (t == T - 1 || ids[i + 1] != id);
+        seen += start ? 1 : 0;
+        const int local = seen - 1;   // the segment token t belongs to
+        if (id != 0 && local < p.n_max) {
+          SegEntry* se = p.segs + seg_base + local;
+          if (start) { se->b = (int)b; se->t0 = (int)t; se->local = local; }
+          if (end) se->len = (int)(t + 1);   // end for now; turned into a length below
+        }
       }
       row_segs += total;
     }
