@@ -47,7 +47,7 @@ struct Roles {
   static constexpr int kPrefetchWave = kProducer0 + kComputeWaves;
   static constexpr int kThreads = (kPrefetchWave + 1) * kWave;
 };
-constexpr int kPrefetchAhead = 1;   // chunks between the L2 prefetch and the use of a record
+constexpr int kPrefetchAhead = 0;   // extra chunks between the L2 prefetch and the use of a record
 
 // An operand kept in LDS as rows n (value channel) of k-contiguous values.
 template <class F> struct LdsPlane;
@@ -446,9 +446,9 @@ __global__ __launch_bounds__(Roles<TPW>::kThreads) void kda_recur_kernel(RecurPa
 // it is loaded into the wave's registers one chunk ahead, each group right
 // after its last use; only S and Delta pass through LDS.  Two barriers per
 // chunk: B1 after the Delta phase (Delta visible), B2 at the end (the new
-// state visible, the Delta buffer free).  The fifth wave pulls records two
-// chunks ahead into L2 (further ahead, the lines wait in L2 longer and more
-// of them are evicted before use).
+// state visible, the Delta buffer free).  The fifth wave pulls the next
+// chunk's record into L2 (further ahead, the lines wait in L2 longer and
+// more of them are evicted before use).
 //
 // With kTrans the same loop carries, instead of the state, the transition of
 // a row's first segment: the recurrence is affine in the state a segment
