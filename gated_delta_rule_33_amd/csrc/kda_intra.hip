@@ -205,21 +205,22 @@ __device__ __forceinline__ ItemPos item_pos(const IntraParams& p, int64_t item) 
   return q;
 }
 
-// q advanced by d (a position used as a stride: d.chunk whole chunks and
-// d.h heads, d.ci < nc_fixed after d.b whole rows).
-__device__ __forceinline__ ItemPos item_advance(const IntraParams& p, ItemPos q, const ItemPos& d) {
-  q.h += d.h;
-  q.chunk += d.chunk;
-  q.b += d.b;
-  q.ci += d.ci;
-  if (q.h >= p.H) {
-    q.h -= p.H;
-    q.chunk += 1;
-    q.ci += 1;
+// q moved back by d (a position used as a stride: d.chunk whole chunks and
+// d.h heads, d.ci < nc_fixed after d.b whole rows), with borrows instead of
+// an integer division per item.
+__device__ __forceinline__ ItemPos item_retreat(const IntraParams& p, ItemPos q, const ItemPos& d) {
+  q.h -= d.h;
+  q.chunk -= d.chunk;
+  q.b -= d.b;
+  q.ci -= d.ci;
+  if (q.h < 0) {
+    q.h += p.H;
+    q.chunk -= 1;
+    q.ci -= 1;
   }
-  if (!p.packed && q.ci >= p.nc_fixed) {
-    q.ci -= p.nc_fixed;
-    q.b += 1;
+  if (!p.packed && q.ci < 0) {
+    q.ci += p.nc_fixed;
+    q.b -= 1;
   }
   return q;
 }
@@ -306,8 +307,11 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
     issue_rows<TI, K>(sm.q, gq_ + (it.tok0 * H + it.h) * K, H * K, it.len, w, lane);
   };
 
+  // Items are walked from the last one back: the records of the first
+  // chunks, which the recurrence reads first, are then the most recently
+  // written and still in L2 and the memory-side cache when it starts.
   {
-    const ItemInfo first = item_info(p, item_pos(p, blockIdx.x));
+    const ItemInfo first = item_info(p, item_pos(p, n_items - 1 - (int64_t)blockIdx.x));
     issue_k(first);
     issue_gb(first, 0);
     issue_q(first);
@@ -315,15 +319,15 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
   int it_no = 0;
   const ItemPos stride = item_pos(p, gridDim.x);
-  ItemPos pos = item_pos(p, blockIdx.x);
-  for (int64_t item = blockIdx.x; item < n_items; item += gridDim.x, ++it_no) {
+  ItemPos pos = item_pos(p, n_items - 1 - (int64_t)blockIdx.x);
+  for (int64_t idx = blockIdx.x; idx < n_items; idx += gridDim.x, ++it_no) {
+    const int64_t item = n_items - 1 - idx;
     const int cb = S::kDB ? (it_no & 1) : 0;
     const ItemInfo cur = item_info(p, pos);
     const int len = cur.len;
     const int64_t h = cur.h;
-    const int64_t nxt_item = item + gridDim.x;
-    const bool has_next = nxt_item < n_items;
-    const ItemPos npos = item_advance(p, pos, stride);
+    const bool has_next = idx + gridDim.x < n_items;
+    const ItemPos npos = item_retreat(p, pos, stride);
     const ItemInfo nxt = has_next ? item_info(p, npos) : cur;
     pos = npos;
     char* rec = p.records + item * p.record_bytes;
