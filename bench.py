@@ -39,6 +39,15 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix peak, vendor figure
 METRIC = "KDA fwd ms & tokens/s, B=1 H=32 T=8192 K=V=128 bf16; % MFMA/HBM roofline"
 TPU_V7X_FIXED_MS = 1.870        # pages' fastest H=32/T=8192 fixed forward (context, another machine)
+# The pages' TPU v7x forward latencies of the fused kernel per workload (the tokamax packed forward page,
+# performance table and representative-shape table): context from another machine, never a target.
+TPU_V7X_CONTEXT_MS = {
+    "bf16_b1_h8_t1024_fixed": 0.208,
+    "bf16_b1_h8_t1024_packed4": 0.337,
+    "bf16_b1_h32_t8192_fixed_state": 1.870,
+    "bf16_b1_h32_t8192_packed25_l2": 2.891,
+}
+PARITY_TOL_BF16 = 2e-2          # max|err| / rms(ref) for bf16 inputs
 
 
 KERNEL_SOURCES = {   # sources a kernel's code depends on (its traffic figures go stale when they change)
@@ -312,6 +321,13 @@ def time_layer_ops(w, steps: int, warmup: int):
     return out
 
 
+def path_survey_bytes(w):
+    """Algorithmic bytes of the whole forward with a bf16 output (the pages'
+    output dtype): inputs read once, o in bf16 and the fp32 states written once."""
+    alg = algorithmic(w, out_bytes=2)
+    return sum(a["bytes"] for a in alg.values())
+
+
 def summarize(w, res, out_bytes):
     steps = len(res["step_ms"])
     ms = res["total_ms"] / steps
@@ -332,22 +348,47 @@ def summarize(w, res, out_bytes):
                 path_bytes=path_bytes, path_flops=path_flops)
 
 
-def cpu_baseline(w, inp, gpu_out):
-    """The oracle (fp64 build, as it stands) on the host cores, on the whole
-    workload; also the parity of the benchmarked GPU output against it."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_parity(w, inp, gpu_out, threads=None):
+    """Parity of a benchmarked GPU output against the fp64 oracle build on the
+    same inputs (max|err| / rms(ref), per tensor)."""
     import oracle
-    threads = min(oracle.default_threads(), w.B * w.H)
-    t0 = time.perf_counter()
     o_ref, fin_ref = oracle.forward_inputs(inp, w, precision="f64", num_threads=threads)
-    dt = time.perf_counter() - t0
     o_gpu, fin_gpu = gpu_out
     parity = {"o_rel_err": oracle.rel_err(o_gpu, o_ref)}
     if fin_ref is not None:
         parity["final_rel_err"] = oracle.rel_err(fin_gpu, fin_ref)
-    cpu = {"value": round(w.B * w.T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-           "sample": f"whole workload {w.name} (B*T*H = {w.B * w.T * w.H} head-tokens), fp64 token loop, "
-                     f"{dt:.2f} s on {threads} threads ({os.cpu_count()} CPUs visible)"}
-    return cpu, parity
+    return parity
+
+
+def cpu_baseline(w, inp):
+    """The plain fp32 oracle build, as it stands, timed on the host cores over
+    the whole workload (one thread per independent (row, head) recurrence, at
+    most one per core)."""
+    import oracle
+    threads = min(oracle.default_threads(), w.B * w.H)
+    t0 = time.perf_counter()
+    oracle.forward_inputs(inp, w, precision="f32", num_threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.B * w.T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload {w.name} (B*T*H = {w.B * w.T * w.H} head-tokens), plain fp32 token loop, "
+                      f"{dt:.2f} s on {threads} threads ({os.cpu_count()} CPUs visible, {cpu_model()})"}
+
+
+def gpu_outputs(res):
+    o = res["call"].tensors["o"].float().cpu().numpy()
+    fin = res["call"].tensors["final_state"]
+    return o, (None if fin is None else fin.cpu().numpy())
 
 
 def main():
@@ -356,9 +397,11 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bf16_b1_h32_t8192_fixed_state", choices=sorted(WORKLOADS))
-    ap.add_argument("--extra", default="bf16_b1_h32_t8192_packed25_l2",
-                    help="second workload timed and reported under 'extra' ('' for none)")
+    ap.add_argument("--extra", default="bf16_b1_h32_t8192_packed25_l2,bf16_b1_h8_t1024_fixed,bf16_b1_h8_t1024_packed4",
+                    help="comma-separated workloads also timed and reported under 'extra' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle parity of the benchmarked outputs (it gates the exit status)")
     ap.add_argument("--no-layer-ops", dest="layer_ops", action="store_false",
                     help="skip the timing of the short convolution and the gated RMSNorm")
     ap.add_argument("--no-gate-in-kernel", dest="gate_in_kernel", action="store_false",
@@ -389,38 +432,55 @@ def main():
     s = summarize(w, res, out_bytes=4)
     log(f"[bench] {w.name}: {s['ms'] * 1e3:.1f} us/step, kernels {s['kernels']}")
 
-    o = res["call"].tensors["o"].float().cpu().numpy()
-    fin = res["call"].tensors["final_state"]
-    fin = None if fin is None else fin.cpu().numpy()
-    cpu, parity = (None, None)
+    cpu = None
+    parities = {}
     if not args.no_cpu_baseline:
         log("[bench] oracle on the host")
-        cpu, parity = cpu_baseline(w, res["inp"], (o, fin))
-        log(f"[bench] cpu baseline {cpu}, parity {parity}")
+        cpu = cpu_baseline(w, res["inp"])
+        log(f"[bench] cpu baseline {cpu}")
+    if not args.no_parity:
+        parities[w.name] = oracle_parity(w, res["inp"], gpu_outputs(res))
+        log(f"[bench] parity {w.name} {parities[w.name]}")
 
     dom = s["kernels"][s["dominant"]]
+    path_traffic = None
+    kernel_traffic = {n: measured_traffic(n, w.name) for n in s["kernels"] if n in KERNEL_SOURCES}
+    if kernel_traffic and all(v is not None for v in kernel_traffic.values()):
+        path_traffic = sum(kernel_traffic.values())
+    survey_bytes = path_survey_bytes(w)
     roofline = {"bound": "hbm", "kernel": s["dominant"], "achieved": dom["achieved_gbps"], "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom["achieved_gbps"] / HBM_PEAK_GBPS, 4),
                 "traffic": measured_traffic(s["dominant"], w.name), "alg_bytes": dom["alg_bytes"],
                 "mfma_tflops": dom["achieved_tflops"],
-                "mfma_frac": round(dom["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}
+                "mfma_frac": round(dom["achieved_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+                "path": {"alg_bytes": s["path_bytes"], "alg_bytes_basis": "inputs read once, fp32 o and fp32 "
+                         "states written once", "achieved": round(s["path_gbps"], 1),
+                         "frac": round(s["path_gbps"] / HBM_PEAK_GBPS, 4),
+                         "alg_bytes_bf16_o": survey_bytes,
+                         "frac_bf16_o": round(survey_bytes / (s["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "traffic": path_traffic, "kernel_traffic": kernel_traffic,
+                         "mfma_tflops": round(s["path_tflops"], 2),
+                         "mfma_frac": round(s["path_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)}}
     extra = {"timing": "value/ms_per_step: K steps with no per-kernel events; kernels and step_ms: K further "
                        "steps with an event around every kernel",
-             "path": {"alg_bytes": s["path_bytes"], "alg_flops": s["path_flops"],
-                      "gbps": round(s["path_gbps"], 1), "hbm_frac": round(s["path_gbps"] / HBM_PEAK_GBPS, 4),
-                      "tflops": round(s["path_tflops"], 2)},
              "step_ms": {"median": round(s["median_ms"], 4), "min": round(s["min_ms"], 4),
                          "max": round(s["max_ms"], 4)},
-             "kernels": s["kernels"], "parity_vs_oracle": parity,
-             "tpu_v7x_context_ms": TPU_V7X_FIXED_MS}
-    if args.extra:
-        w2 = WORKLOADS[args.extra]
+             "kernels": s["kernels"], "parity_vs_oracle": parities,
+             "vs_baseline_basis": f"tokens/s over the pages' TPU v7x {TPU_V7X_FIXED_MS} ms for this workload "
+                                  "(another machine: context only)"}
+    extra_names = [n for n in (args.extra or "").split(",") if n]
+    for name in extra_names:
+        w2 = WORKLOADS[name]
         log(f"[bench] {w2.name}")
         res2 = time_workload(w2, args.steps, args.warmup)
         s2 = summarize(w2, res2, out_bytes=4)
         extra[w2.name] = {"ms_per_step": round(s2["ms"], 4), "tokens_per_s": round(s2["tokens_per_s"], 1),
                           "median_ms": round(s2["median_ms"], 4), "kernels": s2["kernels"],
-                          "path_hbm_frac": round(s2["path_gbps"] / HBM_PEAK_GBPS, 4)}
+                          "path_hbm_frac": round(s2["path_gbps"] / HBM_PEAK_GBPS, 4),
+                          "tpu_v7x_context_ms": TPU_V7X_CONTEXT_MS.get(w2.name)}
+        if not args.no_parity:
+            parities[w2.name] = oracle_parity(w2, res2["inp"], gpu_outputs(res2))
+            log(f"[bench] parity {w2.name} {parities[w2.name]}")
         del res2
     if args.gate_in_kernel and w.safe_gate:
         log(f"[bench] {w.name} with the gate activated in the kernel")
@@ -432,9 +492,7 @@ def main():
                                            "the same decay distribution, activated in the kernel"}
         del res3
     if args.bwd:
-        for wb in (w, WORKLOADS[args.extra] if args.extra else None):
-            if wb is None:
-                continue
+        for wb in [w] + [WORKLOADS[n] for n in extra_names if WORKLOADS[n].T >= 8192]:
             log(f"[bench] backward of {wb.name}")
             extra.setdefault("backward", {})[wb.name] = time_bwd(wb, args.steps, args.warmup)
     if args.cp:
@@ -456,6 +514,10 @@ def main():
         "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
     }
     print(json.dumps(line), flush=True)
+    bad = {n: p for n, p in parities.items() if max(p.values()) > PARITY_TOL_BF16}
+    if bad:
+        log(f"[bench] parity above {PARITY_TOL_BF16}: {bad}")
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -45,23 +45,38 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int64_t nc_fixed = 0, cmax = 0, smax = 0, record_bytes = 0;
-  size_t off_hdr = 0, off_segs = 0, off_chunks = 0, off_records = 0, total = 0;
+  size_t off_hdr = 0, off_segs = 0, off_chunks = 0, off_rows = 0, off_records = 0, total = 0;
 };
 
 bool is_pow_ok(int64_t d) { return d == 64 || d == 128; }
+
+// The integer a caller stored in an enum field or argument.  C callers (and
+// ctypes) can pass any int there; reading it as the enum type would be
+// undefined for values outside the enumerators, so its bytes are copied.
+int32_t enum_int(const kda_dtype_t& e) {
+  int32_t x;
+  static_assert(sizeof(x) == sizeof(e), "enum is int-sized");
+  std::memcpy(&x, &e, sizeof(x));
+  return x;
+}
+bool dtype_ok(const kda_dtype_t& e) { return enum_int(e) == KDA_F32 || enum_int(e) == KDA_BF16; }
+bool is_bf16(const kda_dtype_t& e) { return enum_int(e) == KDA_BF16; }
+
+// a * b into *out unless it overflows int64 (both >= 0).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
 kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
   if (d == nullptr) return fail(KDA_ERR_INVALID_ARGUMENT, "desc is NULL");
   if (d->B < 0 || d->T < 0 || d->H < 0)
     return fail(KDA_ERR_INVALID_ARGUMENT, "B, T and H must be >= 0");
-  if (d->T > (int64_t)1 << 30 || d->B * d->T > (int64_t)1 << 31)
+  int64_t tokens = 0;
+  if (d->T > (int64_t)1 << 30 || !mul_ok(d->B, d->T, &tokens) || tokens > (int64_t)1 << 31)
     return fail(KDA_ERR_NOT_IMPLEMENTED, "B*T above 2^31 tokens is not supported");
+  if (d->H > (int64_t)1 << 16) return fail(KDA_ERR_NOT_IMPLEMENTED, "more than 65536 heads is not supported");
   if (!is_pow_ok(d->K) || !is_pow_ok(d->V))
     return fail(KDA_ERR_NOT_IMPLEMENTED, "K and V must each be 64 or 128");
-  if (d->dtype != KDA_F32 && d->dtype != KDA_BF16)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_F32 or KDA_BF16");
-  if (d->o_dtype != KDA_F32 && d->o_dtype != KDA_BF16)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "o_dtype must be KDA_F32 or KDA_BF16");
+  if (!dtype_ok(d->dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_F32 or KDA_BF16");
+  if (!dtype_ok(d->o_dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "o_dtype must be KDA_F32 or KDA_BF16");
   if (d->chunk_size != 64) return fail(KDA_ERR_NOT_IMPLEMENTED, "chunk_size must be 64");
   if (d->use_qk_l2norm != 0 && d->use_qk_l2norm != 1)
     return fail(KDA_ERR_INVALID_ARGUMENT, "use_qk_l2norm must be 0 or 1");
@@ -73,8 +88,15 @@ kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
     return fail(KDA_ERR_INVALID_ARGUMENT, "scale must be finite (or NaN for 1/sqrt(K))");
   if (has_seg && d->max_segments < 1)
     return fail(KDA_ERR_INVALID_ARGUMENT, "packed input (segment_ids) needs max_segments >= 1");
+  // Every size below fits int64 (and size_t) once these hold.
+  int64_t slots = 0, chunk_slots = 0, rec_total = 0;
+  const int64_t n_seg = has_seg ? d->max_segments : 1;
+  if (!mul_ok(d->B, n_seg, &slots) || slots > (int64_t)1 << 31 ||
+      !mul_ok(d->B, (d->T + 63) / 64 + (has_seg ? d->max_segments : 0), &chunk_slots) ||
+      !mul_ok(chunk_slots, d->H, &rec_total) || !mul_ok(rec_total, (int64_t)1 << 22, &rec_total))
+    return fail(KDA_ERR_NOT_IMPLEMENTED, "the workspace for this request would not fit a 64-bit size");
 
-  const kda::InType in = d->dtype == KDA_BF16 ? kda::InType::BF16 : kda::InType::F32;
+  const kda::InType in = is_bf16(d->dtype) ? kda::InType::BF16 : kda::InType::F32;
   Plan p;
   p.nc_fixed = (d->T + 63) / 64;
   p.record_bytes = kda::record_bytes(in, d->K, d->V);
@@ -92,6 +114,8 @@ kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
   off = align_up(off + (has_seg ? (size_t)p.smax * sizeof(kda::SegEntry) : 0));
   p.off_chunks = off;
   off = align_up(off + (has_seg ? (size_t)p.cmax * sizeof(kda::ChunkEntry) : 0));
+  p.off_rows = off;
+  off = align_up(off + (has_seg ? (size_t)d->B * sizeof(kda::RowInfo) : 0));
   p.off_records = off;
   off = align_up(off + (size_t)p.cmax * (size_t)d->H * (size_t)p.record_bytes);
   p.total = off;
@@ -197,8 +221,8 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
 
   kda::CallArgs a{};
   a.B = d.B; a.T = d.T; a.H = d.H; a.K = d.K; a.V = d.V;
-  a.in = d.dtype == KDA_BF16 ? kda::InType::BF16 : kda::InType::F32;
-  a.out = d.o_dtype == KDA_BF16 ? kda::OutType::BF16 : kda::OutType::F32;
+  a.in = is_bf16(d.dtype) ? kda::InType::BF16 : kda::InType::F32;
+  a.out = is_bf16(d.o_dtype) ? kda::OutType::BF16 : kda::OutType::F32;
   a.scale = std::isnan(d.scale) ? (float)(1.0 / std::sqrt((double)d.K)) : d.scale;
   a.l2norm = d.use_qk_l2norm;
   a.n_max = has_seg ? d.max_segments : 0;
@@ -219,6 +243,7 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
   a.hdr = reinterpret_cast<kda::TableHeader*>(ws + plan.off_hdr);
   a.segs = reinterpret_cast<kda::SegEntry*>(ws + plan.off_segs);
   a.chunks = reinterpret_cast<kda::ChunkEntry*>(ws + plan.off_chunks);
+  a.rows = reinterpret_cast<kda::RowInfo*>(ws + plan.off_rows);
   a.records = ws + plan.off_records;
   a.record_bytes = plan.record_bytes;
   a.stream = static_cast<hipStream_t>(stream);
@@ -256,13 +281,13 @@ kda_status_t kda_short_conv_fwd(int64_t B, int64_t T, int64_t D, int32_t W, kda_
   if (W < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "W must be >= 1 (W = 0 disables the convolution: skip the call)");
   if (W > 8) return fail(KDA_ERR_NOT_IMPLEMENTED, "kernel sizes above 8 are not supported");
   if (D % 8 != 0) return fail(KDA_ERR_NOT_IMPLEMENTED, "D must be a multiple of 8");
-  if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_F32 or KDA_BF16");
+  if (!dtype_ok(dtype)) return fail(KDA_ERR_INVALID_ARGUMENT, "dtype must be KDA_F32 or KDA_BF16");
   if (B * T * D == 0) return KDA_OK;
   if (!x || !weight || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "x, weight and y must be non-NULL");
   if ((reinterpret_cast<uintptr_t>(x) & 15) || (reinterpret_cast<uintptr_t>(y) & 15) ||
       (reinterpret_cast<uintptr_t>(weight) & 3) || (reinterpret_cast<uintptr_t>(segment_ids) & 3))
     return fail(KDA_ERR_INVALID_ARGUMENT, "x and y must be 16-byte aligned, weight and segment_ids 4-byte aligned");
-  kda::ConvArgs a{B, T, D, W, dtype == KDA_BF16, x, weight, segment_ids, y, static_cast<hipStream_t>(stream)};
+  kda::ConvArgs a{B, T, D, W, is_bf16(dtype), x, weight, segment_ids, y, static_cast<hipStream_t>(stream)};
   const hipError_t e = observed("kda_short_conv", a.stream, [&] { return kda::launch_short_conv(a); });
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
   return KDA_OK;
@@ -273,15 +298,15 @@ kda_status_t kda_gated_rmsnorm_fwd(int64_t rows, int64_t V, kda_dtype_t o_dtype,
                                    float eps, void* y, void* stream) {
   if (rows < 0) return fail(KDA_ERR_INVALID_ARGUMENT, "rows must be >= 0");
   if (V != 64 && V != 128 && V != 256) return fail(KDA_ERR_NOT_IMPLEMENTED, "V must be 64, 128 or 256");
-  for (kda_dtype_t t : {o_dtype, gate_dtype, y_dtype})
-    if (t != KDA_F32 && t != KDA_BF16) return fail(KDA_ERR_INVALID_ARGUMENT, "dtypes must be KDA_F32 or KDA_BF16");
+  if (!dtype_ok(o_dtype) || !dtype_ok(gate_dtype) || !dtype_ok(y_dtype))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "dtypes must be KDA_F32 or KDA_BF16");
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(KDA_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
   if (rows == 0) return KDA_OK;
   if (!o || !gate || !weight || !y) return fail(KDA_ERR_INVALID_ARGUMENT, "o, gate, weight and y must be non-NULL");
   const void* ptrs[] = {o, gate, weight, y};
   for (const void* p : ptrs)
     if (reinterpret_cast<uintptr_t>(p) & 3) return fail(KDA_ERR_INVALID_ARGUMENT, "pointers must be 4-byte aligned");
-  kda::NormArgs a{rows, V, o_dtype == KDA_BF16, gate_dtype == KDA_BF16, y_dtype == KDA_BF16, o, gate, weight, eps, y,
+  kda::NormArgs a{rows, V, is_bf16(o_dtype), is_bf16(gate_dtype), is_bf16(y_dtype), o, gate, weight, eps, y,
                   static_cast<hipStream_t>(stream)};
   const hipError_t e = observed("kda_gated_rmsnorm", a.stream, [&] { return kda::launch_gated_rmsnorm(a); });
   if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
@@ -321,8 +346,10 @@ kda_status_t cp_validate(const kda_cp_desc_t* d) {
   if (d->T % d->P != 0) return fail(KDA_ERR_INVALID_ARGUMENT, "T must be a multiple of P");
   if (d->n_states < 1) return fail(KDA_ERR_INVALID_ARGUMENT, "n_states must be >= 1");
   if (!is_pow_ok(d->K) || !is_pow_ok(d->V)) return fail(KDA_ERR_NOT_IMPLEMENTED, "K and V must each be 64 or 128");
-  if (d->B * d->P * d->n_states * d->H > (int64_t)INT32_MAX)
-    return fail(KDA_ERR_NOT_IMPLEMENTED, "B * P * n_states * H above 2^31 is not supported");
+  int64_t n = 0;
+  if (!mul_ok(d->B, d->P, &n) || !mul_ok(n, d->n_states, &n) || !mul_ok(n, d->H, &n) || n > (int64_t)INT32_MAX ||
+      d->T > (int64_t)1 << 30)
+    return fail(KDA_ERR_NOT_IMPLEMENTED, "B * P * n_states * H above 2^31 (or T above 2^30) is not supported");
   return KDA_OK;
 }
 
@@ -487,7 +514,7 @@ kda_status_t backward(const kda_fwd_desc_t* desc, const void* q, const void* k, 
   char* ws = static_cast<char*>(workspace);
   kda::CallArgs t{};   // the segment tables, built as for the forward
   t.B = d.B; t.T = d.T; t.H = d.H; t.K = d.K; t.V = d.V;
-  t.in = d.dtype == KDA_BF16 ? kda::InType::BF16 : kda::InType::F32;
+  t.in = is_bf16(d.dtype) ? kda::InType::BF16 : kda::InType::F32;
   t.out = kda::OutType::F32;
   t.n_max = has_seg ? d.max_segments : 0;
   t.nc_fixed = bp.t.nc_fixed;
@@ -497,6 +524,7 @@ kda_status_t backward(const kda_fwd_desc_t* desc, const void* q, const void* k, 
   t.hdr = reinterpret_cast<kda::TableHeader*>(ws + bp.t.off_hdr);
   t.segs = reinterpret_cast<kda::SegEntry*>(ws + bp.t.off_segs);
   t.chunks = reinterpret_cast<kda::ChunkEntry*>(ws + bp.t.off_chunks);
+  t.rows = reinterpret_cast<kda::RowInfo*>(ws + bp.t.off_rows);
   t.stream = s;
   const int64_t slot_elems = d.H * d.K * d.V;
   hipError_t e = hipSuccess;
@@ -520,7 +548,7 @@ kda_status_t backward(const kda_fwd_desc_t* desc, const void* q, const void* k, 
     kda::BwdArgs a{};
     a.B = d.B; a.T = d.T; a.H = d.H; a.K = d.K; a.V = d.V;
     a.in = t.in;
-    a.do_bf16 = d.o_dtype == KDA_BF16;
+    a.do_bf16 = is_bf16(d.o_dtype);
     a.scale = std::isnan(d.scale) ? (float)(1.0 / std::sqrt((double)d.K)) : d.scale;
     a.l2norm = d.use_qk_l2norm;
     a.n_max = t.n_max;

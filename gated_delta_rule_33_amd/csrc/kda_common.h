@@ -290,6 +290,11 @@ struct SegEntry {
   int32_t chunk_begin, n_chunks; // global chunk index of its first chunk, chunk count
   int32_t pad0, pad1;
 };
+// Per row of packed input: the state slots its segments fill and the first
+// token of its unrecorded segments (T when all are recorded).
+struct RowInfo {
+  int32_t n_recorded, tail_t0;
+};
 struct TableHeader {
   int32_t n_segments;   // recorded segments (all rows)
   int32_t n_chunks;     // chunks of recorded segments

@@ -38,6 +38,7 @@ struct CallArgs {
   TableHeader* hdr;
   SegEntry* segs;
   ChunkEntry* chunks;
+  RowInfo* rows;
   char* records;
   int64_t record_bytes;
   hipStream_t stream;

@@ -10,8 +10,10 @@
 //
 // Workgroup 0 builds the tables row by row with block-wide prefix sums; the
 // other workgroups write o = 0 for padding tokens.  Segments past max_segments
-// in a row are not recorded: workgroup 0 zeroes their outputs and raises
-// KDA_FLAG_SEGMENT_OVERFLOW.
+// in a row are not recorded: workgroup 0 raises KDA_FLAG_SEGMENT_OVERFLOW and
+// notes per row where the unrecorded tokens begin and how many state slots
+// were filled; a second, grid-wide kernel then zeroes the outputs of the
+// unrecorded tokens and the final states of the slots no segment reaches.
 #include "kda_launch.h"
 
 namespace kda {
@@ -59,6 +61,7 @@ struct PrepParams {
   TableHeader* hdr;
   SegEntry* segs;
   ChunkEntry* chunks;
+  RowInfo* rows;
   void* o;
   float* fin;
 };
@@ -154,17 +157,17 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
         p.chunks[se.chunk_begin + c] = ce;
       }
     }
-    // Outputs of unrecorded segments are zero; so are the final states of
-    // slots no segment of this row reaches.
-    if (row_segs > p.n_max && o != nullptr) {
-      const SegEntry last = p.segs[seg_base + nrec - 1];
-      for (int64_t t = last.t0 + last.len; t < T; ++t)
-        if (row[t] != 0) zero_token(o, b * T + t, HV, tid, kPrepThreads);
-    }
-    if (p.fin) {
-      const int64_t slot_elems = p.H * p.K * p.V;
-      for (int64_t e = (int64_t)nrec * slot_elems + tid; e < (int64_t)p.n_max * slot_elems; e += kPrepThreads)
-        p.fin[b * p.n_max * slot_elems + e] = 0.f;
+    // Where the row's unrecorded tokens begin (T when every segment is
+    // recorded) and how many state slots its segments fill.
+    if (tid == 0) {
+      RowInfo ri;
+      ri.n_recorded = nrec;
+      ri.tail_t0 = (int)T;
+      if (row_segs > p.n_max) {
+        const SegEntry last = p.segs[seg_base + nrec - 1];
+        ri.tail_t0 = last.t0 + last.len;
+      }
+      p.rows[b] = ri;
     }
     seg_base += nrec;
     __syncthreads();
@@ -176,6 +179,35 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
   }
 }
 
+// Grid-wide zeroing after the tables: the outputs of tokens of unrecorded
+// segments (a row with more than max_segments segments) and the final states
+// of the slots no segment of a row reaches.  One wave per token or per
+// (row, slot, head) state block.
+constexpr int kTailThreads = 256;
+
+template <class TO>
+__global__ __launch_bounds__(kTailThreads) void kda_prep_tail_kernel(PrepParams p) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * (kTailThreads / 64) + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * (kTailThreads / 64);
+  const int64_t HV = p.H * p.V, KV = p.K * p.V;
+  TO* o = static_cast<TO*>(p.o);
+  if (o != nullptr) {
+    for (int64_t tok = wave; tok < p.B * p.T; tok += n_waves) {
+      const int64_t b = tok / p.T, t = tok % p.T;
+      if (t >= p.rows[b].tail_t0 && p.ids[tok] != 0) zero_token(o, tok, HV, lane, 64);
+    }
+  }
+  if (p.fin != nullptr) {
+    for (int64_t blk = wave; blk < p.B * p.n_max * p.H; blk += n_waves) {
+      const int64_t b = blk / ((int64_t)p.n_max * p.H), local = (blk / p.H) % p.n_max;
+      if (local < p.rows[b].n_recorded) continue;
+      f32x4* dst = reinterpret_cast<f32x4*>(p.fin + blk * KV);
+      for (int64_t e = lane; e < KV / 4; e += 64) dst[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
 __global__ void kda_fill_zero_kernel(float* x, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     x[i] = 0.f;
@@ -184,7 +216,7 @@ __global__ void kda_fill_zero_kernel(float* x, int64_t n) {
 }  // namespace
 
 hipError_t launch_prep(const CallArgs& a) {
-  PrepParams p{a.seg_ids, a.B, a.T, a.H, a.K, a.V, a.n_max, a.hdr, a.segs, a.chunks, a.o, a.fin};
+  PrepParams p{a.seg_ids, a.B, a.T, a.H, a.K, a.V, a.n_max, a.hdr, a.segs, a.chunks, a.rows, a.o, a.fin};
   const int64_t tokens = a.B * a.T;
   const int zero_groups = (int)std::min<int64_t>(256, (tokens + 15) / 16);
   const dim3 grid(1 + zero_groups);
@@ -192,6 +224,14 @@ hipError_t launch_prep(const CallArgs& a) {
     hipLaunchKernelGGL(kda_prep_kernel<float>, grid, dim3(kPrepThreads), 0, a.stream, p);
   else
     hipLaunchKernelGGL(kda_prep_kernel<uint16_t>, grid, dim3(kPrepThreads), 0, a.stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || (a.o == nullptr && a.fin == nullptr)) return e;
+  const int64_t waves = std::max<int64_t>(tokens, a.B * a.n_max * a.H);
+  const unsigned tail_groups = (unsigned)std::min<int64_t>(1024, (waves + 3) / 4);
+  if (a.out == OutType::F32)
+    hipLaunchKernelGGL(kda_prep_tail_kernel<float>, dim3(tail_groups), dim3(kTailThreads), 0, a.stream, p);
+  else
+    hipLaunchKernelGGL(kda_prep_tail_kernel<uint16_t>, dim3(tail_groups), dim3(kTailThreads), 0, a.stream, p);
   return hipGetLastError();
 }
 

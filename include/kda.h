@@ -66,10 +66,13 @@ typedef struct {
 } kda_fwd_desc_t;
 
 /*
- * Bytes of device workspace kda_chunk_fwd needs for `desc`.  Depends only on
- * the descriptor (sizes, dtype, max_segments, whether segments are given is
- * taken from max_segments > 0).  Returns INVALID_ARGUMENT / NOT_IMPLEMENTED
- * for descriptors kda_chunk_fwd would reject.
+ * Bytes of device workspace kda_chunk_fwd needs for `desc` and for whether
+ * segment_ids will be passed: has_segment_ids must be non-zero exactly when
+ * the forward call will get a non-NULL segment_ids (the segment and chunk
+ * tables are only laid out then).  The size depends on nothing else (sizes,
+ * dtype, max_segments).  Returns INVALID_ARGUMENT / NOT_IMPLEMENTED for
+ * descriptors kda_chunk_fwd would reject (with has_segment_ids non-zero,
+ * max_segments < 1 is INVALID_ARGUMENT).
  */
 kda_status_t kda_chunk_fwd_workspace_size(const kda_fwd_desc_t* desc, int has_segment_ids,
                                           size_t* bytes);
