@@ -15,6 +15,7 @@
 #include <cstdint>
 #include <cstring>
 #include <initializer_list>
+#include <mutex>
 #include <string>
 
 #include "kda.h"
@@ -188,6 +189,59 @@ kda_status_t kda_chunk_fwd_rerun(const kda_fwd_desc_t* desc, const float* initia
   x.rerun = true;
   return forward(desc, nullptr, nullptr, nullptr, nullptr, nullptr, x, initial_state, segment_ids, o, final_state,
                  workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// The forward's workspace for callers that cannot allocate: a fixed region
+// in device memory, one copy per GPU, held until the process ends.  In host
+// code `scratch` only names the symbol; its device address (different on
+// every GPU) is looked up once per device with hipGetSymbolAddress and used
+// from then on.
+__device__ __attribute__((aligned(256))) char scratch[KDA_STATIC_WORKSPACE_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kda_status_t static_workspace(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KDA_ERR_NOT_IMPLEMENTED, "device index above 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr)
+      return fail(KDA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status_t kda_chunk_fwd_noalloc(const kda_fwd_desc_t* desc, const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta, const float* initial_state,
+                                   const int32_t* segment_ids, void* o, float* final_state, void* stream) {
+  Plan plan;
+  kda_status_t st = validate(desc, segment_ids != nullptr, &plan);
+  if (st != KDA_OK) return st;
+  if (plan.total > (size_t)KDA_STATIC_WORKSPACE_BYTES)
+    return fail(KDA_ERR_WORKSPACE_TOO_SMALL, "this forward needs " + std::to_string(plan.total) +
+                                                 " bytes of workspace; the fixed region holds " +
+                                                 std::to_string((size_t)KDA_STATIC_WORKSPACE_BYTES));
+  void* ws = nullptr;
+  st = static_workspace(&ws);
+  if (st != KDA_OK) return st;
+  return forward(desc, q, k, v, g, beta, FwdExtra{}, initial_state, segment_ids, o, final_state, ws,
+                 (size_t)KDA_STATIC_WORKSPACE_BYTES, stream);
 }
 
 }  // extern "C"

@@ -20,8 +20,10 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
+KDA_STATIC_WORKSPACE_BYTES = 64 << 20   # the fixed workspace region of kda_chunk_fwd_noalloc, per GPU
 
-EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_gated", "kda_chunk_fwd_transition",
+EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_gated",
+            "kda_chunk_fwd_transition",
             "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_chunk_bwd_rerun", "kda_cp_gather_final_grads",
             "kda_cp_chain_bwd", "kda_cp_scatter_initial_grads",
             "kda_chunk_fwd_rerun", "kda_cp_plan", "kda_cp_gather_states", "kda_cp_chain", "kda_cp_scatter_states",
@@ -68,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_workspace_size.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_gated.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
     lib.kda_chunk_fwd_transition.argtypes = [ctypes.POINTER(KdaFwdDesc), p, p, p, p, p, p, p, p, p, p, p, sz, p]

@@ -106,6 +106,28 @@ kda_status_t kda_chunk_fwd(const kda_fwd_desc_t* desc,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same forward, with its workspace taken from a fixed region of device
+ * memory inside the library instead of a caller's buffer.  The region holds
+ * KDA_STATIC_WORKSPACE_BYTES; each GPU the library runs on keeps its own copy
+ * from the library's load until the process ends.  A request whose
+ * kda_chunk_fwd_workspace_size exceeds it returns KDA_ERR_WORKSPACE_TOO_SMALL
+ * and enqueues nothing.  The call itself allocates nothing.  The region of
+ * the current device is used (the stream must belong to it); every call on
+ * one GPU shares it, so calls that overlap in time on one GPU (other streams,
+ * other threads) race and their results are undefined.  The segment-overflow
+ * flag of such a call cannot be read back.  All other arguments, the results
+ * and the errors are those of kda_chunk_fwd.
+ */
+#define KDA_STATIC_WORKSPACE_BYTES (64u << 20)
+kda_status_t kda_chunk_fwd_noalloc(const kda_fwd_desc_t* desc,
+                                   const void* q, const void* k, const void* v,
+                                   const void* g, const void* beta,
+                                   const float* initial_state, const int32_t* segment_ids,
+                                   void* o, float* final_state, void* stream);
+
+/*
  * The forward with the gate activated inside the kernel (chunk_kda options
  * use_gate_in_kernel, A_log and dt_bias of the page "feat(kda): integrate KDA
  * attention with tokamax backend and CP support", Public API; the layer's
