@@ -51,10 +51,12 @@ PARITY_TOL_BF16 = 2e-2          # max|err| / rms(ref) for bf16 inputs
 
 
 KERNEL_SOURCES = {   # sources a kernel's code depends on (its traffic figures go stale when they change)
-    "kda_intra": ["kda_intra.hip", "kda_common.h", "kda_launch.h"],
+    "kda_intra": ["kda_intra.hip", "kda_intra_item.h", "kda_common.h", "kda_launch.h"],
+    "kda_fused": ["kda_fused.hip", "kda_intra_item.h", "kda_common.h", "kda_launch.h"],
     "kda_recur": ["kda_recur.hip", "kda_common.h", "kda_launch.h"],
     "kda_prep": ["kda_prep.hip", "kda_common.h", "kda_launch.h"],
 }
+PATH_STEPS = ("kda_prep", "kda_intra", "kda_recur")   # the steps of one forward (kda_fused does the last two)
 COPY_CALIBRATION_MIB = 512
 
 
@@ -104,7 +106,8 @@ def algorithmic(w, out_bytes: int):
     multiply-add, triangles at their true size) per 64-token chunk and head:
     A 258k + Aqk 266k + solve 44k + W 266k + U 266k MAC in the intra-chunk
     kernel; Delta 1049k + Qg S 1049k + Aqk Delta 266k + state update 1049k
-    MAC in the recurrence (for K = V = 128)."""
+    MAC in the recurrence (for K = V = 128).  The fused kernel does the work
+    of both (its records never reach HBM by design)."""
     es = 2 if w.dtype == "bf16" else 4
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     tok = B * T * H
@@ -119,6 +122,7 @@ def algorithmic(w, out_bytes: int):
         "kda_prep": dict(bytes=prep_bytes, flops=0.0),
         "kda_intra": dict(bytes=intra_bytes, flops=2.0 * chunks * 1.10e6 * scale),
         "kda_recur": dict(bytes=recur_bytes, flops=2.0 * chunks * 3.413e6 * scale),
+        "kda_fused": dict(bytes=intra_bytes + recur_bytes, flops=2.0 * chunks * (1.10e6 + 3.413e6) * scale),
     }
 
 
@@ -325,7 +329,7 @@ def path_survey_bytes(w):
     """Algorithmic bytes of the whole forward with a bf16 output (the pages'
     output dtype): inputs read once, o in bf16 and the fp32 states written once."""
     alg = algorithmic(w, out_bytes=2)
-    return sum(a["bytes"] for a in alg.values())
+    return sum(alg[n]["bytes"] for n in PATH_STEPS)
 
 
 def summarize(w, res, out_bytes):
@@ -340,8 +344,8 @@ def summarize(w, res, out_bytes):
                           achieved_gbps=round(a["bytes"] / (avg * 1e-3) / 1e9, 1) if avg > 0 else None,
                           achieved_tflops=round(a["flops"] / (avg * 1e-3) / 1e12, 2) if avg > 0 else None)
     dom = max(kern, key=lambda n: kern[n]["avg_us"])
-    path_bytes = sum(a["bytes"] for a in alg.values())
-    path_flops = sum(a["flops"] for a in alg.values())
+    path_bytes = sum(alg[n]["bytes"] for n in PATH_STEPS)
+    path_flops = sum(alg[n]["flops"] for n in PATH_STEPS)
     return dict(ms=ms, median_ms=statistics.median(res["step_ms"]), min_ms=min(res["step_ms"]),
                 max_ms=max(res["step_ms"]), tokens_per_s=w.B * w.T / (ms * 1e-3), kernels=kern, dominant=dom,
                 path_gbps=path_bytes / (ms * 1e-3) / 1e9, path_tflops=path_flops / (ms * 1e-3) / 1e12,

@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_intra.hip", "kda_recur.hip", "kda_layer.hip", "kda_cp.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_intra.hip", "kda_fused.hip", "kda_recur.hip", "kda_layer.hip",
+           "kda_cp.hip", "kda_bwd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),

@@ -26,6 +26,7 @@ namespace {
 thread_local std::string g_last_error;
 kda_launch_observer_t g_observer = nullptr;
 void* g_observer_user = nullptr;
+bool g_fused_forward = true;
 
 // Enqueue one kernel, with the observer (if any) called around it.
 template <class F>
@@ -46,7 +47,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int64_t nc_fixed = 0, cmax = 0, smax = 0, record_bytes = 0;
-  size_t off_hdr = 0, off_segs = 0, off_chunks = 0, off_rows = 0, off_records = 0, total = 0;
+  size_t off_hdr = 0, off_segs = 0, off_chunks = 0, off_rows = 0, off_records = 0, off_fused = 0, total = 0;
 };
 
 bool is_pow_ok(int64_t d) { return d == 64 || d == 128; }
@@ -119,6 +120,9 @@ kda_status_t validate(const kda_fwd_desc_t* d, bool has_seg, Plan* plan) {
   off = align_up(off + (has_seg ? (size_t)d->B * sizeof(kda::RowInfo) : 0));
   p.off_records = off;
   off = align_up(off + (size_t)p.cmax * (size_t)d->H * (size_t)p.record_bytes);
+  p.off_fused = off;   // scheduling words, ready words and lane states of the fused forward
+  off = align_up(off + sizeof(kda::FusedCtl) + (size_t)p.cmax * (size_t)d->H * sizeof(uint32_t));
+  off = align_up(off + (has_seg ? 0 : (size_t)d->B * (size_t)d->H * (size_t)d->K * (size_t)d->V * sizeof(float)));
   p.total = off;
   *plan = p;
   return KDA_OK;
@@ -299,6 +303,12 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
   a.chunks = reinterpret_cast<kda::ChunkEntry*>(ws + plan.off_chunks);
   a.rows = reinterpret_cast<kda::RowInfo*>(ws + plan.off_rows);
   a.records = ws + plan.off_records;
+  a.fused_ctl = reinterpret_cast<kda::FusedCtl*>(ws + plan.off_fused);
+  a.fused_ready = reinterpret_cast<uint32_t*>(ws + plan.off_fused + sizeof(kda::FusedCtl));
+  a.fused_lane_state = has_seg ? nullptr
+                               : reinterpret_cast<float*>(ws + align_up(plan.off_fused + sizeof(kda::FusedCtl) +
+                                                                        (size_t)plan.cmax * (size_t)d.H * 4));
+  a.n_xcd = kda::xcd_count();
   a.record_bytes = plan.record_bytes;
   a.stream = static_cast<hipStream_t>(stream);
 
@@ -311,11 +321,15 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
     if (e != hipSuccess) return fail(KDA_ERR_HIP, std::string("launch: ") + hipGetErrorString(e));
     return KDA_OK;
   }
-  if (!x.rerun) {
-    if (has_seg) e = observed("kda_prep", s, [&] { return kda::launch_prep(a); });
-    if (e == hipSuccess) e = observed("kda_intra", s, [&] { return kda::launch_intra(a); });
+  if (!x.rerun && g_fused_forward && kda::fused_supported(a)) {
+    e = observed("kda_fused", s, [&] { return kda::launch_fused(a); });
+  } else {
+    if (!x.rerun) {
+      if (has_seg) e = observed("kda_prep", s, [&] { return kda::launch_prep(a); });
+      if (e == hipSuccess) e = observed("kda_intra", s, [&] { return kda::launch_intra(a); });
+    }
+    if (e == hipSuccess) e = observed("kda_recur", s, [&] { return kda::launch_recur(a); });
   }
-  if (e == hipSuccess) e = observed("kda_recur", s, [&] { return kda::launch_recur(a); });
   if (e == hipSuccess && a.trans != nullptr) {
     kda::CallArgs t = a;
     t.trans_only = true;
@@ -379,6 +393,8 @@ kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, 
   *flags = hdr.flags;
   return KDA_OK;
 }
+
+void kda_set_fused_forward(int enable) { g_fused_forward = enable != 0; }
 
 void kda_set_launch_observer(kda_launch_observer_t fn, void* user) {
   g_observer = fn;

@@ -295,6 +295,15 @@ struct SegEntry {
 struct RowInfo {
   int32_t n_recorded, tail_t0;
 };
+// Scheduling words of the fused forward (zeroed before every call): arrivals
+// per (XCD, compute unit) decide the workgroup's role, and per-XCD tickets
+// hand out recurrence lanes and records to produce.
+struct FusedCtl {
+  uint32_t cu_arrivals[8][256];
+  uint32_t lane_ticket[8];
+  uint32_t item_ticket[8];
+  uint32_t pad[48];
+};
 struct TableHeader {
   int32_t n_segments;   // recorded segments (all rows)
   int32_t n_chunks;     // chunks of recorded segments

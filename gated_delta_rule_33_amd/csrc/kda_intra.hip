@@ -24,12 +24,15 @@
 // split is used while span <= 64 (always true under the safe-gate bound
 // g >= -5 of the chunk_kda options, where span <= 75 is possible only at the
 // very edge) and the block is evaluated pair by pair otherwise.
-#include "kda_launch.h"
+#include <cstring>
+
+#include "kda_intra_item.h"
 
 namespace kda {
 namespace {
 
-constexpr float kSpanMax = 64.f;
+using namespace detail;
+
 constexpr int kIntraWaves = 8;                       // two per SIMD
 constexpr int kIntraThreads = kIntraWaves * kWave;
 
@@ -87,23 +90,6 @@ struct IntraSmem {
   __device__ float* red_buf() { return kRedInQ ? reinterpret_cast<float*>(q) : scratch; }
 };
 
-// Activated log decay of the in-kernel gate for z = exp(A_log) (g + dt_bias):
-// mode 2 (safe gate) lower_bound * sigmoid(z), mode 1 log sigmoid(z) in the
-// form min(z, 0) - log(1 + exp(-|z|)), which neither overflows nor cancels.
-// Hardware exp, log and reciprocal (about one ulp each): the absolute error
-// of g stays near 1e-7, far below what the bf16 operands carry.
-__device__ __forceinline__ float gate_log_decay(int mode, float lower_bound, float z) {
-  if (mode == 2) return lower_bound * __builtin_amdgcn_rcpf(1.f + __expf(-z));
-  return fminf(z, 0.f) - __logf(1.f + __expf(-fabsf(z)));
-}
-
-// Four consecutive elements as floats.
-__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-__device__ __forceinline__ f32x4 ld4(const uint16_t* p) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
-  return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
-               __uint_as_float(v.y & 0xffff0000u)};
-}
 __device__ __forceinline__ float ld1(const float* p) { return *p; }
 // Two consecutive elements (even offset) as floats.
 __device__ __forceinline__ void ld2(const float* p, float& a, float& b) {
@@ -151,94 +137,6 @@ __device__ __forceinline__ void issue_rows(TI* lds, const TI* src, int64_t row_s
 
 // Wait for every outstanding vector memory operation of this wave.
 __device__ __forceinline__ void wait_loads() { vm_wait<0>(); }
-
-// A copy of x the compiler cannot see through.  Per-lane LDS addresses derived
-// from it inside the item loop are recomputed per item instead of being
-// hoisted out of the loop, where they would all stay live and spill.
-__device__ __forceinline__ int opaque(int x) {
-  int y;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(y) : "v"(x));
-  return y;
-}
-
-// 16-deep fp32 product on the matrix cores: element s of lane group g holds k = 4g + s.
-__device__ __forceinline__ void mma16_f32(f32x4& c, const float a[4], const float b[4]) {
-#pragma unroll
-  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
-}
-
-struct IntraParams {
-  const void *q, *k, *v, *g, *beta;
-  int gate_mode;               // 0: g is the log decay; 1: log sigmoid(z); 2: lower_bound * sigmoid(z)
-  float lower_bound;
-  const float *a_log, *dt_bias;
-  int64_t B, T, H;
-  float scale;
-  int l2norm;
-  int64_t nc_fixed;          // chunks per row (fixed rows)
-  int packed;
-  TableHeader* hdr;
-  const ChunkEntry* chunks;
-  char* records;
-  int64_t record_bytes;
-};
-
-struct ItemInfo {
-  int64_t h, tok0;   // head, first token's row index b * T + t0
-  int len;
-};
-
-// Position of an item = chunk * H + h, with chunk = b * nc_fixed + ci for
-// fixed rows.  Integer division is a long instruction sequence on the GPU,
-// so it is done once per workgroup; the item loop advances the position by
-// a constant stride with carries.
-struct ItemPos {
-  int64_t chunk, h, b, ci;
-};
-
-__device__ __forceinline__ ItemPos item_pos(const IntraParams& p, int64_t item) {
-  ItemPos q;
-  q.h = item % p.H;
-  q.chunk = item / p.H;
-  q.b = p.packed ? 0 : q.chunk / p.nc_fixed;
-  q.ci = p.packed ? 0 : q.chunk % p.nc_fixed;
-  return q;
-}
-
-// q moved back by d (a position used as a stride: d.chunk whole chunks and
-// d.h heads, d.ci < nc_fixed after d.b whole rows), with borrows instead of
-// an integer division per item.
-__device__ __forceinline__ ItemPos item_retreat(const IntraParams& p, ItemPos q, const ItemPos& d) {
-  q.h -= d.h;
-  q.chunk -= d.chunk;
-  q.b -= d.b;
-  q.ci -= d.ci;
-  if (q.h < 0) {
-    q.h += p.H;
-    q.chunk -= 1;
-    q.ci -= 1;
-  }
-  if (!p.packed && q.ci < 0) {
-    q.ci += p.nc_fixed;
-    q.b -= 1;
-  }
-  return q;
-}
-
-__device__ __forceinline__ ItemInfo item_info(const IntraParams& p, const ItemPos& q) {
-  ItemInfo it;
-  it.h = q.h;
-  if (p.packed) {
-    const ChunkEntry ce = p.chunks[q.chunk];
-    it.tok0 = (int64_t)ce.b * p.T + ce.t0;
-    it.len = ce.len;
-  } else {
-    const int64_t t0 = q.ci * kChunk;
-    it.tok0 = q.b * p.T + t0;
-    it.len = (int)min<int64_t>(kChunk, p.T - t0);
-  }
-  return it;
-}
 
 // One workgroup per CU, looping over (chunk, head) items.  The inputs of the
 // next item are loaded into LDS (direct-to-LDS, asynchronous) while the
@@ -929,6 +827,34 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 }
 
 
+// bf16 inputs: one item per workgroup of four waves, items from the last
+// back (the last workgroups to run write the records of the first chunks,
+// which the recurrence reads first); about 66 KB of LDS, two per CU.
+template <int K, int V>
+__global__ __launch_bounds__(256, 2) void kda_intra4_kernel(IntraParams p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  const int64_t n_items = p.packed ? (int64_t)p.hdr->n_chunks * p.H : p.B * p.nc_fixed * p.H;
+  if (!p.packed && blockIdx.x == 0 && threadIdx.x == 0) p.hdr->flags = 0;   // no tables without segments
+  if ((int64_t)blockIdx.x >= n_items) return;
+  intra4_item<K, V>(p, n_items - 1 - (int64_t)blockIdx.x, smem_raw);
+}
+
+template <int K, int V>
+hipError_t launch_intra4_t(const CallArgs& a) {
+  IntraParams p{a.q, a.k, a.v, a.g, a.beta, a.gate_mode, a.lower_bound, a.a_log, a.dt_bias, a.B, a.T, a.H,
+                a.scale, a.l2norm, a.nc_fixed,
+                a.n_max > 0, a.hdr, a.chunks, a.records, a.record_bytes};
+  const size_t smem = sizeof(Intra4Smem<K, V>);
+  auto kern = kda_intra4_kernel<K, V>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  const int64_t items = (a.n_max > 0 ? a.cmax : a.B * a.nc_fixed) * a.H;
+  if (items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(256), smem, a.stream, p);
+  return hipGetLastError();
+}
+
 template <class TI, int K, int V>
 hipError_t launch_intra_t(const CallArgs& a) {
   IntraParams p{a.q, a.k, a.v, a.g, a.beta, a.gate_mode, a.lower_bound, a.a_log, a.dt_bias, a.B, a.T, a.H,
@@ -961,13 +887,32 @@ int64_t record_bytes(InType in, int64_t K, int64_t V) {
 
 hipError_t launch_intra(const CallArgs& a) {
 #define KDA_LI(TI, KK, VV) if (a.K == KK && a.V == VV) return launch_intra_t<TI, KK, VV>(a);
+#define KDA_LI4(KK, VV) if (a.K == KK && a.V == VV) return launch_intra4_t<KK, VV>(a);
   if (a.in == InType::BF16) {
-    KDA_LI(uint16_t, 64, 64) KDA_LI(uint16_t, 64, 128) KDA_LI(uint16_t, 128, 64) KDA_LI(uint16_t, 128, 128)
+    KDA_LI4(64, 64) KDA_LI4(64, 128) KDA_LI4(128, 64) KDA_LI4(128, 128)
   } else {
     KDA_LI(float, 64, 64) KDA_LI(float, 64, 128) KDA_LI(float, 128, 64) KDA_LI(float, 128, 128)
   }
 #undef KDA_LI
+#undef KDA_LI4
   return hipErrorInvalidValue;
+}
+
+// XCDs of the current device: 8 on a gfx950 device with 256 compute units
+// (32 per XCD); 0 (unknown) elsewhere, which keeps the fused forward off.
+int xcd_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] == 0) {
+    hipDeviceProp_t prop;
+    int n = -1;
+    if (hipGetDeviceProperties(&prop, dev) == hipSuccess && std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+        prop.multiProcessorCount % 32 == 0 && prop.multiProcessorCount / 32 <= 8)
+      n = prop.multiProcessorCount / 32;
+    cached[dev] = n;
+  }
+  return cached[dev] > 0 ? cached[dev] : 0;
 }
 
 // Compute units of the current device (cached per device).

@@ -41,6 +41,10 @@ struct CallArgs {
   RowInfo* rows;
   char* records;
   int64_t record_bytes;
+  FusedCtl* fused_ctl;         // fused forward: scheduling words, then one ready word per record
+  uint32_t* fused_ready;
+  float* fused_lane_state;     // fused forward: state slices of suspended recurrence lanes [B*H*K*V]
+  int n_xcd;                   // XCDs of the device (0: unknown, no fused forward)
   hipStream_t stream;
 };
 
@@ -107,6 +111,11 @@ int64_t bwd_record_floats(int64_t K, int64_t V);
 
 hipError_t launch_prep(const CallArgs& a);
 hipError_t launch_intra(const CallArgs& a);
+// The fused forward (bf16, no segment ids, K = V = 128) on devices whose XCDs
+// hold 32 compute units each.
+bool fused_supported(const CallArgs& a);
+hipError_t launch_fused(const CallArgs& a);
+int xcd_count();
 hipError_t launch_recur(const CallArgs& a);
 hipError_t launch_zero_states(const CallArgs& a);
 hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t stream);

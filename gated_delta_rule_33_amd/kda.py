@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libkda.so")
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
+KDA_FLAG_FUSED_TIMEOUT = 0x2
 KDA_STATIC_WORKSPACE_BYTES = 64 << 20   # the fixed workspace region of kda_chunk_fwd_noalloc, per GPU
 
 EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_gated",
@@ -27,7 +28,7 @@ EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noal
             "kda_chunk_bwd_workspace_size", "kda_chunk_bwd", "kda_chunk_bwd_rerun", "kda_cp_gather_final_grads",
             "kda_cp_chain_bwd", "kda_cp_scatter_initial_grads",
             "kda_chunk_fwd_rerun", "kda_cp_plan", "kda_cp_gather_states", "kda_cp_chain", "kda_cp_scatter_states",
-            "kda_short_conv_fwd", "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer",
+            "kda_short_conv_fwd", "kda_gated_rmsnorm_fwd", "kda_chunk_fwd_flags", "kda_set_launch_observer", "kda_set_fused_forward",
             "kda_last_error", "kda_version")
 
 # void (*)(const char* kernel_name, void* stream, int phase, void* user)
@@ -104,6 +105,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_flags.restype = ctypes.c_int
     lib.kda_set_launch_observer.argtypes = [LAUNCH_OBSERVER, ctypes.c_void_p]
     lib.kda_set_launch_observer.restype = None
+    lib.kda_set_fused_forward.argtypes = [ctypes.c_int]
+    lib.kda_set_fused_forward.restype = None
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.restype = ctypes.c_char_p
     _lib = lib
@@ -296,6 +299,13 @@ def gated_rmsnorm(o, gate, weight, eps: float = 1e-6, out_dtype=None, out=None):
                                                     float(eps), _ptr(y), ctypes.c_void_p(stream)),
                "kda_gated_rmsnorm_fwd")
     return y
+
+
+def set_fused_forward(enable: bool) -> None:
+    """Select the forward schedule for later calls (process-wide): the fused
+    persistent kernel where it applies (default), or always the two-kernel
+    path (intra-chunk kernel, then recurrence kernel)."""
+    load_library().kda_set_fused_forward(1 if enable else 0)
 
 
 def set_launch_observer(fn):

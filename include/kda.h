@@ -49,6 +49,9 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
 /* Flags reported by kda_chunk_fwd_flags(). */
 #define KDA_FLAG_SEGMENT_OVERFLOW 0x1u  /* a row held more than max_segments segments */
+#define KDA_FLAG_FUSED_TIMEOUT 0x2u     /* the fused forward gave up waiting for a chunk record
+                                           (another kernel held the device's compute units);
+                                           the outputs of that call are undefined */
 
 typedef struct {
   int64_t B, T, H;        /* >= 0 each; a zero size makes the call a no-op */
@@ -415,6 +418,20 @@ kda_status_t kda_chunk_fwd_flags(const void* workspace, size_t workspace_bytes, 
  */
 typedef void (*kda_launch_observer_t)(const char* kernel_name, void* stream, int phase, void* user);
 void kda_set_launch_observer(kda_launch_observer_t fn, void* user);
+
+/*
+ * Forward schedule.  With bf16 inputs, no segment_ids, no transition output
+ * and K = V = 128 on a gfx950 device of 8 XCDs, kda_chunk_fwd and
+ * kda_chunk_fwd_gated run the intra-chunk step and the recurrence as one
+ * persistent kernel ("kda_fused", the fused forward of the page "Add packed
+ * KDA forward megakernel", Summary) whose per-chunk records pass through L2;
+ * every other call, and every call after kda_set_fused_forward(0), runs
+ * them as two kernels ("kda_intra", then "kda_recur") with the records in
+ * HBM.  Both compute the same function of the inputs; the setting only
+ * selects the schedule (tests use it to compare the two).  Default 1.
+ * Process-wide; set it while no other thread is inside a forward call.
+ */
+void kda_set_fused_forward(int enable);
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* kda_last_error(void);

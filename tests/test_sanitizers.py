@@ -21,8 +21,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HERE = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "gated_delta_rule_33_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-LIB_SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_intra.hip", "kda_recur.hip", "kda_layer.hip", "kda_cp.hip",
-               "kda_bwd.hip"]
+LIB_SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_intra.hip", "kda_fused.hip", "kda_recur.hip", "kda_layer.hip",
+               "kda_cp.hip", "kda_bwd.hip"]
 # Host-side sanitizer flags, each behind -Xarch_host so no device code is built with them.
 HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
             "-Xarch_host", "-fno-sanitize-recover=all"]
