@@ -398,8 +398,10 @@ def gpu_outputs(res):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # The warmup also brings the GPU's clocks up to their loaded level: a few
+    # steps are not enough (the first ones run measurably slower).
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="bf16_b1_h32_t8192_fixed_state", choices=sorted(WORKLOADS))
     ap.add_argument("--extra", default="bf16_b1_h32_t8192_packed25_l2,bf16_b1_h8_t1024_fixed,bf16_b1_h8_t1024_packed4",
                     help="comma-separated workloads also timed and reported under 'extra' ('' for none)")

@@ -26,7 +26,7 @@ namespace {
 thread_local std::string g_last_error;
 kda_launch_observer_t g_observer = nullptr;
 void* g_observer_user = nullptr;
-bool g_fused_forward = true;
+bool g_fused_forward = false;
 
 // Enqueue one kernel, with the observer (if any) called around it.
 template <class F>

@@ -89,21 +89,27 @@ __device__ __forceinline__ bool is_ready(const uint32_t* word) {
 
 // The queue of one XCD: its sequence-heads xcd, xcd + n_xcd, ... (hx of
 // them), chunk-major.  Ticket q is chunk q / hx of the (q % hx)-th of them.
+// Record indices stay below 2^30 here, so the arithmetic is 32-bit.
 struct XcdQueue {
   int xcd;
   int64_t hx;
   __device__ int64_t item(const FusedParams& p, int64_t q) const {   // -1 past the end
-    const int64_t n = hx > 0 ? q / hx : p.nc;
-    if (n >= p.nc) return -1;
-    const int64_t sh = xcd + p.n_xcd * (q % hx);
-    return ((sh / p.ip.H) * p.nc + n) * p.ip.H + sh % p.ip.H;
+    const uint32_t qq = (uint32_t)q, hh = (uint32_t)hx, H = (uint32_t)p.ip.H, nc = (uint32_t)p.nc;
+    if (hh == 0 || q >= (int64_t)hh * nc) return -1;
+    const uint32_t n = qq / hh;
+    const uint32_t sh = (uint32_t)xcd + (uint32_t)p.n_xcd * (qq - n * hh);
+    const uint32_t b = sh / H;
+    return (int64_t)((b * nc + n) * H + (sh - b * H));
   }
 };
 
-// Produces one record with the calling workgroup's four waves and publishes it.
-template <int K, int V>
-__device__ __forceinline__ void produce(const FusedParams& p, int64_t item, char* lds) {
-  intra4_item<K, V>(p.ip, item, lds);
+// Produces one record with the calling workgroup's four waves from the rows
+// `in` and publishes it, loading the rows of the item next_item() names into
+// `next` meanwhile (see intra4_item).
+template <int K, int V, class NextItem>
+__device__ __forceinline__ void produce(const FusedParams& p, int64_t item, char* lds, const ItemRows<K>& in,
+                                        const NextItem& next_item, ItemRows<K>& next) {
+  intra4_item<K, V>(p.ip, item, lds, in, next_item, next);
   __builtin_amdgcn_s_waitcnt(0);   // this wave's record stores are acknowledged
   block_sync();
   if (threadIdx.x == 0) __hip_atomic_store(p.ready + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -303,77 +309,88 @@ __device__ __forceinline__ int64_t recur_lane(const FusedParams& p, int64_t sh, 
   return n_chunks;
 }
 
+// A workgroup of role 0 holds a recurrence lane (ticket t) and runs it from
+// chunk n whenever records n and n + 1 are ready; when they are not, it
+// produces an item of the queue instead, and waits for them only once the
+// queue is empty.  Returns when no lane is left.
 template <class TO, int K, int V>
-__global__ __launch_bounds__(256, 2) void kda_fused_kernel(FusedParams p) {
-  extern __shared__ __align__(16) char smem_raw[];
-  __shared__ int s_task;
+__device__ __forceinline__ void run_lanes(const FusedParams& p, const XcdQueue& qu, char* smem_raw, int* s_task) {
   constexpr int NV = V / kVT;
   FusedCtl* ctl = p.ctl;
-  XcdQueue qu;
-  qu.xcd = (int)(read_xcc_id() % (unsigned)p.n_xcd);
-  // Sequence-heads of this XCD: xcd, xcd + n_xcd, ...
-  qu.hx = p.n_sh > qu.xcd ? (p.n_sh - qu.xcd + p.n_xcd - 1) / p.n_xcd : 0;
   const int xcd = qu.xcd;
-  const int64_t hx = qu.hx;
-  if (threadIdx.x == 0) s_task = (int)atomicAdd(&ctl->cu_arrivals[xcd][read_cu_slot()], 1u);
-  block_sync();
-  const int role = __builtin_amdgcn_readfirstlane(s_task);   // uniform: read through LDS
-  block_sync();
-
-  // One loop for both roles, so that the item code and the lane code each
-  // appear once.  A workgroup of role 0 holds a recurrence lane (ticket t)
-  // and runs it from chunk n whenever records n and n + 1 are ready; when
-  // they are not, it produces an item of the queue instead, and waits for
-  // them only once the queue is empty.  The other workgroups only produce.
-  bool lanes = role == 0;
   int64_t t = -1, n = 0;
   for (;;) {
-    if (lanes && t < 0) {
-      if (threadIdx.x == 0) s_task = (int)atomicAdd(&ctl->lane_ticket[xcd], 1u);
+    if (t < 0) {
+      if (threadIdx.x == 0) *s_task = (int)atomicAdd(&ctl->lane_ticket[xcd], 1u);
       block_sync();
-      t = __builtin_amdgcn_readfirstlane(s_task);
+      t = __builtin_amdgcn_readfirstlane(*s_task);
       block_sync();
       n = 0;
-      if (t >= hx * NV) {
-        lanes = false;
-        t = -1;
-      }
+      if (t >= qu.hx * NV) return;
     }
-    int64_t need = -1;   // record index the lane waits for
-    if (lanes) {
-      const int64_t sh = xcd + p.n_xcd * (t / NV);
-      const int64_t base = ((sh / p.ip.H) * p.nc + n) * p.ip.H + sh % p.ip.H;
-      if (threadIdx.x == 0) {
-        int v = -1;
-        if (!is_ready(p.ready + base)) v = 0;
-        else if (n + 1 < p.nc && !is_ready(p.ready + base + p.ip.H)) v = 1;
-        s_task = v;
-      }
-      block_sync();
-      const int v = __builtin_amdgcn_readfirstlane(s_task);
-      block_sync();
-      if (v < 0) {
-        n = recur_lane<TO, K, V>(p, sh, (int)(t % NV), smem_raw, &s_task, n);
-        block_sync();
-        if (n >= p.nc) t = -1;
-        continue;
-      }
-      need = base + v * p.ip.H;
+    const int64_t sh = xcd + p.n_xcd * (t / NV);
+    const int64_t base = ((sh / p.ip.H) * p.nc + n) * p.ip.H + sh % p.ip.H;
+    if (threadIdx.x == 0) {
+      int v = -1;
+      if (!is_ready(p.ready + base)) v = 0;
+      else if (n + 1 < p.nc && !is_ready(p.ready + base + p.ip.H)) v = 1;
+      *s_task = v;
     }
-    if (threadIdx.x == 0) s_task = (int)qu.item(p, (int64_t)atomicAdd(&ctl->item_ticket[xcd], 1u));
     block_sync();
-    const int64_t item = __builtin_amdgcn_readfirstlane(s_task);
+    const int v = __builtin_amdgcn_readfirstlane(*s_task);
+    block_sync();
+    if (v < 0) {
+      n = recur_lane<TO, K, V>(p, sh, (int)(t % NV), smem_raw, s_task, n);
+      block_sync();
+      if (n >= p.nc) t = -1;
+      continue;
+    }
+    const int64_t need = base + v * p.ip.H;   // the record the lane waits for
+    if (threadIdx.x == 0) *s_task = (int)qu.item(p, (int64_t)atomicAdd(&ctl->item_ticket[xcd], 1u));
+    block_sync();
+    const int64_t item = __builtin_amdgcn_readfirstlane(*s_task);
     block_sync();
     if (item >= 0) {
-      produce<K, V>(p, item, smem_raw);
+      ItemRows<K> in = load_item_rows<K>(p.ip, item), unused;
+      produce<K, V>(p, item, smem_raw, in, NoNextItem{}, unused);
       block_sync();
       continue;
     }
-    if (!lanes) break;
     // Every item is claimed by a running workgroup, whose production
     // completes without waiting.
     wait_ready(p.ready + need, p.ip.hdr);
   }
+}
+
+// Production only, until the queue is empty.
+template <int K, int V>
+__device__ __forceinline__ void produce_all(const FusedParams& p, const XcdQueue& qu, char* smem_raw, int* s_task) {
+  for (;;) {
+    if (threadIdx.x == 0) *s_task = (int)qu.item(p, (int64_t)atomicAdd(&p.ctl->item_ticket[qu.xcd], 1u));
+    block_sync();
+    const int64_t item = __builtin_amdgcn_readfirstlane(*s_task);
+    block_sync();
+    if (item < 0) return;
+    ItemRows<K> in = load_item_rows<K>(p.ip, item), unused;
+    produce<K, V>(p, item, smem_raw, in, NoNextItem{}, unused);
+    block_sync();
+  }
+}
+
+template <class TO, int K, int V>
+__global__ __launch_bounds__(256, 2) void kda_fused_kernel(FusedParams p) {
+  extern __shared__ __align__(16) char smem_raw[];
+  __shared__ int s_task;
+  XcdQueue qu;
+  qu.xcd = (int)(read_xcc_id() % (unsigned)p.n_xcd);
+  // Sequence-heads of this XCD: xcd, xcd + n_xcd, ...
+  qu.hx = p.n_sh > qu.xcd ? (p.n_sh - qu.xcd + p.n_xcd - 1) / p.n_xcd : 0;
+  if (threadIdx.x == 0) s_task = (int)atomicAdd(&p.ctl->cu_arrivals[qu.xcd][read_cu_slot()], 1u);
+  block_sync();
+  const int role = __builtin_amdgcn_readfirstlane(s_task);   // uniform: read through LDS
+  block_sync();
+  if (role == 0) run_lanes<TO, K, V>(p, qu, smem_raw, &s_task);
+  produce_all<K, V>(p, qu, smem_raw, &s_task);
 }
 
 // Zeroes the control block and the ready words (n words from ctl on) and the

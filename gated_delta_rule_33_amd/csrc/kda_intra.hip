@@ -827,16 +827,29 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 }
 
 
-// bf16 inputs: one item per workgroup of four waves, items from the last
-// back (the last workgroups to run write the records of the first chunks,
-// which the recurrence reads first); about 66 KB of LDS, two per CU.
+// bf16 inputs: workgroups of four waves, two per CU (about 66 KB of LDS
+// each), each running items n_items - 1 - blockIdx.x, then gridDim.x fewer,
+// and so on (the last items to run are the first chunks, which the
+// recurrence reads first).  A workgroup loads the next item's rows while it
+// finishes the current one.
 template <int K, int V>
 __global__ __launch_bounds__(256, 2) void kda_intra4_kernel(IntraParams p) {
   extern __shared__ __align__(16) char smem_raw[];
+  __shared__ int64_t s_next;
   const int64_t n_items = p.packed ? (int64_t)p.hdr->n_chunks * p.H : p.B * p.nc_fixed * p.H;
   if (!p.packed && blockIdx.x == 0 && threadIdx.x == 0) p.hdr->flags = 0;   // no tables without segments
-  if ((int64_t)blockIdx.x >= n_items) return;
-  intra4_item<K, V>(p, n_items - 1 - (int64_t)blockIdx.x, smem_raw);
+  int64_t item = n_items - 1 - (int64_t)blockIdx.x;
+  if (item < 0) return;
+  ItemRows<K> in = load_item_rows<K>(p, item), nx;
+  for (;;) {
+    const int64_t next = item - (int64_t)gridDim.x;
+    if (threadIdx.x == 0) s_next = next >= 0 ? next : -1;
+    intra4_item<K, V>(p, item, smem_raw, in, [&] { return uniform_i64(&s_next); }, nx);
+    if (next < 0) break;
+    block_sync();
+    in = nx;
+    item = next;
+  }
 }
 
 template <int K, int V>
@@ -851,7 +864,8 @@ hipError_t launch_intra4_t(const CallArgs& a) {
   if (e != hipSuccess) return e;
   const int64_t items = (a.n_max > 0 ? a.cmax : a.B * a.nc_fixed) * a.H;
   if (items <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)items), dim3(256), smem, a.stream, p);
+  const unsigned grid = (unsigned)std::min<int64_t>(items, 2 * (int64_t)cu_count());
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, a.stream, p);
   return hipGetLastError();
 }
 

@@ -187,11 +187,83 @@ __device__ __forceinline__ void frag_ld_bf16(const uint16_t* row, int o, int g, 
   x[6] = __uint_as_float(b.y << 16); x[7] = __uint_as_float(b.y & 0xffff0000u);
 }
 
+// The raw inputs of one lane of an item: its row of q, k and g (bf16 pairs in
+// fragment order: channels 32 kb + 4 gq .. +3 in [kb][0], 32 kb + 16 + 4 gq
+// .. +3 in [kb][1]) and its beta, with `keep` all ones, or for rows past
+// the chunk's end the first row's values with `keep` zero (applied when the
+// rows are widened, so that nothing waits for the loads before then).  Kept
+// packed (50 registers), so that the next item's can be in flight while the
+// current item finishes.
+template <int K>
+struct ItemRows {
+  uint2 q[K / 32][2], k[K / 32][2], g[K / 32][2];
+  uint32_t beta, keep;
+};
+
+template <int K>
+__device__ __forceinline__ ItemRows<K> load_item_rows(const IntraParams& p, int64_t item) {
+  constexpr int KB = K / 32;
+  const ItemInfo it = item_info(p, item_pos(p, item));
+  const int tid = opaque((int)threadIdx.x) & 255;
+  const int m = tid & 15, gq = (tid >> 4) & 3, r_own = 16 * (tid >> 6) + m;
+  ItemRows<K> x;
+  // Rows past the chunk's end read the chunk's first row (always present),
+  // so that no load is conditional.
+  const bool row_ok = r_own < it.len;
+  x.keep = row_ok ? 0xffffffffu : 0u;
+  const int64_t tok = it.tok0 + (row_ok ? r_own : 0);
+  const int64_t off = (tok * p.H + it.h) * K;
+  const uint16_t* qr = static_cast<const uint16_t*>(p.q) + off;
+  const uint16_t* kr = static_cast<const uint16_t*>(p.k) + off;
+  const uint16_t* gr = static_cast<const uint16_t*>(p.g) + off;
+  auto ld = [&](const uint16_t* r, int o) { return *reinterpret_cast<const uint2*>(r + o); };
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int o = 32 * kb + 16 * hf + 4 * gq;
+      x.q[kb][hf] = ld(qr, o);
+      x.k[kb][hf] = ld(kr, o);
+      x.g[kb][hf] = ld(gr, o);
+    }
+  }
+  x.beta = (uint32_t) static_cast<const uint16_t*>(p.beta)[tok * p.H + it.h];
+  return x;
+}
+
+// An int64 that every lane of the wave holds alike (read from LDS), as a scalar.
+__device__ __forceinline__ int64_t uniform_i64(const int64_t* lds) {
+  const int64_t v = *lds;
+  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)(uint64_t)v);
+  const int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo);
+}
+
+__device__ __forceinline__ void widen8(const uint2 a[2], uint32_t keep, float x[8]) {
+  const uint32_t w[4] = {a[0].x & keep, a[0].y & keep, a[1].x & keep, a[1].y & keep};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// No next item (see intra4_item).
+struct NoNextItem {
+  __device__ int64_t operator()() const { return -1; }
+};
+
 // One (chunk, head) item by the four waves of the calling workgroup, in the
-// LDS at smem_raw (sizeof(Intra4Smem<K, V>) bytes).  The caller separates
-// consecutive items with a barrier.
-template <int K, int V>
-__device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, char* smem_raw) {
+// LDS at smem_raw (sizeof(Intra4Smem<K, V>) bytes), from the rows `in` that
+// this lane loaded with load_item_rows.  Once this item's own rows are no
+// longer needed, next_item() (called by every lane, after the item's first
+// barriers, with a result alike in all lanes) names the next item this
+// workgroup will run, and that item's rows are loaded into `next` (nothing
+// for -1), so that their latency overlaps the rest of this item.  The
+// caller separates consecutive items with a barrier.
+template <int K, int V, class NextItem>
+__device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, char* smem_raw,
+                                            const ItemRows<K>& in, const NextItem& next_item, ItemRows<K>& next) {
   using S = Intra4Smem<K, V>;
   using P = Prec<uint16_t>;
   using PA = typename P::A;
@@ -204,7 +276,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   using PAq = typename P::Aq;
   using L = RecordLayout<uint16_t, K, V>;
   constexpr int KB = K / 32;
-  constexpr int CBW = K / 64;   // key-channel blocks of W and Kt per wave
+  constexpr int CBW = K / 64;   // key-channel blocks of W per wave
   constexpr int VBW = V / 64;   // value blocks of U per wave
   S& sm = *reinterpret_cast<S*>(smem_raw);
 
@@ -219,27 +291,15 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   char* rec = p.records + item * p.record_bytes;
   const bool row_ok = r_own < len;
 
-  // ---- this lane's row of q, k and g (fragment order), beta, and its share of the value rows
+  // ---- this lane's row of q, k and g (fragment order) and beta
   float qx[KB][8], kx[KB][8], gx[KB][8];
-  {
-    const int64_t off = ((it.tok0 + r_own) * H + h) * K;
-    const uint16_t* qr = static_cast<const uint16_t*>(p.q) + off;
-    const uint16_t* kr = static_cast<const uint16_t*>(p.k) + off;
-    const uint16_t* gr = static_cast<const uint16_t*>(p.g) + off;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      if (row_ok) {
-        frag_ld_bf16(qr, 32 * kb, gq, qx[kb]);
-        frag_ld_bf16(kr, 32 * kb, gq, kx[kb]);
-        frag_ld_bf16(gr, 32 * kb, gq, gx[kb]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qx[kb][j] = kx[kb][j] = gx[kb][j] = 0.f;
-      }
-    }
+  for (int kb = 0; kb < KB; ++kb) {
+    widen8(in.q[kb], in.keep, qx[kb]);
+    widen8(in.k[kb], in.keep, kx[kb]);
+    widen8(in.g[kb], in.keep, gx[kb]);
   }
-  const float beta_own =
-      row_ok ? bits_to_f32(static_cast<const uint16_t*>(p.beta)[(it.tok0 + r_own) * H + h]) : 0.f;
+  const float beta_own = bits_to_f32((uint16_t)(in.beta & in.keep));
   if (p.gate_mode && row_ok) {
     // In-kernel gate: z = exp(A_log_h) (g + dt_bias_hc), log decay lower_bound
     // * sigmoid(z) under the safe gate, else log sigmoid(z).
@@ -342,7 +402,10 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     // and running sums come from lane m - dd of the same 16-lane row, each
     // lane group sums its quarter of the channels.  Norm factors are applied
     // with the other tiles below.
-    float sk_d[16], sq_d[16];
+    // Lane (m, gq) keeps D[i][r = f + m] for i = f + 4 gq + ii, i.e. the
+    // step dd = m - 4 gq - ii (each step's sums are alike in the four lane
+    // groups of a column).
+    f32x4 dKK = {0, 0, 0, 0}, dQK = {0, 0, 0, 0};
 #define KDA_DIAG_STEP(DD)                                                              \
     {                                                                                  \
       float pk = 0.f, pq = 0.f;                                                        \
@@ -356,28 +419,23 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
       }                                                                                \
       pk += __shfl_xor(pk, 16); pk += __shfl_xor(pk, 32);                              \
       pq += __shfl_xor(pq, 16); pq += __shfl_xor(pq, 32);                              \
-      sk_d[DD] = pk; sq_d[DD] = pq;                                                    \
+      _Pragma("unroll") for (int ii = 0; ii < 4; ++ii) {                               \
+        const bool mine = m - (DD) == 4 * gq + ii;                                     \
+        dKK[ii] = mine ? pk : dKK[ii];                                                 \
+        dQK[ii] = mine ? pq : dQK[ii];                                                 \
+      }                                                                                \
     }
     KDA_DIAG_STEP(0) KDA_DIAG_STEP(1) KDA_DIAG_STEP(2) KDA_DIAG_STEP(3)
     KDA_DIAG_STEP(4) KDA_DIAG_STEP(5) KDA_DIAG_STEP(6) KDA_DIAG_STEP(7)
     KDA_DIAG_STEP(8) KDA_DIAG_STEP(9) KDA_DIAG_STEP(10) KDA_DIAG_STEP(11)
     KDA_DIAG_STEP(12) KDA_DIAG_STEP(13) KDA_DIAG_STEP(14) KDA_DIAG_STEP(15)
 #undef KDA_DIAG_STEP
-    // lane (m, gq) keeps D[i][r = f + m] for i = f + 4gq + ii, i.e. dd = m - 4gq - ii
 #pragma unroll
-    for (int ii = 0; ii < 4; ++ii) {
-      const int dd = m - 4 * gq - ii;
-      float vk = 0.f, vq = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        if (e == dd) { vk = sk_d[e]; vq = sq_d[e]; }
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-        if (I == R) {
-          accKK[I][ii] = dd >= 0 ? vk : 0.f;
-          accQK[I][ii] = dd >= 0 ? vq : 0.f;
-        }
-    }
+    for (int I = 0; I < 4; ++I)
+      if (I == R) {
+        accKK[I] = dKK;
+        accQK[I] = dQK;
+      }
   }
   // Row operands k exp(G_r - G_f), q exp(G_r - G_f) (every factor <= 1); the
   // output's operand scale nq q exp(G_r) goes to the record; the column table
@@ -407,6 +465,12 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     frag_wr(sm.X + r_own * S::XP, 32 * kb, gq, xx);
   }
   block_sync();   // B2: X, nk, beta, factor rows
+  // The next item's rows (this item's are dead from here on), issued before
+  // this item's larger stores.
+  {
+    const int64_t nx = next_item();
+    if (nx >= 0) next = load_item_rows<K>(p, nx);
+  }
 
   // ---- A and Aqk for row block R: tiles (I, R) hold D[i][r], I <= R
 #pragma unroll
@@ -465,10 +529,17 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     }
   }
   // Kt = (k exp(G_C - G))^T tiles [c-block][token slab] from columns of X:
-  // k_r exp(G_C - G_r) = X_r exp(G_C - G_l(I(r))).
+  // k_r exp(G_C - G_r) = X_r exp(G_C - G_l(I(r))).  The waves with fewer A
+  // tiles above take more channel blocks: 4, 3, 1, 0 of 8 (K = 128) or
+  // 2, 1, 1, 0 of 4 (K = 64).
+  constexpr int NCBK = K / 16;
+  auto kt_bound = [](int w) { return NCBK == 8 ? (w == 0 ? 0 : w == 1 ? 4 : w == 2 ? 7 : 8)
+                                               : (w == 0 ? 0 : w == 1 ? 2 : w == 2 ? 3 : 4); };
+  const int kt_begin = kt_bound(R), kt_end = kt_bound(R + 1);
 #pragma unroll
-  for (int u = 0; u < CBW; ++u) {
-    const int cb = CBW * R + u, c = 16 * cb + m;
+  for (int u = 0; u < NCBK / 2; ++u) {
+    const int cb = kt_begin + u, c = 16 * cb + m;
+    if (cb >= kt_end) break;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       float xv[8], kt[8];

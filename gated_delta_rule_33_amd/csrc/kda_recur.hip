@@ -678,6 +678,219 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   }
 }
 
+// The same loop with its two halves on separate waves.  Per chunk, only
+// Delta and the state update are on the chain from one chunk to the next;
+// the read-out O = scale Qg S + scale Aqk Delta is not.  Four chain waves
+// (Delta for tokens 16w.., the update of key-channel blocks w NCB..) and
+// four read-out waves (O for tokens 16w..) share the workgroup, a chain
+// wave and a read-out wave on each SIMD, so that the read-out's matrix work
+// and latencies fill the chain's waits instead of lengthening each chunk.
+// The state is double-buffered in LDS: the read-out of chunk n reads S_n
+// between the barriers B1(n) and B2(n) while the chain writes S_{n+1} into
+// the other buffer; Delta_n is read by both between the same barriers.
+// Operand loads, precisions and sums are those of the kernel above.  While
+// the chain computes Delta_n, the read-out waves pull this workgroup's share
+// of record n + 2 into L2 (the chain loads record n + 1's operands then).
+template <class TI, class TO, int K, int V>
+__global__ __launch_bounds__(2 * kComputeWaves * kWave) void kda_recur_split_kernel(RecurParams p) {
+  using P = Prec<TI>;
+  using PS = typename P::S;
+  using PD = typename P::D;
+  using PW = typename P::W;
+  using PK = typename P::Kt;
+  using PQ = typename P::Qg;
+  using PA = typename P::Aq;
+  using L = RecordLayout<TI, K, V>;
+  constexpr int NV = V / kVT;
+  constexpr int NCB = K / 64;
+  constexpr int KB = K / 32;
+  constexpr int TS = tile_bytes<PS>(), TD = tile_bytes<PD>();
+  __shared__ __align__(16) char s_state[2][KB * TS];
+  __shared__ __align__(16) char s_delta[2 * TD];
+  __shared__ __align__(16) float s_out[kComputeWaves][kChunk / kComputeWaves * kOutLd];
+  __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = wave & (kComputeWaves - 1);
+  const bool readout = wave >= kComputeWaves;
+  const int m = lane & 15, gq = lane >> 4;
+  const int64_t H = p.H;
+
+  // XCD-aware decode, as above.
+  const int64_t id = blockIdx.x;
+  const int64_t seq_head = (id / (8 * NV)) * 8 + id % 8;
+  const int j = (int)((id / 8) % NV);
+  const int64_t n_seq_heads = p.packed ? (int64_t)p.hdr->n_segments * H : p.n_seq_heads_fixed;
+  if (seq_head >= n_seq_heads) return;
+  const int64_t h = seq_head % H, sq = seq_head / H;
+
+  int64_t b, slot, n_chunks, first_chunk, t_begin, seq_len;
+  if (p.packed) {
+    const SegEntry se = p.segs[sq];
+    b = se.b;
+    slot = ((int64_t)se.b * p.n_max + se.local) * H + h;
+    n_chunks = se.n_chunks;
+    first_chunk = se.chunk_begin;
+    t_begin = se.t0;
+    seq_len = se.len;
+  } else {
+    b = sq;
+    slot = b * H + h;
+    n_chunks = p.nc_fixed;
+    first_chunk = b * p.nc_fixed;
+    t_begin = 0;
+    seq_len = p.T;
+  }
+  auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
+  const int v0 = kVT * j;
+
+  if (!readout) {
+    // ---- chain wave w
+    PW wn[KB];
+    f32x4 u;
+    PK kt[NCB][2];
+    f32x4 gc[NCB];
+    auto load_w = [&](const char* r) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
+      u = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + j) * 1024)[lane];
+    };
+    auto load_kt = [&](const char* r) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          kt[c][kb].load(r + L::kKt + (int64_t)((w * NCB + c) * 2 + kb) * tile_bytes<PK>(), lane);
+        gc[c] = reinterpret_cast<const f32x4*>(r + L::kGc)[4 * (w * NCB + c) + gq];
+      }
+    };
+    f32x4 st[NCB];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int c0 = 16 * (w * NCB + c) + 4 * gq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st[c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
+      float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
+      const int cb = w * NCB + c;
+      PS::store_half(s_state[0] + (cb / 2) * TS, lane, cb & 1, x);
+    }
+    if (n_chunks > 0) {
+      load_w(record(0));
+      load_kt(record(0));
+    }
+    block_sync();   // B0
+    for (int64_t n = 0; n < n_chunks; ++n) {
+      const char* rn1 = record(n + 1 < n_chunks ? n + 1 : n);
+      const char* cur = s_state[n & 1];
+      // Delta = U - W S for tokens 16w..16w+15
+      {
+        PS sf[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) sf[kb].load(cur + kb * TS, lane);
+        f32x4 d0 = u, d1 = {0, 0, 0, 0};
+#pragma unroll
+        for (int kb = 0; kb < KB; kb += 2) {
+          mma(d0, wn[kb], sf[kb]);
+          if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
+        }
+        float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
+        PD::store_half(s_delta + (w / 2) * TD, lane, w & 1, x);
+      }
+      load_w(rn1);
+      block_sync();   // B1
+      // S <- diag(exp(G_C)) S + Kt^T Delta, into the other buffer
+      PD dd[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta + kb * TD, lane);
+      char* nxt = s_state[(n + 1) & 1];
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        f32x4 a0, a1 = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a0[i] = st[c][i] * gc[c][i];
+        mma(a0, kt[c][0], dd[0]);
+        mma(a1, kt[c][1], dd[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[c][i] = a0[i] + a1[i];
+        float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
+        const int cb = w * NCB + c;
+        PS::store_half(nxt + (cb / 2) * TS, lane, cb & 1, x);
+      }
+      load_kt(rn1);
+      block_sync();   // B2
+    }
+    if (p.fin) {
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int c0 = 16 * (w * NCB + c) + 4 * gq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p.fin[(slot * K + c0 + i) * V + v0 + m] = st[c][i];
+      }
+    }
+    return;
+  }
+
+  // ---- read-out wave w: O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
+  TO* out = static_cast<TO*>(p.o);
+  PQ qg[KB];
+  PA aq[2];
+  auto load_q = [&](const char* r) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PA>(), lane);
+  };
+  // Every 64-byte segment of the workgroup's 1/NV share of a record, once,
+  // split over the four read-out waves.
+  auto prefetch = [&](int64_t n) {
+    constexpr int SEGS = (int)(L::kBytes / 64);
+    constexpr int SHARE = (SEGS + NV - 1) / NV;
+    constexpr int PER = (SHARE + kComputeWaves - 1) / kComputeWaves;
+    const char* r = record(n);
+#pragma unroll
+    for (int i = 0; i < (PER + kWave - 1) / kWave; ++i) {
+      const int e = i * kWave + lane, seg = j * SHARE + w * PER + e;
+      if (e < PER && w * PER + e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
+    }
+  };
+  if (n_chunks > 0) load_q(record(0));
+  if (n_chunks > 1) prefetch(1);
+  block_sync();   // B0
+  for (int64_t n = 0; n < n_chunks; ++n) {
+    const int64_t t0 = t_begin + n * kChunk;
+    const int len = (int)min<int64_t>(kChunk, seq_len - n * kChunk);
+    const char* rn1 = record(n + 1 < n_chunks ? n + 1 : n);
+    if (n + 2 < n_chunks) prefetch(n + 2);
+    block_sync();   // B1: Delta_n and S_n in LDS
+    const char* cur = s_state[n & 1];
+    PS sf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sf[kb].load(cur + kb * TS, lane);
+    PD dd[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta + kb * TD, lane);
+    f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+#pragma unroll
+    for (int kb = 0; kb < KB; kb += 2) {
+      mma(o0, qg[kb], sf[kb]);
+      if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
+    }
+    mma(o1, aq[0], dd[0]);
+    if (w >= 2) mma(o0, aq[1], dd[1]);
+    load_q(rn1);
+    float* tl = s_out[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tl[(4 * gq + i) * kOutLd + m] = o0[i] + o1[i];
+    const int r = lane >> 2, q4 = 4 * (lane & 3);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * kOutLd + q4);
+    if (16 * w + r < len) store_out4(out, ((b * p.T + t0 + 16 * w + r) * H + h) * V + v0 + q4, x);
+    block_sync();   // B2
+  }
+  vm_wait<0>();   // the prefetches' LDS writes land before the workgroup ends
+}
+
 template <class TI, class TO, int K, int V, int TPW>
 hipError_t launch_recur_w(const RecurParams& p, int64_t seq_heads, hipStream_t stream) {
   constexpr int NVW = V / kVT / TPW;
@@ -704,10 +917,15 @@ hipError_t launch_recur_t(const CallArgs& a) {
                        dim3((kComputeWaves + 1) * kWave), 0, a.stream, p);
     return hipGetLastError();
   }
-  // Two tiles per workgroup once one tile per workgroup would need several
-  // rounds of workgroups over the CUs.
-  if (seq_heads * (V / kVT) > 2 * (int64_t)cu_count()) return launch_recur_w<TI, TO, K, V, 2>(p, seq_heads, a.stream);
+  // One split workgroup per CU while they fit in one round; then the
+  // register-direct kernel (two per CU); then two tiles per workgroup.
   const int64_t grid = (seq_heads + 7) / 8 * 8 * (V / kVT);
+  if (grid <= (int64_t)cu_count()) {
+    hipLaunchKernelGGL((kda_recur_split_kernel<TI, TO, K, V>), dim3((unsigned)grid), dim3(2 * kComputeWaves * kWave),
+                       0, a.stream, p);
+    return hipGetLastError();
+  }
+  if (seq_heads * (V / kVT) > 2 * (int64_t)cu_count()) return launch_recur_w<TI, TO, K, V, 2>(p, seq_heads, a.stream);
   hipLaunchKernelGGL((kda_recur_reg_kernel<TI, TO, K, V, false>), dim3((unsigned)grid), dim3((kComputeWaves + 1) * kWave), 0,
                      a.stream, p);
   return hipGetLastError();

@@ -303,8 +303,8 @@ def gated_rmsnorm(o, gate, weight, eps: float = 1e-6, out_dtype=None, out=None):
 
 def set_fused_forward(enable: bool) -> None:
     """Select the forward schedule for later calls (process-wide): the fused
-    persistent kernel where it applies (default), or always the two-kernel
-    path (intra-chunk kernel, then recurrence kernel)."""
+    persistent kernel where it applies, or always the two-kernel path
+    (intra-chunk kernel, then recurrence kernel; the default)."""
     load_library().kda_set_fused_forward(1 if enable else 0)
 
 

@@ -420,16 +420,18 @@ typedef void (*kda_launch_observer_t)(const char* kernel_name, void* stream, int
 void kda_set_launch_observer(kda_launch_observer_t fn, void* user);
 
 /*
- * Forward schedule.  With bf16 inputs, no segment_ids, no transition output
- * and K = V = 128 on a gfx950 device of 8 XCDs, kda_chunk_fwd and
- * kda_chunk_fwd_gated run the intra-chunk step and the recurrence as one
- * persistent kernel ("kda_fused", the fused forward of the page "Add packed
- * KDA forward megakernel", Summary) whose per-chunk records pass through L2;
- * every other call, and every call after kda_set_fused_forward(0), runs
- * them as two kernels ("kda_intra", then "kda_recur") with the records in
- * HBM.  Both compute the same function of the inputs; the setting only
- * selects the schedule (tests use it to compare the two).  Default 1.
- * Process-wide; set it while no other thread is inside a forward call.
+ * Forward schedule.  By default the forward runs the intra-chunk step and
+ * the recurrence as two kernels ("kda_intra", then "kda_recur") with the
+ * per-chunk records in HBM.  After kda_set_fused_forward(1), calls with
+ * bf16 inputs, no segment_ids, no transition output and K = V = 128 on a
+ * gfx950 device of 8 XCDs run both as one persistent kernel ("kda_fused",
+ * the fused forward of the page "Add packed KDA forward megakernel",
+ * Summary) whose records pass through L2; other calls keep the two kernels.
+ * Both compute the same function of the inputs (up to fp32 rounding: the
+ * kernels are compiled apart); the setting only selects the schedule.
+ * Default 0: on MI355X the two kernels are the faster schedule at the sizes
+ * measured so far.  Process-wide; set it while no other thread is inside a
+ * forward call.
  */
 void kda_set_fused_forward(int enable);
 
