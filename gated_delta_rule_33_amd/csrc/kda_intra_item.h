@@ -21,7 +21,10 @@
 namespace kda {
 namespace detail {
 
-constexpr float kSpanMax = 64.f;
+constexpr float kSpanMax = 64.f;   // natural-log span limit of the split diagonal block
+constexpr float kLog2e = 1.4426950408889634f;
+// 2^x on the hardware exponential (G differences below are in log2 units).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // A copy of x the compiler cannot see through.  Per-lane addresses derived
 // from it inside an item loop are recomputed per item instead of being
@@ -156,7 +159,7 @@ struct Intra4Smem {
   };
   union {
     float X[64 * XP];            // k exp(G_l(I) - G), rows of the chunk (A, Aqk and Kt)
-    float KG[64 * XP];           // then beta nk k exp(G) (W)
+    float KG[64 * XP];           // then nk k exp(G) (W)
     uint16_t v[64 * VP];         // then the value rows (U)
   };
 };
@@ -315,12 +318,14 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   }
 
   // ---- running sum of g over the rows: inclusive scan over the block's 16
-  //      rows (lanes m of one 16-lane row), then the sums of earlier blocks
+  //      rows (lanes m of one 16-lane row), then the sums of earlier blocks.
+  //      G is carried in log2 units (G log2 e) from here on, so each
+  //      exponential below is one hardware exp2.
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      float x = gx[kb][j];
+      float x = gx[kb][j] * kLog2e;
       x += dpp_shr<1>(x);
       x += dpp_shr<2>(x);
       x += dpp_shr<4>(x);
@@ -357,10 +362,10 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     const float gf = sm.Gf[R][c], gl = sm.Gl[R][c], gc = sm.Gl[3][c];
 #pragma unroll
     for (int I = 0; I < 4; ++I)
-      if (I <= R) sm.d[R * (R + 1) / 2 + I][c] = __expf(gf - sm.Gl[I][c]);
-    sm.gff[R][c] = __expf(gf);
-    sm.ktf[R][c] = __expf(gc - gl);
-    if (R == 3) reinterpret_cast<float*>(rec + L::kGc)[c] = __expf(gc);
+      if (I <= R) sm.d[R * (R + 1) / 2 + I][c] = exp2_hw(gf - sm.Gl[I][c]);
+    sm.gff[R][c] = exp2_hw(gf);
+    sm.ktf[R][c] = exp2_hw(gc - gl);
+    if (R == 3) reinterpret_cast<float*>(rec + L::kGc)[c] = exp2_hw(gc);
   }
   // Norms of this lane's row (all four lane groups hold a quarter of its channels).
   float nqr = 1.f, nkr = 1.f;
@@ -392,7 +397,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   }
   span = fmaxf(span, __shfl_xor(span, 16));
   span = fmaxf(span, __shfl_xor(span, 32));
-  const bool diag_split = __builtin_amdgcn_readfirstlane(span <= kSpanMax ? 1 : 0) != 0;
+  const bool diag_split = __builtin_amdgcn_readfirstlane(span <= kSpanMax * kLog2e ? 1 : 0) != 0;
   f32x4 accKK[4], accQK[4];
 #pragma unroll
   for (int I = 0; I < 4; ++I) { accKK[I] = f32x4{0, 0, 0, 0}; accQK[I] = f32x4{0, 0, 0, 0}; }
@@ -413,7 +418,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
       _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                  \
         const float ki = DD == 0 ? kx[kb][j] : dpp_shr<DD>(kx[kb][j]);                 \
         const float gi = DD == 0 ? gx[kb][j] : dpp_shr<DD>(gx[kb][j]);                 \
-        const float t = ki * __expf(gx[kb][j] - gi);                                   \
+        const float t = ki * exp2_hw(gx[kb][j] - gi);                                  \
         pk += kx[kb][j] * t;                                                           \
         pq += qx[kb][j] * t;                                                           \
       }                                                                                \
@@ -451,11 +456,11 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     float xk[8], xq[8], xg[8], xx[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float er = __expf(gx[kb][j] - gfr[j]);
+      const float er = exp2_hw(gx[kb][j] - gfr[j]);
       xk[j] = kx[kb][j] * er;
       xq[j] = qx[kb][j] * er;
       xg[j] = p.scale * nqr * xq[j] * efr[j];
-      xx[j] = kx[kb][j] * __expf(glr[j] - gx[kb][j]);
+      xx[j] = kx[kb][j] * exp2_hw(glr[j] - gx[kb][j]);
     }
     fkr[kb].set(xk);
     fqr[kb].set(xq);
@@ -556,16 +561,17 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     }
   }
   block_sync();   // B3: A^T in M; X is dead
-  // W's operand rows beta nk k exp(G) take X's place (read as columns after
-  // the solve), rebuilt from the row operand pair k exp(G - G_f) (hi + lo,
-  // about 16 significant bits; the operand is rounded to a pair again).
+  // W's operand rows nk k exp(G) take X's place (read as columns after the
+  // solve), rebuilt from the row operand pair k exp(G - G_f) (hi + lo, about
+  // 16 significant bits; the operand is rounded to a pair again).  beta is
+  // applied on the T side, which W and U share.
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     float efr[8], kg[8];
     frag_rd(sm.gff[R], 32 * kb, gq, efr);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      kg[j] = beta_own * nkr * ((float)fkr[kb].hi[j] + (float)fkr[kb].lo[j]) * efr[j];
+      kg[j] = nkr * ((float)fkr[kb].hi[j] + (float)fkr[kb].lo[j]) * efr[j];
     frag_wr(sm.KG + r_own * S::XP, 32 * kb, gq, kg);
   }
 
@@ -680,24 +686,26 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   }
   block_sync();   // B6: T complete
 
-  // ---- T fragments (row block rb, token slab kb <= rb / 2): T[r][i], T[r][i] beta_i
-  auto t_frag = [&](int rb, int kb, bool with_beta) {
+  // ---- T diag(beta) fragments (row block rb, token slab kb <= rb / 2):
+  //      T[r][i] beta_i, the operand both W and U take
+  auto t_frag = [&](int rb, int kb) {
     const int r = 16 * rb + m;
     float x[8];
     const f32x4 a = ld4(sm.M + r * S::MP + 32 * kb + 4 * gq), c4 = ld4(sm.M + r * S::MP + 32 * kb + 16 + 4 * gq);
+    const f32x4 b0 = ld4(sm.beta + 32 * kb + 4 * gq), b1 = ld4(sm.beta + 32 * kb + 16 + 4 * gq);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = 32 * kb + kperm(gq, j);
-      const float tv = j < 4 ? a[j] : c4[j - 4];
-      x[j] = (i <= r) ? (with_beta ? tv * sm.beta[i] : tv) : 0.f;
+      const float tv = j < 4 ? a[j] * b0[j] : c4[j - 4] * b1[j - 4];
+      x[j] = (i <= r) ? tv : 0.f;
     }
     PT fr;
     fr.set(x);
     return fr;
   };
   PT tf[6];   // (rb, kb): (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-  tf[0] = t_frag(0, 0, false); tf[1] = t_frag(1, 0, false); tf[2] = t_frag(2, 0, false);
-  tf[3] = t_frag(2, 1, false); tf[4] = t_frag(3, 0, false); tf[5] = t_frag(3, 1, false);
+  tf[0] = t_frag(0, 0); tf[1] = t_frag(1, 0); tf[2] = t_frag(2, 0);
+  tf[3] = t_frag(2, 1); tf[4] = t_frag(3, 0); tf[5] = t_frag(3, 1);
   auto t_idx = [](int rb, int kb) { return rb < 2 ? rb : 2 * rb - 2 + kb; };
 
   // ---- the value rows (16R + l / VPR + 4t, 16-byte piece l % VPR): loaded
@@ -713,7 +721,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
                     : uint4{0, 0, 0, 0};
   }
 
-  // ---- -W = -T diag(beta) (K exp(G)): W^T tiles D[c][r] from columns of KG
+  // ---- -W = -(T diag(beta)) (K exp(G)): W^T tiles D[c][r] from columns of KG
 #pragma unroll
   for (int u = 0; u < CBW; ++u) {
     const int cb = CBW * R + u, c = 16 * cb + m;
@@ -744,11 +752,6 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     *reinterpret_cast<uint4*>(sm.v + r * S::VP + 8 * pc) = vv[t];
   }
   block_sync();   // B8
-#pragma unroll
-  for (int tt = 0; tt < 6; ++tt) {   // the T fragments again, with beta
-    const int rb = tt < 2 ? tt : (tt + 2) / 2, kb = tt < 2 ? 0 : (tt & 1);
-    tf[tt] = t_frag(rb, kb, true);
-  }
 #pragma unroll
   for (int u = 0; u < VBW; ++u) {
     const int vb = VBW * R + u;
