@@ -326,6 +326,8 @@ kda_status_t forward(const kda_fwd_desc_t* desc, const void* q, const void* k, c
   } else {
     if (!x.rerun) {
       if (has_seg) e = observed("kda_prep", s, [&] { return kda::launch_prep(a); });
+      else if (KDA_DEBUG_CHECKS)
+        e = observed("kda_clear_flags", s, [&] { return kda::launch_fill_zero(reinterpret_cast<float*>(&a.hdr->flags), 1, s); });
       if (e == hipSuccess) e = observed("kda_intra", s, [&] { return kda::launch_intra(a); });
     }
     if (e == hipSuccess) e = observed("kda_recur", s, [&] { return kda::launch_recur(a); });
@@ -403,7 +405,7 @@ void kda_set_launch_observer(kda_launch_observer_t fn, void* user) {
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
-const char* kda_version(void) { return "kda-mi355x 0.1.0"; }
+const char* kda_version(void) { return KDA_DEBUG_CHECKS ? "kda-mi355x 0.2.0 debug-checks" : "kda-mi355x 0.2.0"; }
 
 }  // extern "C"
 

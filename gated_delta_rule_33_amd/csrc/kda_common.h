@@ -304,6 +304,16 @@ struct FusedCtl {
   uint32_t item_ticket[8];
   uint32_t pad[48];
 };
+// Debug builds (-DKDA_DEBUG_CHECKS=1) check the g <= 0 precondition on the
+// device and report a violation in the table header's flags.
+#ifndef KDA_DEBUG_CHECKS
+#define KDA_DEBUG_CHECKS 0
+#endif
+// Raises `bit` in the flags word if any lane's `bad` is set.
+__device__ __forceinline__ void flag_if_any(uint32_t* flags, bool bad, uint32_t bit) {
+  if (bad) atomicOr(flags, bit);
+}
+
 struct TableHeader {
   int32_t n_segments;   // recorded segments (all rows)
   int32_t n_chunks;     // chunks of recorded segments

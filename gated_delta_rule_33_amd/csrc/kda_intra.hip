@@ -173,7 +173,9 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
   const TI* gb_ = static_cast<const TI*>(p.beta);
   const int64_t H = p.H;
   const int64_t n_items = p.packed ? (int64_t)p.hdr->n_chunks * H : p.B * p.nc_fixed * H;
-  if (!p.packed && blockIdx.x == 0 && tid == 0) p.hdr->flags = 0;   // no tables without segments
+  // No tables without segments: the flags start clear (debug builds clear
+  // them before the launch, since their checks may raise flags meanwhile).
+  if (!KDA_DEBUG_CHECKS && !p.packed && blockIdx.x == 0 && tid == 0) p.hdr->flags = 0;
   if ((int64_t)blockIdx.x >= n_items) return;
 
   // beta of the next item travels as raw input bits in one register per lane
@@ -255,6 +257,12 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
       float g0[RP], g1[RP];
 #pragma unroll
       for (int i = 0; i < RP; ++i) ld2(gvbuf + SK::idx(r0 + i, c), g0[i], g1[i]);   // all reads in flight
+      if (KDA_DEBUG_CHECKS && !p.gate_mode) {   // g is the log decay: g <= 0 is a precondition
+        bool pos = false;
+#pragma unroll
+        for (int i = 0; i < RP; ++i) pos = pos || (r0 + i < len && (g0[i] > 0.f || g1[i] > 0.f));
+        flag_if_any(&p.hdr->flags, pos, KDA_FLAG_GATE_POSITIVE);
+      }
       if (p.gate_mode) {
         // In-kernel gate: z = exp(A_log_h) (g + dt_bias_hc); the log decay is
         // lower_bound * sigmoid(z) under the safe gate, else log sigmoid(z).
@@ -837,7 +845,9 @@ __global__ __launch_bounds__(256, 2) void kda_intra4_kernel(IntraParams p) {
   extern __shared__ __align__(16) char smem_raw[];
   __shared__ int64_t s_next;
   const int64_t n_items = p.packed ? (int64_t)p.hdr->n_chunks * p.H : p.B * p.nc_fixed * p.H;
-  if (!p.packed && blockIdx.x == 0 && threadIdx.x == 0) p.hdr->flags = 0;   // no tables without segments
+  // No tables without segments: the flags start clear (debug builds clear
+  // them before the launch, since their checks may raise flags meanwhile).
+  if (!KDA_DEBUG_CHECKS && !p.packed && blockIdx.x == 0 && threadIdx.x == 0) p.hdr->flags = 0;
   int64_t item = n_items - 1 - (int64_t)blockIdx.x;
   if (item < 0) return;
   ItemRows<K> in = load_item_rows<K>(p, item), nx;

@@ -303,6 +303,14 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     widen8(in.g[kb], in.keep, gx[kb]);
   }
   const float beta_own = bits_to_f32((uint16_t)(in.beta & in.keep));
+  if (KDA_DEBUG_CHECKS && p.gate_mode == 0) {   // g is the log decay: g <= 0 is a precondition
+    bool pos = false;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pos = pos || gx[kb][j] > 0.f;
+    flag_if_any(&p.hdr->flags, pos, KDA_FLAG_GATE_POSITIVE);
+  }
   if (p.gate_mode && row_ok) {
     // In-kernel gate: z = exp(A_log_h) (g + dt_bias_hc), log decay lower_bound
     // * sigmoid(z) under the safe gate, else log sigmoid(z).

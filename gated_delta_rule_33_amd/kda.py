@@ -16,11 +16,13 @@ from typing import Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkda.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libkda_debug.so")   # same ABI, device checks of preconditions
 
 KDA_OK, KDA_ERR_INVALID_ARGUMENT, KDA_ERR_NOT_IMPLEMENTED, KDA_ERR_WORKSPACE_TOO_SMALL, KDA_ERR_HIP = range(5)
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_SEGMENT_OVERFLOW = 0x1
 KDA_FLAG_FUSED_TIMEOUT = 0x2
+KDA_FLAG_GATE_POSITIVE = 0x4   # raised only by libkda_debug.so
 KDA_STATIC_WORKSPACE_BYTES = 64 << 20   # the fixed workspace region of kda_chunk_fwd_noalloc, per GPU
 
 EXPORTED = ("kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_gated",
@@ -57,11 +59,26 @@ class KdaError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libkda.so (raises if it has not been built)."""
+def load_library(path: Optional[str] = None):
+    """Load the library once for this process (raises if it has not been
+    built): libkda.so, or libkda_debug.so (device checks of the input
+    preconditions, reported through the workspace flags) when the
+    environment sets KDA_LIBRARY=debug."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        if path is None:
+            path = DEBUG_LIB_PATH if os.environ.get("KDA_LIBRARY", "") == "debug" else LIB_PATH
+        _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str):
+    """Open a build of the library (libkda.so or libkda_debug.so) with its
+    argument types declared; not cached.  torch is imported first, so that
+    the library binds to the HIP runtime torch loaded (torch ships its own
+    copy; a process holding two runtimes cannot share device memory between
+    them)."""
+    import torch  # noqa: F401  (loads torch's HIP runtime before the library's dependency is resolved)
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with gated_delta_rule_33_amd/build.py "
                           "(or __graft_entry__.build())")
@@ -109,7 +126,6 @@ def load_library(path: str = LIB_PATH):
     lib.kda_set_fused_forward.restype = None
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.restype = ctypes.c_char_p
-    _lib = lib
     return lib
 
 

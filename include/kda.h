@@ -49,9 +49,18 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype_t;
 
 /* Flags reported by kda_chunk_fwd_flags(). */
 #define KDA_FLAG_SEGMENT_OVERFLOW 0x1u  /* a row held more than max_segments segments */
-#define KDA_FLAG_FUSED_TIMEOUT 0x2u     /* the fused forward gave up waiting for a chunk record
-                                           (another kernel held the device's compute units);
-                                           the outputs of that call are undefined */
+#define KDA_FLAG_FUSED_TIMEOUT 0x2u     /* a bounded wait of the fused forward ran out (not
+                                           expected: it only waits for records a running
+                                           workgroup is producing); the outputs of that call
+                                           are undefined */
+#define KDA_FLAG_GATE_POSITIVE 0x4u     /* some g > 0 reached a forward that takes g as the log
+                                           decay (g <= 0 is a precondition, page "feat(kda):
+                                           integrate KDA attention with tokamax backend and CP
+                                           support", Implementation Details: g is a log decay).
+                                           Checked only by the debug build of the library,
+                                           libkda_debug.so (KDA_DEBUG_CHECKS), whose results are
+                                           otherwise those of libkda.so; the release build never
+                                           sets it. */
 
 typedef struct {
   int64_t B, T, H;        /* >= 0 each; a zero size makes the call a no-op */

@@ -27,6 +27,15 @@ def test_library_exports_every_declared_symbol():
     for name in _declared_functions():
         assert hasattr(lib, name), name
     assert lib.kda_version().decode().startswith("kda-mi355x")
+    assert "debug" not in lib.kda_version().decode()
+
+
+def test_debug_library_exports_every_declared_symbol():
+    """libkda_debug.so (device checks of preconditions) has the same ABI."""
+    lib = kda.open_library(kda.DEBUG_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.kda_version().decode().endswith("debug-checks")
 
 
 def _desc(**kw):
