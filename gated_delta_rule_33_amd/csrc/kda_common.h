@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 constexpr int kChunk = 64;      // tokens per chunk
@@ -31,6 +33,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // Direct-to-LDS loads.  One instruction moves 16 bytes per lane from each
 // lane's global address to LDS at (M0 = wave-uniform LDS base) + 16 * lane,
@@ -99,6 +104,36 @@ __device__ __forceinline__ void split_bf16x2(float a, float b, bf16x2& hi, bf16x
   lo = to_bf16x2(a - __uint_as_float(hb << 16), b - __uint_as_float(hb & 0xffff0000u));
 }
 
+// Two floats rounded to fp16 (nearest even) with one packed conversion.
+__device__ __forceinline__ f16x2 to_f16x2(float a, float b) { return __builtin_convertvector(f32x2{a, b}, f16x2); }
+
+// A zero in a vector register that the compiler cannot see through: a load
+// whose address it offsets stays a vector-memory load (counted by vmcnt,
+// which barriers here do not wait for) even where the address is uniform.
+__device__ __forceinline__ int vector_zero() {
+  int y;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(y));
+  return y;
+}
+
+// Largest value of x >= 0 over the wave, as a wave-uniform value: DPP
+// shifts within each 16-lane row leave the row's largest in its lane 15,
+// two row broadcasts carry those to lane 63 (lanes a DPP move has no source
+// for read 0, which leaves a maximum of non-negative values alone).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_move<0x111, 0xF>(x));   // row_shr:1
+  x = fmaxf(x, dpp_move<0x112, 0xF>(x));   // row_shr:2
+  x = fmaxf(x, dpp_move<0x114, 0xF>(x));   // row_shr:4
+  x = fmaxf(x, dpp_move<0x118, 0xF>(x));   // row_shr:8
+  x = fmaxf(x, dpp_move<0x142, 0xA>(x));   // row_bcast:15 into rows 1 and 3
+  x = fmaxf(x, dpp_move<0x143, 0xC>(x));   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 // Input element loads (the raw input types are float and bf16 bits).
 __device__ __forceinline__ float load_in(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) { return bits_to_f32(p[i]); }
@@ -110,7 +145,8 @@ __device__ __forceinline__ float load_in(const uint16_t* p, int64_t i) { return 
 //          bits of significand with the range of fp32
 //   FragF  fp32 elements, multiplied on the fp32 matrix path
 // Products: B*B 1 instruction, P*B / B*P 2, P*P 3 (the lo*lo term is below
-// the pair's own rounding), F*F 8.
+// the pair's own rounding), F*F 8.  Two fp16 forms for the state update of
+// the recurrence (FragH, FragHP below): H*HP 2.
 struct FragB {
   bf16x8 v;
   static constexpr int kBytesPerLane = 16;
@@ -202,6 +238,79 @@ struct FragF {
   }
 };
 
+// One fp16 per element (11 bits of significand), rounded to nearest even.
+// Holds the decayed keys Kt of a record, each 16-key block scaled by a power
+// of two that brings its largest magnitude into [2^14, 2^15), so neither
+// overflow nor subnormals touch it whatever the keys' scale.
+struct FragH {
+  f16x8 v;
+  static constexpr int kBytesPerLane = 16;
+  __device__ __forceinline__ void set(const float x[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const f16x2 h = to_f16x2(x[j], x[j + 1]);
+      v[j] = h[0];
+      v[j + 1] = h[1];
+    }
+  }
+  __device__ __forceinline__ void load(const void* tile, int lane) {
+    v = reinterpret_cast<const f16x8*>(tile)[lane];
+  }
+  __device__ __forceinline__ void store(void* tile, int lane) const {
+    reinterpret_cast<f16x8*>(tile)[lane] = v;
+  }
+  // The same values as a bf16 pair (exact: 11 significant bits fit in two
+  // bf16 of 8 each, and the range of fp16 lies inside bf16's).
+  __device__ __forceinline__ FragP widen() const {
+    FragP r;
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      bf16x2 h, l;
+      split_bf16x2((float)v[j], (float)v[j + 1], h, l);
+      r.hi[j] = h[0]; r.hi[j + 1] = h[1];
+      r.lo[j] = l[0]; r.lo[j + 1] = l[1];
+    }
+    return r;
+  }
+};
+
+// An fp16 pair hi + lo with hi = fp16(x), lo = fp16(x - hi), both rounded to
+// nearest even: about 22 bits of significand where x and x - hi are normal
+// fp16 numbers (2^-3 <= |x| < 2^15), an absolute error within 2^-25 below;
+// its user scales x by a power of two into that range (recurrence state
+// update).
+struct FragHP {
+  f16x8 hi, lo;
+  static constexpr int kBytesPerLane = 32;
+  __device__ __forceinline__ void set(const float x[8]) {
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const f16x2 hp = to_f16x2(x[j], x[j + 1]);
+      const f16x2 lp = to_f16x2(x[j] - (float)hp[0], x[j + 1] - (float)hp[1]);
+      hi[j] = hp[0]; hi[j + 1] = hp[1];
+      lo[j] = lp[0]; lo[j + 1] = lp[1];
+    }
+  }
+  __device__ __forceinline__ void load(const void* tile, int lane) {
+    const f16x8* t = reinterpret_cast<const f16x8*>(tile);
+    hi = t[lane];
+    lo = t[64 + lane];
+  }
+  // Elements 4 half .. 4 half + 3 of this lane's fragment, split into a pair.
+  __device__ static __forceinline__ void store_half(void* tile, int lane, int half, const float x[4]) {
+    f16x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; j += 2) {
+      const f16x2 hp = to_f16x2(x[j], x[j + 1]);
+      const f16x2 lp = to_f16x2(x[j] - (float)hp[0], x[j + 1] - (float)hp[1]);
+      h[j] = hp[0]; h[j + 1] = hp[1];
+      l[j] = lp[0]; l[j + 1] = lp[1];
+    }
+    reinterpret_cast<f16x4*>(tile)[2 * lane + half] = h;
+    reinterpret_cast<f16x4*>(tile)[128 + 2 * lane + half] = l;
+  }
+};
+
 // Bytes one 16x32 fragment tile occupies in memory.
 template <class F>
 constexpr int tile_bytes() { return F::kBytesPerLane * kWave; }
@@ -224,6 +333,13 @@ __device__ __forceinline__ void mma(f32x4& c, const FragP& a, const FragP& b) {
   mfma_bb(c, a.hi, b.lo);
   mfma_bb(c, a.hi, b.hi);
 }
+__device__ __forceinline__ void mfma_hh(f32x4& c, const f16x8& a, const f16x8& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& c, const FragH& a, const FragHP& b) {
+  mfma_hh(c, a.v, b.lo);
+  mfma_hh(c, a.v, b.hi);
+}
 __device__ __forceinline__ void mma(f32x4& c, const FragF& a, const FragF& b) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a[j], b.a[j], c, 0, 0, 0);
@@ -234,7 +350,10 @@ __device__ __forceinline__ void mma(f32x4& c, const FragF& a, const FragF& b) {
 // Operand precisions per role.  bf16 inputs: the products whose rounding
 // reaches the output at the 1e-2 level use pairs; T, W and Qg stay single
 // bf16 (each costs at most a few 1e-3 of the output's rms on the benchmark
-// workloads), V is an exact bf16 input.  fp32 inputs: fp32 throughout.
+// workloads), V is an exact bf16 input.  The state update takes Kt as
+// block-scaled fp16 (half the bytes of a bf16 pair: the recurrence's step is
+// bound by the record bytes its waves load) and Delta as a scaled fp16 pair
+// (Du).  fp32 inputs: fp32 throughout.
 template <class TI> struct Prec;
 template <> struct Prec<uint16_t> {
   using A = FragP;   // exp-scaled q/k operands of the intra-chunk products
@@ -242,15 +361,16 @@ template <> struct Prec<uint16_t> {
   using X = FragP;   // beta * k * exp(G) for W
   using V = FragB;   // values (exact)
   using W = FragB;   // -W as stored for the recurrence
-  using Kt = FragP;  // k * exp(G_C - G) (state update)
+  using Kt = FragH;  // k * exp(G_C - G) 2^s per 16-key block (state update)
   using Qg = FragB;  // scale * q * exp(G) (output, inter-chunk part)
   using Aq = FragP;  // scale * Aqk (output, intra-chunk part)
   using S = FragP;   // the state as an operand
-  using D = FragP;   // the scaled residuals Delta as an operand
+  using D = FragP;   // the scaled residuals Delta as an operand (output)
+  using Du = FragHP; // Delta 2^t as the state update's operand
 };
 template <> struct Prec<float> {
   using A = FragF; using T = FragF; using X = FragF; using V = FragF; using W = FragF;
-  using Kt = FragF; using Qg = FragF; using Aq = FragF; using S = FragF; using D = FragF;
+  using Kt = FragF; using Qg = FragF; using Aq = FragF; using S = FragF; using D = FragF; using Du = FragF;
 };
 
 // ----------------------------------------------------------------------------
@@ -263,6 +383,8 @@ template <> struct Prec<float> {
 //   U   : T diag(beta) V in output-tile layout, rows = r, cols = value
 //         channel, [4][V/16] tiles of 64 lanes x 4 fp32
 //   Gc  : exp(G_C), K fp32 (decay of the whole chunk)
+//   Ks  : (bf16 inputs) 2^-s of each 16-key block of Kt, K/16 fp32: the
+//         stored block is Kt 2^s
 template <class TI, int K, int V>
 struct RecordLayout {
   using P = Prec<TI>;
@@ -278,7 +400,10 @@ struct RecordLayout {
   static constexpr int64_t kUBytes = 4 * (V / 16) * kWave * 16;
   static constexpr int64_t kGc = kU + kUBytes;
   static constexpr int64_t kGcBytes = K * 4;
-  static constexpr int64_t kBytes = ((kGc + kGcBytes) + 255) / 256 * 256;
+  static constexpr bool kScaledKt = std::is_same<typename P::Kt, FragH>::value;
+  static constexpr int64_t kKs = kGc + kGcBytes;
+  static constexpr int64_t kKsBytes = kScaledKt ? (K / 16) * 4 : 0;
+  static constexpr int64_t kBytes = ((kKs + kKsBytes) + 255) / 256 * 256;
 };
 
 // Chunk and segment tables built for packed inputs.

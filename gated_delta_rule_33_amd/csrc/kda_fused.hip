@@ -36,6 +36,7 @@
 // is still bounded: after kSpinLimit polls the wave gives up, raises
 // KDA_FLAG_FUSED_TIMEOUT and goes on (results are then undefined, but the
 // kernel ends).
+#include "kda_delta.h"
 #include "kda_intra_item.h"
 
 namespace kda {
@@ -154,10 +155,12 @@ __device__ __forceinline__ int64_t recur_lane(const FusedParams& p, int64_t sh, 
   using L = RecordLayout<uint16_t, K, V>;
   constexpr int NCB = K / 64;
   constexpr int KB = K / 32;
-  constexpr int TS = tile_bytes<PS>(), TD = tile_bytes<PD>();
+  using DL = DeltaLds<uint16_t>;
+  constexpr int TS = tile_bytes<PS>();
+  static_assert(KB * TS + sizeof(DL) + 4 * 16 * kOutLd * 4 <= sizeof(Intra4Smem<K, V>), "lane LDS");
   char* s_state = lds;
-  char* s_delta = s_state + KB * TS;
-  float* s_out = reinterpret_cast<float*>(s_delta + 2 * TD);   // [4][16 * kOutLd]
+  DL& s_delta = *reinterpret_cast<DL*>(s_state + KB * TS);
+  float* s_out = reinterpret_cast<float*>(s_state + KB * TS + sizeof(DL));   // [4][16 * kOutLd]
 
   const int lane = opaque((int)threadIdx.x) & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -175,6 +178,7 @@ __device__ __forceinline__ int64_t recur_lane(const FusedParams& p, int64_t sh, 
   f32x4 u;
   PK kt[NCB][2];
   f32x4 gc[NCB];
+  float ks[NCB];
   PQ qg[KB];
   PA aq[2];
   auto load_w = [&](const char* r) {
@@ -188,6 +192,7 @@ __device__ __forceinline__ int64_t recur_lane(const FusedParams& p, int64_t sh, 
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) kt[c][kb].load(r + L::kKt + (int64_t)((w * NCB + c) * 2 + kb) * tile_bytes<PK>(), lane);
       gc[c] = reinterpret_cast<const f32x4*>(r + L::kGc)[4 * (w * NCB + c) + gq];
+      ks[c] = reinterpret_cast<const float*>(r + L::kKs)[w * NCB + c + vector_zero()];
     }
   };
   auto load_q = [&](const char* r) {
@@ -239,29 +244,25 @@ __device__ __forceinline__ int64_t recur_lane(const FusedParams& p, int64_t sh, 
         if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
       }
       float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
-      PD::store_half(s_delta + (w / 2) * TD, lane, w & 1, x);
+      delta_store(s_delta, w, lane, x);
     }
     if (has_next) wait_ready(p.ready + rec_index(n + 1), hdr);
     load_w(rn1);
     block_sync();   // B1
 
-    PD dd[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta + kb * TD, lane);
+    DeltaOperands<uint16_t> du;
+    du.load(s_delta, lane);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-      f32x4 a0, a1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a0[i] = st[c][i] * gc[c][i];
-      mma(a0, kt[c][0], dd[0]);
-      mma(a1, kt[c][1], dd[1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[c][i] = a0[i] + a1[i];
+      state_update<uint16_t>(st[c], gc[c], ks[c], kt[c], du);
       float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
       const int cb = w * NCB + c;
       PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
     }
     load_kt(rn1);
+    PD dd[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta.d + kb * DL::TD, lane);
 
     f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
 #pragma unroll

@@ -544,7 +544,8 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   // Kt = (k exp(G_C - G))^T tiles [c-block][token slab] from columns of X:
   // k_r exp(G_C - G_r) = X_r exp(G_C - G_l(I(r))).  The waves with fewer A
   // tiles above take more channel blocks: 4, 3, 1, 0 of 8 (K = 128) or
-  // 2, 1, 1, 0 of 4 (K = 64).
+  // 2, 1, 1, 0 of 4 (K = 64).  Each 16-key block is stored as fp16 times
+  // 2^s, s putting its largest magnitude in [2^14, 2^15), with 2^-s beside.
   constexpr int NCBK = K / 16;
   auto kt_bound = [](int w) { return NCBK == 8 ? (w == 0 ? 0 : w == 1 ? 4 : w == 2 ? 7 : 8)
                                                : (w == 0 ? 0 : w == 1 ? 2 : w == 2 ? 3 : 4); };
@@ -553,20 +554,34 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   for (int u = 0; u < NCBK / 2; ++u) {
     const int cb = kt_begin + u, c = 16 * cb + m;
     if (cb >= kt_end) break;
+    float kt[2][8];
+    float mx = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      float xv[8], kt[8];
+      float xv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) xv[j] = sm.X[(32 * kb + kperm(gq, j)) * S::XP + c];   // all reads first
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 32 * kb + kperm(gq, j);
-        kt[j] = xv[j] * sm.ktf[r >> 4][c] * sm.nk[r];
+        kt[kb][j] = xv[j] * sm.ktf[r >> 4][c] * sm.nk[r];
+        mx = fmaxf(mx, fabsf(kt[kb][j]));
       }
+    }
+    // max = f 2^e with f in [1/2, 1): 2^(15 - e) brings it into [2^14, 2^15)
+    // (for 0, inf and NaN the exponent reads 0, and the values pass as they are).
+    const int e = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_frexp_expf(wave_max(mx)));
+    const int sh = min(max(15 - e, -100), 100);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = ldexpf(kt[kb][j], sh);
       PK fr;
-      fr.set(kt);
+      fr.set(y);
       fr.store(rec + L::kKt + (int64_t)(cb * 2 + kb) * tile_bytes<PK>(), lane);
     }
+    if (lane == 0) reinterpret_cast<float*>(rec + L::kKs)[cb] = ldexpf(1.f, -sh);
   }
   block_sync();   // B3: A^T in M; X is dead
   // W's operand rows nk k exp(G) take X's place (read as columns after the

@@ -14,6 +14,7 @@
 // every other operand is read straight into registers from the per-chunk
 // records the intra-chunk kernel wrote, one chunk ahead, while a prefetch
 // wave pulls later records into L2.
+#include "kda_delta.h"
 #include "kda_launch.h"
 
 namespace kda {
@@ -97,9 +98,9 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   // S and Delta as operand tiles in fragment order (k = key channel / token):
   // the accumulator rows a wave holds are one half of the same lane's
   // fragment, and each lane reads its fragment as whole 16-byte words.
-  constexpr int TS = tile_bytes<PS>(), TD = tile_bytes<PD>();
+  constexpr int TS = tile_bytes<PS>();
   __shared__ __align__(16) char s_state[KB * TS];
-  __shared__ __align__(16) char s_delta[2 * TD];
+  __shared__ __align__(16) DeltaLds<TI> s_delta;
   __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
   __shared__ __align__(16) float s_out[kComputeWaves][kChunk / kComputeWaves * kOutLd];
 
@@ -170,6 +171,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   f32x4 u;
   PK kt[NCB][2];
   f32x4 gc[NCB];
+  float ks[NCB];
   PQ qg[KB];
   PA aq[2];
   auto load_w = [&](const char* r) {
@@ -184,6 +186,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) kt[c][kb].load(r + L::kKt + (int64_t)((w * NCB + c) * 2 + kb) * tile_bytes<PK>(), lane);
       gc[c] = reinterpret_cast<const f32x4*>(r + L::kGc)[4 * (w * NCB + c) + gq];
+      ks[c] = L::kScaledKt ? reinterpret_cast<const float*>(r + L::kKs)[w * NCB + c + vector_zero()] : 1.f;
     }
   };
   auto load_q = [&](const char* r) {
@@ -236,24 +239,17 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
         if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
       }
       float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
-      PD::store_half(s_delta + (w / 2) * TD, lane, w & 1, x);
+      delta_store(s_delta, w, lane, x);
     }
     load_w(rn1);
     block_sync();   // B1
 
     // S <- diag(exp(G_C)) S + Kt^T Delta
-    PD dd[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta + kb * TD, lane);
+    DeltaOperands<TI> dd;
+    dd.load(s_delta, lane);
 #pragma unroll
     for (int c = 0; c < NCB; ++c) {
-      f32x4 a0, a1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a0[i] = st[c][i] * gc[c][i];
-      mma(a0, kt[c][0], dd[0]);
-      mma(a1, kt[c][1], dd[1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st[c][i] = a0[i] + a1[i];
+      state_update<TI>(st[c], gc[c], ks[c], kt[c], dd);
       float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
       const int cb = w * NCB + c;
       PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
@@ -268,8 +264,11 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
         mma(o0, qg[kb], sf[kb]);
         if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
       }
-      mma(o1, aq[0], dd[0]);
-      if (w >= 2) mma(o0, aq[1], dd[1]);
+      PD od[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) od[kb].load(s_delta.d + kb * DeltaLds<TI>::TD, lane);
+      mma(o1, aq[0], od[0]);
+      if (w >= 2) mma(o0, aq[1], od[1]);
       load_q(rn1);
       float* tl = s_out[w];
 #pragma unroll
@@ -330,10 +329,10 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
   constexpr int NV = V / (kVT * NT);   // workgroups per (sequence, head)
   constexpr int NCB = K / 64;
   constexpr int KB = K / 32;
-  constexpr int TS = tile_bytes<PS>(), TD = tile_bytes<PD>();
+  constexpr int TS = tile_bytes<PS>();
   constexpr int OLD = kVT * NT + 4;    // row pitch of the output staging tile
   __shared__ __align__(16) char s_state[2][NT][KB * TS];
-  __shared__ __align__(16) char s_delta[NT][2 * TD];
+  __shared__ __align__(16) DeltaLds<TI> s_delta[NT];
   __shared__ __align__(16) float s_out[kComputeWaves][kChunk / kComputeWaves * OLD];
   __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
 
@@ -402,6 +401,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
     f32x4 u[NT];
     PK kt[NCB][2];
     f32x4 gc[NCB];
+    float ks[NCB];
     auto load_w = [&](const char* r) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
@@ -416,6 +416,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
         for (int kb = 0; kb < 2; ++kb)
           kt[c][kb].load(r + L::kKt + (int64_t)((w * NCB + c) * 2 + kb) * tile_bytes<PK>(), lane);
         gc[c] = reinterpret_cast<const f32x4*>(r + L::kGc)[4 * (w * NCB + c) + gq];
+        ks[c] = L::kScaledKt ? reinterpret_cast<const float*>(r + L::kKs)[w * NCB + c + vector_zero()] : 1.f;
       }
     };
     f32x4 st[NT][NCB];
@@ -454,27 +455,19 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
           if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
         }
         float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
-        PD::store_half(s_delta[t] + (w / 2) * TD, lane, w & 1, x);
+        delta_store(s_delta[t], w, lane, x);
       }
       load_w(rn1);
       block_sync();   // B1
       // S <- diag(exp(G_C)) S + Kt^T Delta, into the other buffer
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        PD dd[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta[t] + kb * TD, lane);
-        __builtin_amdgcn_sched_barrier(0);
+        DeltaOperands<TI> dd;
+        dd.load(s_delta[t], lane);
         char* nxt = s_state[(n + 1) & 1][t];
 #pragma unroll
         for (int c = 0; c < NCB; ++c) {
-          f32x4 a0, a1 = {0, 0, 0, 0};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) a0[i] = st[t][c][i] * gc[c][i];
-          mma(a0, kt[c][0], dd[0]);
-          mma(a1, kt[c][1], dd[1]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) st[t][c][i] = a0[i] + a1[i];
+          state_update<TI>(st[t][c], gc[c], ks[c], kt[c], dd);
           float x[4] = {st[t][c][0], st[t][c][1], st[t][c][2], st[t][c][3]};
           const int cb = w * NCB + c;
           PS::store_half(nxt + (cb / 2) * TS, lane, cb & 1, x);
@@ -524,7 +517,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
       for (int kb = 0; kb < KB; ++kb) sf[kb].load(cur + kb * TS, lane);
       PD dd[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta[t] + kb * TD, lane);
+      for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta[t].d + kb * DeltaLds<TI>::TD, lane);
       __builtin_amdgcn_sched_barrier(0);   // every operand read issued before the products
       f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
 #pragma unroll
