@@ -9,8 +9,9 @@
 //
 // Layout of the work.  Two workgroups of four waves run on every compute unit
 // (about 66 KB of LDS each).  The first to arrive on a CU runs recurrence
-// lanes: one (row, head, 16 value columns) each, chunk by chunk, exactly the
-// loop of the register-direct recurrence kernel; the second produces records
+// lanes: one (row, head, 16 value columns) each, chunk by chunk, four waves
+// each doing both the chain and the read-out of its token block (the state
+// update of kda_delta.h); the second produces records
 // (the intra-chunk item of kda_intra_item.h) from a queue.  A sequence-head
 // (b, h) belongs to XCD (b H + h) mod n_xcd: its lanes and its records are
 // handled only by workgroups whose hardware XCC_ID is that XCD, so producer

@@ -22,7 +22,6 @@ namespace {
 
 constexpr int kVT = 16;   // value channels per workgroup
 constexpr int kComputeWaves = 4;   // per value tile
-constexpr int kPrefetchAhead = 0;   // extra chunks between the L2 prefetch and the use of a record
 
 // Four consecutive outputs o[i .. i + 3] (i a multiple of 4).  The stores
 // are non-temporal: o is not read again by this forward, and streaming it
@@ -40,12 +39,6 @@ __device__ __forceinline__ void store_out4(uint16_t* o, int64_t i, const f32x4& 
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(o + i));
 }
-// The output tile of a wave (lane (g, n) holding token rows 4g + i, column n)
-// goes through a padded LDS tile of its own, so each lane stores four
-// consecutive columns of one row; row stride 20 keeps both sides free of
-// bank conflicts.
-constexpr int kOutLd = 20;
-
 struct RecurParams {
   int64_t B, T, H;
   int64_t nc_fixed;
@@ -61,48 +54,38 @@ struct RecurParams {
   float* trans;   // [B,H,K,K] transition of each row's carried state, or NULL
 };
 
-// One value tile per workgroup, operands straight to registers.  Each
-// compute wave's share of a record (its token block of Wn, U, Qg and Aqk,
-// its key-channel blocks of Kt and exp(G_C)) is read by that wave alone, so
-// it is loaded into the wave's registers one chunk ahead, each group right
-// after its last use; only S and Delta pass through LDS.  Two barriers per
-// chunk: B1 after the Delta phase (Delta visible), B2 at the end (the new
-// state visible, the Delta buffer free).  The fifth wave pulls the next
-// chunk's record into L2 (further ahead, the lines wait in L2 longer and
-// more of them are evicted before use).
+// The transition of a row's first segment, for context parallelism: the
+// recurrence is affine in the state a segment starts from, S_end = M S_start
+// + (S_end for S_start = 0), and M is the chunk product of diag(exp(G_C)) -
+// Kt^T W, i.e. the state recurrence with U = 0 and S_start = I, with no
+// read-out.  Its columns (K of them, one 16-wide tile per workgroup) index
+// the key channels of S_start.  It exists only where one segment runs from
+// the row's first token to its last (every row without segment ids); the
+// caller zero-fills the others.  This is the transfer matrix a
+// context-parallel rank passes on with its end state.
 //
-// With kTrans the same loop carries, instead of the state, the transition of
-// a row's first segment: the recurrence is affine in the state a segment
-// starts from, S_end = M S_start + (S_end for S_start = 0), and M is the
-// chunk product of diag(exp(G_C)) - Kt^T W, i.e. the loop above with U = 0
-// and S_start = I, with no read-out.  Its columns (K of them, one 16-wide
-// tile per workgroup) index the key channels of S_start.  It exists only
-// where one segment runs from the row's first token to its last (every row
-// without segment ids); the caller zero-fills the others.  This is the
-// transfer matrix a context-parallel rank passes on with its end state.
-template <class TI, class TO, int K, int V, bool kTrans>
-__global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_kernel(RecurParams p) {
+// Four compute waves (wave w: Delta for tokens 16w.., the update of
+// key-channel blocks w K/64..), each loading its share of a record (its token
+// block of Wn, its key blocks of Kt and exp(G_C)) into registers one chunk
+// ahead; S and Delta pass through LDS.  Two barriers per chunk: B1 after the
+// Delta phase (Delta visible), B2 at the end (the new state visible, the
+// Delta buffer free).  The fifth wave pulls the next chunk's Wn and Kt into
+// L2.
+template <class TI, int K, int V>
+__global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_trans_kernel(RecurParams p) {
   using P = Prec<TI>;
   using PS = typename P::S;
-  using PD = typename P::D;
   using PW = typename P::W;
   using PK = typename P::Kt;
-  using PQ = typename P::Qg;
-  using PA = typename P::Aq;
   using L = RecordLayout<TI, K, V>;
   constexpr int kPrefetchWave = kComputeWaves;
-  constexpr int NCOL = kTrans ? K : V;   // columns of the carried matrix
-  constexpr int NV = NCOL / kVT;   // workgroups per (sequence, head)
+  constexpr int NV = K / kVT;      // workgroups per (sequence, head)
   constexpr int NCB = K / 64;      // key-channel blocks of the state per wave
   constexpr int KB = K / 32;       // 32-deep key slabs
-  // S and Delta as operand tiles in fragment order (k = key channel / token):
-  // the accumulator rows a wave holds are one half of the same lane's
-  // fragment, and each lane reads its fragment as whole 16-byte words.
   constexpr int TS = tile_bytes<PS>();
   __shared__ __align__(16) char s_state[KB * TS];
   __shared__ __align__(16) DeltaLds<TI> s_delta;
   __shared__ __align__(16) char s_sink[1024];   // discarded data of the L2 prefetches
-  __shared__ __align__(16) float s_out[kComputeWaves][kChunk / kComputeWaves * kOutLd];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,30 +102,24 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
   if (seq_head >= n_seq_heads) return;
   const int64_t h = seq_head % H, sq = seq_head / H;
 
-  int64_t b, slot, n_chunks, first_chunk, t_begin, seq_len;
+  int64_t b, n_chunks, first_chunk;
   if (p.packed) {
     const SegEntry se = p.segs[sq];
-    if (kTrans && (se.t0 != 0 || se.len != p.T)) return;   // no segment spans this row
+    if (se.t0 != 0 || se.len != p.T) return;   // no segment spans this row
     b = se.b;
-    slot = ((int64_t)se.b * p.n_max + se.local) * H + h;
     n_chunks = se.n_chunks;
     first_chunk = se.chunk_begin;
-    t_begin = se.t0;
-    seq_len = se.len;
   } else {
     b = sq;
-    slot = b * H + h;
     n_chunks = p.nc_fixed;
     first_chunk = b * p.nc_fixed;
-    t_begin = 0;
-    seq_len = p.T;
   }
   auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
 
-  // ---- L2 prefetch wave: touches this workgroup's 1/NV share of the record
-  // kPrefetchAhead chunks ahead (every 64-byte segment once).
+  // ---- L2 prefetch wave: this workgroup's 1/NV share of the record's Wn and
+  // Kt (every 64-byte segment once), one chunk ahead.
   if (wave == kPrefetchWave) {
-    constexpr int SEGS = (int)((kTrans ? L::kQg : L::kBytes) / 64);   // the transition reads Wn and Kt only
+    constexpr int SEGS = (int)(L::kQg / 64);
     constexpr int SHARE = (SEGS + NV - 1) / NV;
     auto prefetch = [&](int64_t n) {
       const char* r = record(n);
@@ -152,10 +129,9 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
         if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
       }
     };
-    for (int64_t n = 1; n <= kPrefetchAhead && n < n_chunks; ++n) prefetch(n);
     block_sync();
     for (int64_t n = 0; n < n_chunks; ++n) {
-      if (n + kPrefetchAhead + 1 < n_chunks) prefetch(n + kPrefetchAhead + 1);
+      if (n + 1 < n_chunks) prefetch(n + 1);
       block_sync();   // B1
       block_sync();   // B2
     }
@@ -165,20 +141,14 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
 
   // ---- compute wave w: token block w, key-channel blocks w*NCB .. +NCB-1
   const int w = wave;
-  TO* out = static_cast<TO*>(p.o);
-  const int v0 = kVT * j;
+  const int v0 = kVT * j;   // first column of M this workgroup carries
   PW wn[KB];
-  f32x4 u;
   PK kt[NCB][2];
   f32x4 gc[NCB];
   float ks[NCB];
-  PQ qg[KB];
-  PA aq[2];
   auto load_w = [&](const char* r) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
-    if constexpr (kTrans) u = f32x4{0, 0, 0, 0};
-    else u = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + j) * 1024)[lane];
   };
   auto load_kt = [&](const char* r) {
 #pragma unroll
@@ -189,50 +159,32 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
       ks[c] = L::kScaledKt ? reinterpret_cast<const float*>(r + L::kKs)[w * NCB + c + vector_zero()] : 1.f;
     }
   };
-  auto load_q = [&](const char* r) {
-    if constexpr (kTrans) return;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PA>(), lane);
-  };
 
-  // State slice: lane (column v0 + m, rows 16cb + 4gq + i) of its blocks.
+  // M's slice: lane (column v0 + m, rows 16cb + 4gq + i) of its blocks, from I.
   f32x4 st[NCB];
 #pragma unroll
   for (int c = 0; c < NCB; ++c) {
     const int c0 = 16 * (w * NCB + c) + 4 * gq;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (kTrans) st[c][i] = (c0 + i == v0 + m) ? 1.f : 0.f;
-      else st[c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + m] : 0.f;
-    }
+    for (int i = 0; i < 4; ++i) st[c][i] = (c0 + i == v0 + m) ? 1.f : 0.f;
     float x[4] = {st[c][0], st[c][1], st[c][2], st[c][3]};
     const int cb = w * NCB + c;
     PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
   }
   if (n_chunks > 0) {
-    const char* r0 = record(0);
-    load_w(r0);
-    load_kt(r0);
-    load_q(r0);
+    load_w(record(0));
+    load_kt(record(0));
   }
   block_sync();
 
   for (int64_t n = 0; n < n_chunks; ++n) {
-    const int64_t t0 = t_begin + n * kChunk;
-    const int len = (int)min<int64_t>(kChunk, seq_len - n * kChunk);
     const char* rn1 = record(n + 1 < n_chunks ? n + 1 : n);
-
-    // Delta = U - W S for tokens 16w..16w+15; the S operand stays in
-    // registers for the output phase.  Two accumulators halve the
-    // dependent chain.
+    // Delta = -W M for tokens 16w..16w+15 (two accumulators halve the chain)
     PS sf[KB];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sf[kb].load(s_state + kb * TS, lane);
     {
-      f32x4 d0 = u, d1 = {0, 0, 0, 0};
+      f32x4 d0 = {0, 0, 0, 0}, d1 = {0, 0, 0, 0};
 #pragma unroll
       for (int kb = 0; kb < KB; kb += 2) {
         mma(d0, wn[kb], sf[kb]);
@@ -244,7 +196,7 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
     load_w(rn1);
     block_sync();   // B1
 
-    // S <- diag(exp(G_C)) S + Kt^T Delta
+    // M <- diag(exp(G_C)) M + Kt^T Delta
     DeltaOperands<TI> dd;
     dd.load(s_delta, lane);
 #pragma unroll
@@ -255,45 +207,14 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_reg_ker
       PS::store_half(s_state + (cb / 2) * TS, lane, cb & 1, x);
     }
     load_kt(rn1);
-
-    if constexpr (!kTrans) {
-      // O = scale Qg S + scale Aqk Delta for tokens 16w..16w+15
-      f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
-#pragma unroll
-      for (int kb = 0; kb < KB; kb += 2) {
-        mma(o0, qg[kb], sf[kb]);
-        if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
-      }
-      PD od[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) od[kb].load(s_delta.d + kb * DeltaLds<TI>::TD, lane);
-      mma(o1, aq[0], od[0]);
-      if (w >= 2) mma(o0, aq[1], od[1]);
-      load_q(rn1);
-      float* tl = s_out[w];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tl[(4 * gq + i) * kOutLd + m] = o0[i] + o1[i];
-      const int r = lane >> 2, q4 = 4 * (lane & 3);
-      const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * kOutLd + q4);
-      if (16 * w + r < len) store_out4(out, ((b * p.T + t0 + 16 * w + r) * H + h) * V + v0 + q4, x);
-    }
     block_sync();   // B2
   }
 
-  if constexpr (kTrans) {
 #pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      const int c0 = 16 * (w * NCB + c) + 4 * gq;
+  for (int c = 0; c < NCB; ++c) {
+    const int c0 = 16 * (w * NCB + c) + 4 * gq;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p.trans[((b * H + h) * K + c0 + i) * K + v0 + m] = st[c][i];
-    }
-  } else if (p.fin) {
-#pragma unroll
-    for (int c = 0; c < NCB; ++c) {
-      const int c0 = 16 * (w * NCB + c) + 4 * gq;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p.fin[(slot * K + c0 + i) * V + v0 + m] = st[c][i];
-    }
+    for (int i = 0; i < 4; ++i) p.trans[((b * H + h) * K + c0 + i) * K + v0 + m] = st[c][i];
   }
 }
 
@@ -558,7 +479,7 @@ hipError_t launch_recur_t(const CallArgs& a) {
       if (e != hipSuccess) return e;
     }
     const int64_t tgrid = (seq_heads + 7) / 8 * 8 * (K / kVT);
-    hipLaunchKernelGGL((kda_recur_reg_kernel<TI, TO, K, V, true>), dim3((unsigned)tgrid),
+    hipLaunchKernelGGL((kda_recur_trans_kernel<TI, K, V>), dim3((unsigned)tgrid),
                        dim3((kComputeWaves + 1) * kWave), 0, a.stream, p);
     return hipGetLastError();
   }
