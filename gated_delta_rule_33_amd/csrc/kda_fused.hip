@@ -117,8 +117,12 @@ __device__ __forceinline__ void produce(const FusedParams& p, int64_t item, char
   if (threadIdx.x == 0) __hip_atomic_store(p.ready + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Four consecutive outputs.  Plain stores: a lane's 16 value columns fill
+// half of each 128-byte line of fp32 o, and L2 joins the two halves (the
+// neighbouring tile's lane writes the other); streamed partial lines would
+// each be written back at the cost of a whole line.
 __device__ __forceinline__ void store_out4(float* o, int64_t i, const f32x4& x) {
-  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(o + i));
+  *reinterpret_cast<f32x4*>(o + i) = x;
 }
 __device__ __forceinline__ void store_out4(uint16_t* o, int64_t i, const f32x4& x) {
   uint32_t w[2];
@@ -128,7 +132,7 @@ __device__ __forceinline__ void store_out4(uint16_t* o, int64_t i, const f32x4& 
     w[j] = (uint32_t)*reinterpret_cast<const uint16_t*>(&a) | ((uint32_t)*reinterpret_cast<const uint16_t*>(&b) << 16);
   }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(o + i));
+  *reinterpret_cast<u32x2*>(o + i) = u32x2{w[0], w[1]};
 }
 
 // One recurrence lane: sequence-head sh (row b, head h), value columns

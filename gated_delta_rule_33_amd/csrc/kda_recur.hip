@@ -23,12 +23,17 @@ namespace {
 constexpr int kVT = 16;   // value channels per workgroup
 constexpr int kComputeWaves = 4;   // per value tile
 
-// Four consecutive outputs o[i .. i + 3] (i a multiple of 4).  The stores
-// are non-temporal: o is not read again by this forward, and streaming it
-// past the caches leaves them to the chunk records.
+// Four consecutive outputs o[i .. i + 3] (i a multiple of 4), as plain
+// stores or, with kStream, non-temporal ones (o is not read again by this
+// forward: streaming it past L2 leaves L2 to the chunk records).  Streaming
+// pays only where each store instruction covers whole 128-byte lines:
+// partial lines are written back separately, each at the cost of a line.
+template <bool kStream>
 __device__ __forceinline__ void store_out4(float* o, int64_t i, const f32x4& x) {
-  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(o + i));
+  if constexpr (kStream) __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(o + i));
+  else *reinterpret_cast<f32x4*>(o + i) = x;
 }
+template <bool kStream>
 __device__ __forceinline__ void store_out4(uint16_t* o, int64_t i, const f32x4& x) {
   uint32_t w[2];
 #pragma unroll
@@ -37,7 +42,8 @@ __device__ __forceinline__ void store_out4(uint16_t* o, int64_t i, const f32x4& 
     w[j] = (uint32_t)*reinterpret_cast<const uint16_t*>(&a) | ((uint32_t)*reinterpret_cast<const uint16_t*>(&b) << 16);
   }
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(o + i));
+  if constexpr (kStream) __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(o + i));
+  else *reinterpret_cast<u32x2*>(o + i) = u32x2{w[0], w[1]};
 }
 struct RecurParams {
   int64_t B, T, H;
@@ -452,14 +458,19 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
       for (int i = 0; i < 4; ++i) tl[(4 * gq + i) * OLD + 16 * t + m] = o0[i] + o1[i];
     }
     load_q(rn1);
-    // Row r of the tile from its 4 lanes: 4 NT consecutive columns each.
-    constexpr int LPR = 4;                  // lanes per row
-    constexpr int CPL = kVT * NT / LPR;     // columns per lane
-    const int r = lane / LPR, q = CPL * (lane % LPR);
+    // Rows of the tile from LPR lanes each, 4 consecutive columns per lane:
+    // every store instruction writes whole row pieces of the tile's 16 NT
+    // columns (with NT = 2 whole 128-byte lines of fp32 o, streamed; with one
+    // tile a line is shared by two workgroups, and plain stores let L2 join
+    // its halves).
+    constexpr int LPR = kVT * NT / 4;   // lanes per row
+    constexpr int RPI = kWave / LPR;    // rows per store instruction
+    const int q = 4 * (lane % LPR);
 #pragma unroll
-    for (int e = 0; e < CPL; e += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * OLD + q + e);
-      if (16 * w + r < len) store_out4(out, ((b * p.T + t0 + 16 * w + r) * H + h) * V + v0 + q + e, x);
+    for (int r0 = 0; r0 < kChunk / kComputeWaves; r0 += RPI) {
+      const int r = r0 + lane / LPR;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * OLD + q);
+      if (16 * w + r < len) store_out4<NT == 2>(out, ((b * p.T + t0 + 16 * w + r) * H + h) * V + v0 + q, x);
     }
     block_sync();   // B2
   }
