@@ -58,6 +58,7 @@ struct RecurParams {
   float* fin;
   void* o;
   float* trans;   // [B,H,K,K] transition of each row's carried state, or NULL
+  int64_t n_units;   // split kernel: units of work (sequence, head, value tiles) of the grid's numbering
 };
 
 // The transition of a row's first segment, for context parallelism: the
@@ -271,52 +272,87 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
   const int m = lane & 15, gq = lane >> 4;
   const int64_t H = p.H;
 
-  // XCD-aware decode, as above.
-  const int64_t id = blockIdx.x;
-  const int64_t seq_head = (id / (8 * NV)) * 8 + id % 8;
-  const int j = (int)((id / 8) % NV);
+  // Units of work: (sequence, head, NT value tiles), numbered XCD-aware as
+  // above (the NV units of a (sequence, head) share id % 8, so they share an
+  // L2).  Workgroup g takes units g, g + gridDim.x, ...: with gridDim.x a
+  // multiple of 8 NV each workgroup keeps one column j and one XCD, and the
+  // sequence-head grows with every step, so the first one past the last
+  // ends the walk.  Each unit's first records are loaded during the last
+  // chunks of the one before.
   const int64_t n_seq_heads = p.packed ? (int64_t)p.hdr->n_segments * H : p.n_seq_heads_fixed;
-  if (seq_head >= n_seq_heads) return;
-  const int64_t h = seq_head % H, sq = seq_head / H;
-
-  int64_t b, slot, n_chunks, first_chunk, t_begin, seq_len;
-  if (p.packed) {
-    const SegEntry se = p.segs[sq];
-    b = se.b;
-    slot = ((int64_t)se.b * p.n_max + se.local) * H + h;
-    n_chunks = se.n_chunks;
-    first_chunk = se.chunk_begin;
-    t_begin = se.t0;
-    seq_len = se.len;
-  } else {
-    b = sq;
-    slot = b * H + h;
-    n_chunks = p.nc_fixed;
-    first_chunk = b * p.nc_fixed;
-    t_begin = 0;
-    seq_len = p.T;
-  }
-  auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
-  const int v0 = kVT * NT * j;   // first value column of tile 0
+  struct Unit {
+    int64_t slot, first_chunk;
+    int h, b, n_chunks, t_begin, seq_len, j;
+    bool valid;
+  };
+  auto decode = [&](int64_t id) {
+    Unit u;
+    const int64_t seq_head = (id / (8 * NV)) * 8 + id % 8;
+    u.j = (int)((id / 8) % NV);
+    u.valid = id < p.n_units && seq_head < n_seq_heads;
+    if (!u.valid) return u;
+    u.h = (int)(seq_head % H);
+    const int64_t sq = seq_head / H;
+    if (p.packed) {
+      const SegEntry se = p.segs[sq];
+      u.b = se.b;
+      u.slot = ((int64_t)se.b * p.n_max + se.local) * H + u.h;
+      u.n_chunks = se.n_chunks;
+      u.first_chunk = se.chunk_begin;
+      u.t_begin = se.t0;
+      u.seq_len = se.len;
+    } else {
+      u.b = (int)sq;
+      u.slot = sq * H + u.h;
+      u.n_chunks = (int)p.nc_fixed;
+      u.first_chunk = sq * p.nc_fixed;
+      u.t_begin = 0;
+      u.seq_len = (int)p.T;
+    }
+    return u;
+  };
+  int64_t uid = blockIdx.x;
+  Unit cur = decode(uid);
+  if (!cur.valid) return;
+  Unit nxt = decode(uid + gridDim.x);
+  auto record = [&](const Unit& u, int64_t n) {
+    return p.records + ((u.first_chunk + n) * H + u.h) * p.record_bytes;
+  };
+  // The record after chunk n of the current unit: its next chunk, else the
+  // next unit's first (else chunk n again, loaded and not used).
+  auto record_after = [&](int64_t n) {
+    return n + 1 < cur.n_chunks ? record(cur, n + 1) : (nxt.valid ? record(nxt, 0) : record(cur, n));
+  };
+  auto advance = [&] {
+    cur = nxt;
+    uid += gridDim.x;
+    nxt = decode(uid + gridDim.x);
+  };
 
   if (prefetcher) {
-    // ---- every 64-byte segment of the workgroup's 1/NV share of a record, once
-    auto prefetch = [&](int64_t n) {
+    // ---- every 64-byte segment of the workgroup's 1/NV share of a record,
+    //      two records ahead in the workgroup's sequence of records
+    auto prefetch = [&](const char* r, int jj) {
       constexpr int SEGS = (int)(L::kBytes / 64);
       constexpr int SHARE = (SEGS + NV - 1) / NV;
-      const char* r = record(n);
 #pragma unroll
       for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
-        const int e = i * kWave + lane, seg = j * SHARE + e;
+        const int e = i * kWave + lane, seg = jj * SHARE + e;
         if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
       }
     };
-    if (n_chunks > 1) prefetch(1);
-    block_sync();   // B0
-    for (int64_t n = 0; n < n_chunks; ++n) {
-      if (n + 2 < n_chunks) prefetch(n + 2);
-      block_sync();   // B1
-      block_sync();   // B2
+    if (cur.n_chunks > 1) prefetch(record(cur, 1), cur.j);
+    for (;;) {
+      block_sync();   // B0
+      for (int64_t n = 0; n < cur.n_chunks; ++n) {
+        const int64_t a = n + 2;
+        if (a < cur.n_chunks) prefetch(record(cur, a), cur.j);
+        else if (nxt.valid && a - cur.n_chunks < nxt.n_chunks) prefetch(record(nxt, a - cur.n_chunks), nxt.j);
+        block_sync();   // B1
+        block_sync();   // B2
+      }
+      if (!nxt.valid) break;
+      advance();
     }
     vm_wait<0>();   // the prefetches' LDS writes land before the workgroup ends
     return;
@@ -329,12 +365,12 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
     PK kt[NCB][2];
     f32x4 gc[NCB];
     float ks[NCB];
-    auto load_w = [&](const char* r) {
+    auto load_w = [&](const char* r, int jj) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) wn[kb].load(r + L::kWn + (int64_t)(w * KB + kb) * tile_bytes<PW>(), lane);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        u[t] = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + NT * j + t) * 1024)[lane];
+        u[t] = reinterpret_cast<const f32x4*>(r + L::kU + (int64_t)(w * (V / 16) + NT * jj + t) * 1024)[lane];
     };
     auto load_kt = [&](const char* r) {
 #pragma unroll
@@ -346,73 +382,77 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
         ks[c] = L::kScaledKt ? reinterpret_cast<const float*>(r + L::kKs)[w * NCB + c + vector_zero()] : 1.f;
       }
     };
-    f32x4 st[NT][NCB];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int c = 0; c < NCB; ++c) {
-        const int c0 = 16 * (w * NCB + c) + 4 * gq;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          st[t][c][i] = p.init ? p.init[(slot * K + c0 + i) * V + v0 + 16 * t + m] : 0.f;
-        float x[4] = {st[t][c][0], st[t][c][1], st[t][c][2], st[t][c][3]};
-        const int cb = w * NCB + c;
-        PS::store_half(s_state[0][t] + (cb / 2) * TS, lane, cb & 1, x);
-      }
-    }
-    if (n_chunks > 0) {
-      load_w(record(0));
-      load_kt(record(0));
-    }
-    block_sync();   // B0
-    for (int64_t n = 0; n < n_chunks; ++n) {
-      const char* rn1 = record(n + 1 < n_chunks ? n + 1 : n);
-      // Delta = U - W S for tokens 16w..16w+15, tile by tile
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const char* cur = s_state[n & 1][t];
-        PS sf[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) sf[kb].load(cur + kb * TS, lane);
-        __builtin_amdgcn_sched_barrier(0);   // every operand read issued before the products
-        f32x4 d0 = u[t], d1 = {0, 0, 0, 0};
-#pragma unroll
-        for (int kb = 0; kb < KB; kb += 2) {
-          mma(d0, wn[kb], sf[kb]);
-          if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
-        }
-        float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
-        delta_store(s_delta[t], w, lane, x);
-      }
-      load_w(rn1);
-      block_sync();   // B1
-      // S <- diag(exp(G_C)) S + Kt^T Delta, into the other buffer
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        DeltaOperands<TI> dd;
-        dd.load(s_delta[t], lane);
-        char* nxt = s_state[(n + 1) & 1][t];
-#pragma unroll
-        for (int c = 0; c < NCB; ++c) {
-          state_update<TI>(st[t][c], gc[c], ks[c], kt[c], dd);
-          float x[4] = {st[t][c][0], st[t][c][1], st[t][c][2], st[t][c][3]};
-          const int cb = w * NCB + c;
-          PS::store_half(nxt + (cb / 2) * TS, lane, cb & 1, x);
-        }
-      }
-      load_kt(rn1);
-      block_sync();   // B2
-    }
-    if (p.fin) {
+    load_w(record(cur, 0), cur.j);
+    load_kt(record(cur, 0));
+    for (;;) {
+      const int v0 = kVT * NT * cur.j;   // first value column of tile 0
+      f32x4 st[NT][NCB];
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
         for (int c = 0; c < NCB; ++c) {
           const int c0 = 16 * (w * NCB + c) + 4 * gq;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) p.fin[(slot * K + c0 + i) * V + v0 + 16 * t + m] = st[t][c][i];
+          for (int i = 0; i < 4; ++i)
+            st[t][c][i] = p.init ? p.init[(cur.slot * K + c0 + i) * V + v0 + 16 * t + m] : 0.f;
+          float x[4] = {st[t][c][0], st[t][c][1], st[t][c][2], st[t][c][3]};
+          const int cb = w * NCB + c;
+          PS::store_half(s_state[0][t] + (cb / 2) * TS, lane, cb & 1, x);
         }
       }
+      block_sync();   // B0
+      for (int64_t n = 0; n < cur.n_chunks; ++n) {
+        const char* rn1 = record_after(n);
+        const int jn = n + 1 < cur.n_chunks || !nxt.valid ? cur.j : nxt.j;
+        // Delta = U - W S for tokens 16w..16w+15, tile by tile
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const char* cs = s_state[n & 1][t];
+          PS sf[KB];
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) sf[kb].load(cs + kb * TS, lane);
+          __builtin_amdgcn_sched_barrier(0);   // every operand read issued before the products
+          f32x4 d0 = u[t], d1 = {0, 0, 0, 0};
+#pragma unroll
+          for (int kb = 0; kb < KB; kb += 2) {
+            mma(d0, wn[kb], sf[kb]);
+            if (kb + 1 < KB) mma(d1, wn[kb + 1], sf[kb + 1]);
+          }
+          float x[4] = {d0[0] + d1[0], d0[1] + d1[1], d0[2] + d1[2], d0[3] + d1[3]};
+          delta_store(s_delta[t], w, lane, x);
+        }
+        load_w(rn1, jn);
+        block_sync();   // B1
+        // S <- diag(exp(G_C)) S + Kt^T Delta, into the other buffer
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          DeltaOperands<TI> dd;
+          dd.load(s_delta[t], lane);
+          char* ns = s_state[(n + 1) & 1][t];
+#pragma unroll
+          for (int c = 0; c < NCB; ++c) {
+            state_update<TI>(st[t][c], gc[c], ks[c], kt[c], dd);
+            float x[4] = {st[t][c][0], st[t][c][1], st[t][c][2], st[t][c][3]};
+            const int cb = w * NCB + c;
+            PS::store_half(ns + (cb / 2) * TS, lane, cb & 1, x);
+          }
+        }
+        load_kt(rn1);
+        block_sync();   // B2
+      }
+      if (p.fin) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int c = 0; c < NCB; ++c) {
+            const int c0 = 16 * (w * NCB + c) + 4 * gq;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.fin[(cur.slot * K + c0 + i) * V + v0 + 16 * t + m] = st[t][c][i];
+          }
+        }
+      }
+      if (!nxt.valid) break;
+      advance();
     }
     return;
   }
@@ -428,51 +468,57 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
     for (int kb = 0; kb < 2; ++kb)
       if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PA>(), lane);
   };
-  if (n_chunks > 0) load_q(record(0));
-  block_sync();   // B0
   float* tl = s_out[w];
-  for (int64_t n = 0; n < n_chunks; ++n) {
-    const int64_t t0 = t_begin + n * kChunk;
-    const int len = (int)min<int64_t>(kChunk, seq_len - n * kChunk);
-    const char* rn1 = record(n + 1 < n_chunks ? n + 1 : n);
-    block_sync();   // B1: Delta_n and S_n in LDS
+  load_q(record(cur, 0));
+  for (;;) {
+    const int v0 = kVT * NT * cur.j;
+    block_sync();   // B0
+    for (int64_t n = 0; n < cur.n_chunks; ++n) {
+      const int64_t t0 = cur.t_begin + n * kChunk;
+      const int len = (int)min<int64_t>(kChunk, cur.seq_len - n * kChunk);
+      const char* rn1 = record_after(n);
+      block_sync();   // B1: Delta_n and S_n in LDS
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const char* cur = s_state[n & 1][t];
-      PS sf[KB];
+      for (int t = 0; t < NT; ++t) {
+        const char* cs = s_state[n & 1][t];
+        PS sf[KB];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) sf[kb].load(cur + kb * TS, lane);
-      PD dd[2];
+        for (int kb = 0; kb < KB; ++kb) sf[kb].load(cs + kb * TS, lane);
+        PD dd[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta[t].d + kb * DeltaLds<TI>::TD, lane);
-      __builtin_amdgcn_sched_barrier(0);   // every operand read issued before the products
-      f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
+        for (int kb = 0; kb < 2; ++kb) dd[kb].load(s_delta[t].d + kb * DeltaLds<TI>::TD, lane);
+        __builtin_amdgcn_sched_barrier(0);   // every operand read issued before the products
+        f32x4 o0 = {0, 0, 0, 0}, o1 = {0, 0, 0, 0};
 #pragma unroll
-      for (int kb = 0; kb < KB; kb += 2) {
-        mma(o0, qg[kb], sf[kb]);
-        if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
+        for (int kb = 0; kb < KB; kb += 2) {
+          mma(o0, qg[kb], sf[kb]);
+          if (kb + 1 < KB) mma(o1, qg[kb + 1], sf[kb + 1]);
+        }
+        mma(o1, aq[0], dd[0]);
+        if (w >= 2) mma(o0, aq[1], dd[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tl[(4 * gq + i) * OLD + 16 * t + m] = o0[i] + o1[i];
       }
-      mma(o1, aq[0], dd[0]);
-      if (w >= 2) mma(o0, aq[1], dd[1]);
+      load_q(rn1);
+      // Rows of the tile from LPR lanes each, 4 consecutive columns per lane:
+      // every store instruction writes whole row pieces of the tile's 16 NT
+      // columns (with NT = 2 whole 128-byte lines of fp32 o, streamed; with
+      // one tile a line is shared by two workgroups, and plain stores let L2
+      // join its halves).
+      constexpr int LPR = kVT * NT / 4;   // lanes per row
+      constexpr int RPI = kWave / LPR;    // rows per store instruction
+      const int q = 4 * (lane % LPR);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tl[(4 * gq + i) * OLD + 16 * t + m] = o0[i] + o1[i];
+      for (int r0 = 0; r0 < kChunk / kComputeWaves; r0 += RPI) {
+        const int r = r0 + lane / LPR;
+        const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * OLD + q);
+        if (16 * w + r < len)
+          store_out4<NT == 2>(out, (((int64_t)cur.b * p.T + t0 + 16 * w + r) * H + cur.h) * V + v0 + q, x);
+      }
+      block_sync();   // B2
     }
-    load_q(rn1);
-    // Rows of the tile from LPR lanes each, 4 consecutive columns per lane:
-    // every store instruction writes whole row pieces of the tile's 16 NT
-    // columns (with NT = 2 whole 128-byte lines of fp32 o, streamed; with one
-    // tile a line is shared by two workgroups, and plain stores let L2 join
-    // its halves).
-    constexpr int LPR = kVT * NT / 4;   // lanes per row
-    constexpr int RPI = kWave / LPR;    // rows per store instruction
-    const int q = 4 * (lane % LPR);
-#pragma unroll
-    for (int r0 = 0; r0 < kChunk / kComputeWaves; r0 += RPI) {
-      const int r = r0 + lane / LPR;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(tl + r * OLD + q);
-      if (16 * w + r < len) store_out4<NT == 2>(out, ((b * p.T + t0 + 16 * w + r) * H + h) * V + v0 + q, x);
-    }
-    block_sync();   // B2
+    if (!nxt.valid) break;
+    advance();
   }
 }
 
@@ -480,7 +526,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
 template <class TI, class TO, int K, int V>
 hipError_t launch_recur_t(const CallArgs& a) {
   RecurParams p{a.B, a.T, a.H, a.nc_fixed, a.n_max > 0, a.n_max, a.B * a.H, a.hdr, a.segs,
-                a.records, a.record_bytes, a.init, a.fin, a.o, a.trans};
+                a.records, a.record_bytes, a.init, a.fin, a.o, a.trans, 0};
   const int64_t seq_heads = (a.n_max > 0 ? a.smax : a.B) * a.H;
   if (seq_heads <= 0) return hipSuccess;
   if (a.trans_only) {
@@ -498,14 +544,23 @@ hipError_t launch_recur_t(const CallArgs& a) {
   // every tile: then each chunk's step is as short as it gets.  Beyond, two
   // tiles per workgroup: the step is longer (the matrix work per SIMD
   // doubles) but each record operand is loaded once for both tiles, which
-  // wins once the workgroups take several rounds.
-  const int64_t grid = (seq_heads + 7) / 8 * 8 * (V / kVT);
-  if (grid <= (int64_t)cu_count())
-    hipLaunchKernelGGL((kda_recur_split_kernel<TI, TO, K, V, 1>), dim3((unsigned)grid), dim3(kSplitWaves * kWave), 0,
+  // wins once the workgroups take several rounds; and a grid of one
+  // workgroup per CU (a multiple of 8 NV units) that walks the units, so
+  // that a unit's first records load under the last chunks of the one
+  // before instead of opening every unit.
+  const int64_t tiles = (seq_heads + 7) / 8 * 8 * (V / kVT);
+  const int64_t cus = cu_count();
+  if (tiles <= cus) {
+    p.n_units = tiles;
+    hipLaunchKernelGGL((kda_recur_split_kernel<TI, TO, K, V, 1>), dim3((unsigned)tiles), dim3(kSplitWaves * kWave), 0,
                        a.stream, p);
-  else
-    hipLaunchKernelGGL((kda_recur_split_kernel<TI, TO, K, V, 2>), dim3((unsigned)(grid / 2)),
+  } else {
+    p.n_units = tiles / 2;
+    const int64_t step = 8 * (V / (2 * kVT));
+    const int64_t grid = std::min<int64_t>(p.n_units, std::max<int64_t>(step, cus / step * step));
+    hipLaunchKernelGGL((kda_recur_split_kernel<TI, TO, K, V, 2>), dim3((unsigned)grid),
                        dim3(kSplitWaves * kWave), 0, a.stream, p);
+  }
   return hipGetLastError();
 }
 
