@@ -778,13 +778,12 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
 #pragma unroll
   for (int u = 0; u < VBW; ++u) {
     const int vb = VBW * R + u;
-    PV vf[2];
+    PV vf[2];   // the bf16 values as they are (no conversion)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      float x[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = bits_to_f32(sm.v[(32 * kb + kperm(gq, j)) * S::VP + 16 * vb + m]);
-      vf[kb].set(x);
+      for (int j = 0; j < 8; ++j)
+        vf[kb].v[j] = __builtin_bit_cast(__bf16, sm.v[(32 * kb + kperm(gq, j)) * S::VP + 16 * vb + m]);
     }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb) {
