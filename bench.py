@@ -20,6 +20,7 @@ per-step statistics.  Prints ONE JSON line on stdout.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -414,6 +415,8 @@ def main():
                     help="skip the timing of the same workload with the gate activated in the kernel")
     ap.add_argument("--no-bwd", dest="bwd", action="store_false",
                     help="skip the timing of the backward (kda_chunk_bwd)")
+    ap.add_argument("--no-spare-slots", dest="spare_slots", action="store_false",
+                    help="skip the timing of the packed workload with final states and spare state slots")
     ap.add_argument("--no-cp", dest="cp", action="store_false",
                     help="skip the timing of the workload cut into 2 and 4 context-parallel slices")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -488,6 +491,18 @@ def main():
             parities[w2.name] = oracle_parity(w2, res2["inp"], gpu_outputs(res2))
             log(f"[bench] parity {w2.name} {parities[w2.name]}")
         del res2
+    if args.spare_slots and "bf16_b1_h32_t8192_packed25_l2" in extra_names:
+        # The packed workload with final states out and max_segments above the
+        # 25 segments each row holds: the 7 spare state slots per row are zeroed.
+        ws = dataclasses.replace(WORKLOADS["bf16_b1_h32_t8192_packed25_l2"], name="packed25_l2_spare7",
+                                 final_state=True, max_segments=32)
+        log(f"[bench] {ws.name}")
+        res4 = time_workload(ws, args.steps, args.warmup)
+        s4 = summarize(ws, res4, out_bytes=4)
+        extra["packed_spare_slots"] = {"workload": "bf16_b1_h32_t8192_packed25_l2 with final states and "
+                                                   "max_segments = 32 (25 segments per row)",
+                                       "ms_per_step": round(s4["ms"], 4), "kernels": s4["kernels"]}
+        del res4
     if args.gate_in_kernel and w.safe_gate:
         log(f"[bench] {w.name} with the gate activated in the kernel")
         res3 = time_workload(w, args.steps, args.warmup, gate_in_kernel=True)

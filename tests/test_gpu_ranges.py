@@ -2,8 +2,9 @@
 
 With bf16 inputs the recurrence's state update multiplies Kt, stored as fp16
 scaled by a power of two per 16-key block, with Delta as an fp16 pair scaled
-by a power of two per chunk (from the chunk's largest |Delta|).  These cases
-move those scales through their range: values scaled by 2^+-20, magnitudes
+by 2^4; a 32-token slab whose Delta that pair does not carry falls back to
+Delta's bf16 pair.  These cases move magnitudes through and past that range:
+values scaled by 2^+-20, magnitudes
 that jump by 2^10 from chunk to chunk or fall to zero, 16-token blocks of
 very different magnitude inside one chunk, and keys scaled by 2^+-20 without
 the in-kernel norm (the Kt block scale).  The bar is the usual 2e-2 of rms,
