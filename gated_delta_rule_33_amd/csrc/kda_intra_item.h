@@ -598,6 +598,20 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     frag_wr(sm.KG + r_own * S::XP, 32 * kb, gq, kg);
   }
 
+  // ---- the value rows (16R + l / VPR + 4t, 16-byte piece l % VPR): loaded
+  //      here, so that the solve and -W cover their latency, and stored to
+  //      LDS once KG is dead.  Rows past the chunk's end read the first row
+  //      (no conditional load) and store zeros.
+  constexpr int VPR = V / 8;                  // 16-byte pieces per value row
+  constexpr int VT = 16 * VPR / kWave;        // pieces per lane
+  uint4 vv[VT];
+#pragma unroll
+  for (int t = 0; t < VT; ++t) {
+    const int e = lane + kWave * t, r = f + e / VPR, pc = e % VPR;
+    vv[t] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) +
+                                            ((it.tok0 + (r < len ? r : 0)) * H + h) * V + 8 * pc);
+  }
+
   // ---- T = (I + A)^-1 by 16x16 blocks on the fp32 matrix path (as above)
   const int g4 = 4 * gq;
   auto a_of_A = [&](int R0, int J0, float x[4]) {
@@ -731,19 +745,6 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   tf[3] = t_frag(2, 1); tf[4] = t_frag(3, 0); tf[5] = t_frag(3, 1);
   auto t_idx = [](int rb, int kb) { return rb < 2 ? rb : 2 * rb - 2 + kb; };
 
-  // ---- the value rows (16R + l / VPR + 4t, 16-byte piece l % VPR): loaded
-  //      here, stored to LDS once X is dead
-  constexpr int VPR = V / 8;                  // 16-byte pieces per value row
-  constexpr int VT = 16 * VPR / kWave;        // pieces per lane
-  uint4 vv[VT];
-#pragma unroll
-  for (int t = 0; t < VT; ++t) {
-    const int e = lane + kWave * t, r = f + e / VPR, pc = e % VPR;
-    vv[t] = r < len ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) +
-                                                      ((it.tok0 + r) * H + h) * V + 8 * pc)
-                    : uint4{0, 0, 0, 0};
-  }
-
   // ---- -W = -(T diag(beta)) (K exp(G)): W^T tiles D[c][r] from columns of KG
 #pragma unroll
   for (int u = 0; u < CBW; ++u) {
@@ -772,7 +773,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
 #pragma unroll
   for (int t = 0; t < VT; ++t) {
     const int e = lane + kWave * t, r = f + e / VPR, pc = e % VPR;
-    *reinterpret_cast<uint4*>(sm.v + r * S::VP + 8 * pc) = vv[t];
+    *reinterpret_cast<uint4*>(sm.v + r * S::VP + 8 * pc) = r < len ? vv[t] : uint4{0, 0, 0, 0};
   }
   block_sync();   // B8
 #pragma unroll
