@@ -835,6 +835,16 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 }
 
 
+// The next item of a workgroup that walks items with a constant stride: its
+// index (from LDS, so that it is a scalar) and its position, advanced with
+// borrows instead of the integer divisions of item_pos.
+struct StrideNextItem {
+  const int64_t* s_next;
+  ItemPos pos;
+  __device__ int64_t operator()() const { return uniform_i64(s_next); }
+  __device__ ItemInfo info(const IntraParams& p, int64_t) const { return item_info(p, pos); }
+};
+
 // bf16 inputs: workgroups of four waves, two per CU (about 66 KB of LDS
 // each), each running items n_items - 1 - blockIdx.x, then gridDim.x fewer,
 // and so on (the last items to run are the first chunks, which the
@@ -850,11 +860,14 @@ __global__ __launch_bounds__(256, 2) void kda_intra4_kernel(IntraParams p) {
   if (!KDA_DEBUG_CHECKS && !p.packed && blockIdx.x == 0 && threadIdx.x == 0) p.hdr->flags = 0;
   int64_t item = n_items - 1 - (int64_t)blockIdx.x;
   if (item < 0) return;
-  ItemRows<K> in = load_item_rows<K>(p, item), nx;
+  const ItemPos stride = item_pos(p, gridDim.x);
+  StrideNextItem nxi{&s_next, item_pos(p, item)};
+  ItemRows<K> in = load_item_rows<K>(p, item_info(p, nxi.pos)), nx;
   for (;;) {
     const int64_t next = item - (int64_t)gridDim.x;
     if (threadIdx.x == 0) s_next = next >= 0 ? next : -1;
-    intra4_item<K, V>(p, item, smem_raw, in, [&] { return uniform_i64(&s_next); }, nx);
+    nxi.pos = item_retreat(p, nxi.pos, stride);
+    intra4_item<K, V>(p, item, smem_raw, in, nxi, nx);
     if (next < 0) break;
     block_sync();
     in = nx;

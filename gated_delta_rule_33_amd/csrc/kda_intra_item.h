@@ -201,15 +201,16 @@ template <int K>
 struct ItemRows {
   uint2 q[K / 32][2], k[K / 32][2], g[K / 32][2];
   uint32_t beta, keep;
+  ItemInfo it;   // the item's head, first token and length
 };
 
 template <int K>
-__device__ __forceinline__ ItemRows<K> load_item_rows(const IntraParams& p, int64_t item) {
+__device__ __forceinline__ ItemRows<K> load_item_rows(const IntraParams& p, const ItemInfo& it) {
   constexpr int KB = K / 32;
-  const ItemInfo it = item_info(p, item_pos(p, item));
   const int tid = opaque((int)threadIdx.x) & 255;
   const int m = tid & 15, gq = (tid >> 4) & 3, r_own = 16 * (tid >> 6) + m;
   ItemRows<K> x;
+  x.it = it;
   // Rows past the chunk's end read the chunk's first row (always present),
   // so that no load is conditional.
   const bool row_ok = r_own < it.len;
@@ -234,6 +235,11 @@ __device__ __forceinline__ ItemRows<K> load_item_rows(const IntraParams& p, int6
   return x;
 }
 
+template <int K>
+__device__ __forceinline__ ItemRows<K> load_item_rows(const IntraParams& p, int64_t item) {
+  return load_item_rows<K>(p, item_info(p, item_pos(p, item)));
+}
+
 // An int64 that every lane of the wave holds alike (read from LDS), as a scalar.
 __device__ __forceinline__ int64_t uniform_i64(const int64_t* lds) {
   const int64_t v = *lds;
@@ -254,6 +260,7 @@ __device__ __forceinline__ void widen8(const uint2 a[2], uint32_t keep, float x[
 // No next item (see intra4_item).
 struct NoNextItem {
   __device__ int64_t operator()() const { return -1; }
+  __device__ ItemInfo info(const IntraParams& p, int64_t item) const { return item_info(p, item_pos(p, item)); }
 };
 
 // One (chunk, head) item by the four waves of the calling workgroup, in the
@@ -261,9 +268,10 @@ struct NoNextItem {
 // this lane loaded with load_item_rows.  Once this item's own rows are no
 // longer needed, next_item() (called by every lane, after the item's first
 // barriers, with a result alike in all lanes) names the next item this
-// workgroup will run, and that item's rows are loaded into `next` (nothing
-// for -1), so that their latency overlaps the rest of this item.  The
-// caller separates consecutive items with a barrier.
+// workgroup will run, next_item.info(p, item) its head, tokens and length,
+// and that item's rows are loaded into `next` (nothing for -1), so that their
+// latency overlaps the rest of this item.  The caller separates consecutive
+// items with a barrier.
 template <int K, int V, class NextItem>
 __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, char* smem_raw,
                                             const ItemRows<K>& in, const NextItem& next_item, ItemRows<K>& next) {
@@ -288,7 +296,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   const int m = lane & 15, gq = lane >> 4;
   const int f = 16 * R, r_own = f + m;
   const int64_t H = p.H;
-  const ItemInfo it = item_info(p, item_pos(p, item));
+  const ItemInfo it = in.it;
   const int len = it.len;
   const int64_t h = it.h;
   char* rec = p.records + item * p.record_bytes;
@@ -482,7 +490,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   // this item's larger stores.
   {
     const int64_t nx = next_item();
-    if (nx >= 0) next = load_item_rows<K>(p, nx);
+    if (nx >= 0) next = load_item_rows<K>(p, next_item.info(p, nx));
   }
 
   // ---- A and Aqk for row block R: tiles (I, R) hold D[i][r], I <= R
