@@ -111,7 +111,7 @@ struct XcdQueue {
 template <int K, int V, class NextItem>
 __device__ __forceinline__ void produce(const FusedParams& p, int64_t item, char* lds, const ItemRows<K>& in,
                                         const NextItem& next_item, ItemRows<K>& next) {
-  intra4_item<K, V>(p.ip, item, lds, in, next_item, next);
+  intra4_item<K, V, false>(p.ip, item, lds, in, next_item, next);
   __builtin_amdgcn_s_waitcnt(0);   // this wave's record stores are acknowledged
   block_sync();
   if (threadIdx.x == 0) __hip_atomic_store(p.ready + item, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -270,9 +270,10 @@ struct NoNextItem {
 // barriers, with a result alike in all lanes) names the next item this
 // workgroup will run, next_item.info(p, item) its head, tokens and length,
 // and that item's rows are loaded into `next` (nothing for -1), so that their
-// latency overlaps the rest of this item.  The caller separates consecutive
-// items with a barrier.
-template <int K, int V, class NextItem>
+// latency overlaps the rest of this item.  kEarlyV issues the item's value
+// loads before the solve instead of after it (16 more registers live through
+// the solve).  The caller separates consecutive items with a barrier.
+template <int K, int V, bool kEarlyV = true, class NextItem>
 __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, char* smem_raw,
                                             const ItemRows<K>& in, const NextItem& next_item, ItemRows<K>& next) {
   using S = Intra4Smem<K, V>;
@@ -607,18 +608,21 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
   }
 
   // ---- the value rows (16R + l / VPR + 4t, 16-byte piece l % VPR): loaded
-  //      here, so that the solve and -W cover their latency, and stored to
-  //      LDS once KG is dead.  Rows past the chunk's end read the first row
-  //      (no conditional load) and store zeros.
+  //      here (kEarlyV), so that the solve and -W cover their latency, else
+  //      after the solve, and stored to LDS once KG is dead.  Rows past the
+  //      chunk's end read the first row (no conditional load) and store zeros.
   constexpr int VPR = V / 8;                  // 16-byte pieces per value row
   constexpr int VT = 16 * VPR / kWave;        // pieces per lane
   uint4 vv[VT];
+  auto load_v = [&] {
 #pragma unroll
-  for (int t = 0; t < VT; ++t) {
-    const int e = lane + kWave * t, r = f + e / VPR, pc = e % VPR;
-    vv[t] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) +
-                                            ((it.tok0 + (r < len ? r : 0)) * H + h) * V + 8 * pc);
-  }
+    for (int t = 0; t < VT; ++t) {
+      const int e = lane + kWave * t, r = f + e / VPR, pc = e % VPR;
+      vv[t] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p.v) +
+                                              ((it.tok0 + (r < len ? r : 0)) * H + h) * V + 8 * pc);
+    }
+  };
+  if constexpr (kEarlyV) load_v();
 
   // ---- T = (I + A)^-1 by 16x16 blocks on the fp32 matrix path (as above)
   const int g4 = 4 * gq;
@@ -730,6 +734,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     }
   }
   block_sync();   // B6: T complete
+  if constexpr (!kEarlyV) load_v();
 
   // ---- T diag(beta) fragments (row block rb, token slab kb <= rb / 2):
   //      T[r][i] beta_i, the operand both W and U take
