@@ -8,43 +8,57 @@
 // forward page describes: no chunk straddles a boundary, and the tail rows of
 // a partial chunk are zero.
 //
-// Workgroup 0 builds the tables row by row with block-wide prefix sums; the
-// other workgroups write o = 0 for padding tokens.  Segments past max_segments
-// in a row are not recorded: workgroup 0 raises KDA_FLAG_SEGMENT_OVERFLOW and
-// notes per row where the unrecorded tokens begin and how many state slots
-// were filled; a second, grid-wide kernel then zeroes the outputs of the
-// unrecorded tokens and the final states of the slots no segment reaches.
+// One workgroup builds the tables row by row with block-wide prefix sums.
+// Segments past max_segments in a row are not recorded: it raises
+// KDA_FLAG_SEGMENT_OVERFLOW and notes per row where the unrecorded tokens
+// begin and how many state slots were filled; a second, grid-wide kernel then
+// zeroes the outputs of padding tokens and of unrecorded tokens, and the
+// final states of the slots no segment reaches.
+// While max_segments fits kLdsSegs, the bounds of a row's segments stay in
+// LDS between the passes (each pass otherwise reads back from global memory
+// what the one before wrote).
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
 
 constexpr int kPrepThreads = 1024;
-constexpr int kPrepTok = 8;   // tokens per thread in the segment scan
+constexpr int kPrepTok = 8;     // tokens per thread in the segment scan
+constexpr int kLdsSegs = 2048;  // segments per row whose bounds LDS holds
 
-// Inclusive prefix sum over the 1024 threads of the block; *total gets the sum.
+// Inclusive prefix sum over a wave (DPP: shifts within each 16-lane row,
+// then the row totals carried on by two row broadcasts).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_add(int x) {
+  return x + __builtin_amdgcn_update_dpp(0, x, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int wave_scan(int x) {
+  x = dpp_add<0x111, 0xF>(x);   // row_shr:1
+  x = dpp_add<0x112, 0xF>(x);   // row_shr:2
+  x = dpp_add<0x114, 0xF>(x);   // row_shr:4
+  x = dpp_add<0x118, 0xF>(x);   // row_shr:8
+  x = dpp_add<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  x = dpp_add<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+// Inclusive prefix sum over the 1024 threads of the block; *total gets the
+// sum.  Each wave scans its lanes, then wave 0 scans the 16 wave sums.
 __device__ int block_scan(int x, int* wave_sums, int* total) {
+  constexpr int NW = kPrepThreads / 64;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  int v = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(v, d);
-    if (lane >= d) v += y;
-  }
+  const int v = wave_scan(x);
   if (lane == 63) wave_sums[wv] = v;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int i = 0; i < kPrepThreads / 64; ++i) {
-      const int s = wave_sums[i];
-      wave_sums[i] = run;
-      run += s;
-    }
-    wave_sums[kPrepThreads / 64] = run;
+  if (wv == 0) {
+    const int ws = lane < NW ? wave_sums[lane] : 0;
+    const int u = wave_scan(ws);
+    if (lane < NW) wave_sums[lane] = u - ws;   // exclusive
+    if (lane == NW - 1) wave_sums[NW] = u;    // total
   }
   __syncthreads();
   const int res = v + wave_sums[wv];
-  *total = wave_sums[kPrepThreads / 64];
+  *total = wave_sums[NW];
   __syncthreads();
   return res;
 }
@@ -66,22 +80,13 @@ struct PrepParams {
   float* fin;
 };
 
-template <class TO>
 __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
-  const int64_t T = p.T, HV = p.H * p.V;
-  TO* o = static_cast<TO*>(p.o);
-  if (blockIdx.x > 0) {
-    // Padding tokens: one wave per token (nothing to do without an output).
-    if (o == nullptr) return;
-    const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)(blockIdx.x - 1) * (kPrepThreads / 64) + (threadIdx.x >> 6);
-    const int64_t n_waves = (int64_t)(gridDim.x - 1) * (kPrepThreads / 64);
-    for (int64_t tok = wave; tok < p.B * T; tok += n_waves)
-      if (p.ids[tok] == 0) zero_token(o, tok, HV, lane, 64);
-    return;
-  }
-
+  const int64_t T = p.T;
   __shared__ int wave_sums[kPrepThreads / 64 + 1];
+  __shared__ int l_t0[kLdsSegs], l_end[kLdsSegs];   // per recorded segment of the row
+  const bool lds = p.n_max <= kLdsSegs;
+  // 16-byte loads of ids where every row starts 16-byte aligned
+  const bool vec = ((reinterpret_cast<uintptr_t>(p.ids) | (uintptr_t)(T * 4)) & 15) == 0;
   const int tid = threadIdx.x;
   int seg_base = 0, chunk_base = 0;
   uint32_t flags = 0;
@@ -94,34 +99,57 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
     int row_segs = 0;
     for (int64_t t0 = 0; t0 < T; t0 += (int64_t)kPrepThreads * kPrepTok) {
       const int64_t tb = t0 + (int64_t)tid * kPrepTok;
-      int ids[kPrepTok + 2];   // tokens tb - 1 .. tb + kPrepTok (0 outside the row)
+      // tokens tb - 1 .. tb + kPrepTok (0 outside the row): every load is
+      // issued, at a clamped index, and masked after
+      int ids[kPrepTok + 2];
+      if (vec && tb + kPrepTok <= T) {
+        // two 16-byte loads: each wave's load instruction covers 1 KB of ids
+        const int4 a = *reinterpret_cast<const int4*>(row + tb);
+        const int4 c = *reinterpret_cast<const int4*>(row + tb + 4);
+        ids[1] = a.x; ids[2] = a.y; ids[3] = a.z; ids[4] = a.w;
+        ids[5] = c.x; ids[6] = c.y; ids[7] = c.z; ids[8] = c.w;
+        ids[0] = row[tb > 0 ? tb - 1 : 0];
+        ids[kPrepTok + 1] = row[tb + kPrepTok < T ? tb + kPrepTok : T - 1];
+      } else {
+#pragma unroll
+        for (int i = 0; i < kPrepTok + 2; ++i) {
+          const int64_t t = tb - 1 + i;
+          ids[i] = row[t < 0 ? 0 : (t < T ? t : T - 1)];
+        }
+      }
 #pragma unroll
       for (int i = 0; i < kPrepTok + 2; ++i) {
         const int64_t t = tb - 1 + i;
-        ids[i] = (t >= 0 && t < T) ? row[t] : 0;
+        ids[i] = (t >= 0 && t < T) ? ids[i] : 0;
       }
-      int starts = 0;
+      // bit i - 1: token tb + i - 1 starts (smask) or ends (emask) a segment
+      uint32_t smask = 0, emask = 0;
 #pragma unroll
       for (int i = 1; i <= kPrepTok; ++i) {
         const int64_t t = tb + i - 1;
-        starts += (t < T && ids[i] != 0 && (t == 0 || ids[i] != ids[i - 1])) ? 1 : 0;
+        const int id = ids[i];
+        const bool in = t < T && id != 0;
+        smask |= (in && (t == 0 || id != ids[i - 1]) ? 1u : 0u) << (i - 1);
+        emask |= (in && (t == T - 1 || ids[i + 1] != id) ? 1u : 0u) << (i - 1);
       }
+      const int starts = __builtin_popcount(smask);
       int total;
       const int incl = block_scan(starts, wave_sums, &total);
-      int seen = row_segs + incl - starts;   // segments started before this thread's first token
-#pragma unroll
-      for (int i = 1; i <= kPrepTok; ++i) {
-        const int64_t t = tb + i - 1;
-        if (t >= T) break;
-        const int id = ids[i];
-        const bool start = id != 0 && (t == 0 || id != ids[i - 1]);
-        const bool end = id != 0 && (t == T - 1 || ids[i + 1] != id);
-        seen += start ? 1 : 0;
-        const int local = seen - 1;   // the segment token t belongs to
-        if (id != 0 && local < p.n_max) {
+      const int seen = row_segs + incl - starts;   // segments started before this thread's first token
+      // only the tokens that start or end a segment do anything
+      for (uint32_t ev = smask | emask; ev != 0; ev &= ev - 1) {
+        const int bit = __builtin_ctz(ev);
+        const int local = seen + __builtin_popcount(smask & ((2u << bit) - 1)) - 1;   // its segment
+        if (local >= p.n_max) break;
+        const int t = (int)(tb + bit);
+        const bool start = (smask >> bit) & 1, end = (emask >> bit) & 1;
+        if (lds) {
+          if (start) l_t0[local] = t;
+          if (end) l_end[local] = t + 1;
+        } else {
           SegEntry* se = p.segs + seg_base + local;
-          if (start) { se->b = (int)b; se->t0 = (int)t; se->local = local; }
-          if (end) se->len = (int)(t + 1);   // end for now; turned into a length below
+          if (start) se->t0 = t;
+          if (end) se->len = t + 1;   // end for now; turned into a length below
         }
       }
       row_segs += total;
@@ -129,44 +157,55 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
     __syncthreads();
     const int nrec = min(row_segs, p.n_max);
     if (row_segs > p.n_max) flags |= KDA_FLAG_SEGMENT_OVERFLOW;
-    // Pass 2: lengths, chunk counts and first chunk of each recorded segment.
+    // Pass 2: lengths, chunk counts and first chunk of each recorded
+    // segment, and its entry; pass 3: its chunk entries (one thread per
+    // segment, right after).
+    int last_end = 0;   // end of the row's last recorded segment (thread 0)
     for (int s0 = 0; s0 < nrec; s0 += kPrepThreads) {
       const int s = s0 + tid;
-      int nch = 0;
+      int st = 0, len = 0, nch = 0;
       if (s < nrec) {
-        SegEntry* se = p.segs + seg_base + s;
-        se->len = se->len - se->t0;
-        nch = (se->len + kChunk - 1) / kChunk;
-        se->n_chunks = nch;
+        if (lds) {
+          st = l_t0[s];
+          len = l_end[s] - st;
+        } else {
+          st = p.segs[seg_base + s].t0;
+          len = p.segs[seg_base + s].len - st;
+        }
+        nch = (len + kChunk - 1) / kChunk;
       }
       int total;
       const int incl = block_scan(nch, wave_sums, &total);
-      if (s < nrec) p.segs[seg_base + s].chunk_begin = chunk_base + incl - nch;
+      if (s < nrec) {
+        SegEntry se;
+        se.b = (int)b;
+        se.t0 = st;
+        se.len = len;
+        se.local = s;
+        se.chunk_begin = chunk_base + incl - nch;
+        se.n_chunks = nch;
+        se.pad0 = se.pad1 = 0;
+        p.segs[seg_base + s] = se;
+        for (int c = 0; c < nch; ++c) {
+          ChunkEntry ce;
+          ce.b = (int)b;
+          ce.t0 = st + c * kChunk;
+          ce.len = min(kChunk, len - c * kChunk);
+          ce.seg = seg_base + s;
+          p.chunks[se.chunk_begin + c] = ce;
+        }
+        if (s == nrec - 1) wave_sums[kPrepThreads / 64] = st + len;
+      }
       chunk_base += total;
     }
     __syncthreads();
-    // Pass 3: chunk entries (one thread per recorded segment).
-    for (int s = tid; s < nrec; s += kPrepThreads) {
-      const SegEntry se = p.segs[seg_base + s];
-      for (int c = 0; c < se.n_chunks; ++c) {
-        ChunkEntry ce;
-        ce.b = (int)b;
-        ce.t0 = se.t0 + c * kChunk;
-        ce.len = min(kChunk, se.len - c * kChunk);
-        ce.seg = seg_base + s;
-        p.chunks[se.chunk_begin + c] = ce;
-      }
-    }
+    if (nrec > 0) last_end = wave_sums[kPrepThreads / 64];
     // Where the row's unrecorded tokens begin (T when every segment is
     // recorded) and how many state slots its segments fill.
     if (tid == 0) {
       RowInfo ri;
       ri.n_recorded = nrec;
-      ri.tail_t0 = (int)T;
-      if (row_segs > p.n_max) {
-        const SegEntry last = p.segs[seg_base + nrec - 1];
-        ri.tail_t0 = last.t0 + last.len;
-      }
+      ri.tail_t0 = row_segs > p.n_max ? last_end : (int)T;
       p.rows[b] = ri;
     }
     seg_base += nrec;
@@ -179,10 +218,10 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
   }
 }
 
-// Grid-wide zeroing after the tables: the outputs of tokens of unrecorded
-// segments (a row with more than max_segments segments) and the final states
-// of the slots no segment of a row reaches.  One wave per token or per
-// (row, slot, head) state block.
+// Grid-wide zeroing after the tables: the outputs of padding tokens and of
+// tokens of unrecorded segments (a row with more than max_segments
+// segments), and the final states of the slots no segment of a row reaches.
+// One wave per token or per (row, slot, head) state block.
 constexpr int kTailThreads = 256;
 
 template <class TO>
@@ -195,7 +234,8 @@ __global__ __launch_bounds__(kTailThreads) void kda_prep_tail_kernel(PrepParams 
   if (o != nullptr) {
     for (int64_t tok = wave; tok < p.B * p.T; tok += n_waves) {
       const int64_t b = tok / p.T, t = tok % p.T;
-      if (t >= p.rows[b].tail_t0 && p.ids[tok] != 0) zero_token(o, tok, HV, lane, 64);
+      const int id = p.ids[tok];
+      if (id == 0 || t >= p.rows[b].tail_t0) zero_token(o, tok, HV, lane, 64);
     }
   }
   if (p.fin != nullptr) {
@@ -217,16 +257,10 @@ __global__ void kda_fill_zero_kernel(float* x, int64_t n) {
 
 hipError_t launch_prep(const CallArgs& a) {
   PrepParams p{a.seg_ids, a.B, a.T, a.H, a.K, a.V, a.n_max, a.hdr, a.segs, a.chunks, a.rows, a.o, a.fin};
-  const int64_t tokens = a.B * a.T;
-  const int zero_groups = (int)std::min<int64_t>(256, (tokens + 15) / 16);
-  const dim3 grid(1 + zero_groups);
-  if (a.out == OutType::F32)
-    hipLaunchKernelGGL(kda_prep_kernel<float>, grid, dim3(kPrepThreads), 0, a.stream, p);
-  else
-    hipLaunchKernelGGL(kda_prep_kernel<uint16_t>, grid, dim3(kPrepThreads), 0, a.stream, p);
+  hipLaunchKernelGGL(kda_prep_kernel, dim3(1), dim3(kPrepThreads), 0, a.stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (a.o == nullptr && a.fin == nullptr)) return e;
-  const int64_t waves = std::max<int64_t>(tokens, a.B * a.n_max * a.H);
+  const int64_t waves = std::max<int64_t>(a.B * a.T, a.B * a.n_max * a.H);
   const unsigned tail_groups = (unsigned)std::min<int64_t>(1024, (waves + 3) / 4);
   if (a.out == OutType::F32)
     hipLaunchKernelGGL(kda_prep_tail_kernel<float>, dim3(tail_groups), dim3(kTailThreads), 0, a.stream, p);
