@@ -443,7 +443,8 @@ struct TableHeader {
   int32_t n_segments;   // recorded segments (all rows)
   int32_t n_chunks;     // chunks of recorded segments
   uint32_t flags;       // KDA_FLAG_* bits
-  int32_t pad[61];      // keeps the header 256 bytes
+  uint32_t tail_work;   // packed input: some output or final state needs zeroing after the tables
+  int32_t pad[60];      // keeps the header 256 bytes
 };
 
 }  // namespace kda

@@ -90,6 +90,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
   const int tid = threadIdx.x;
   int seg_base = 0, chunk_base = 0;
   uint32_t flags = 0;
+  bool tail_work = false;   // padding, unrecorded segments or unreached state slots
   for (int64_t b = 0; b < p.B; ++b) {
     const int32_t* row = p.ids + b * T;
     // Pass 1: segment starts and ends.  Each thread takes kPrepTok
@@ -124,14 +125,17 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
       }
       // bit i - 1: token tb + i - 1 starts (smask) or ends (emask) a segment
       uint32_t smask = 0, emask = 0;
+      bool padding = false;
 #pragma unroll
       for (int i = 1; i <= kPrepTok; ++i) {
         const int64_t t = tb + i - 1;
         const int id = ids[i];
         const bool in = t < T && id != 0;
+        padding = padding || (t < T && id == 0);
         smask |= (in && (t == 0 || id != ids[i - 1]) ? 1u : 0u) << (i - 1);
         emask |= (in && (t == T - 1 || ids[i + 1] != id) ? 1u : 0u) << (i - 1);
       }
+      if (__syncthreads_or(padding ? 1 : 0)) tail_work = true;
       const int starts = __builtin_popcount(smask);
       int total;
       const int incl = block_scan(starts, wave_sums, &total);
@@ -157,6 +161,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
     __syncthreads();
     const int nrec = min(row_segs, p.n_max);
     if (row_segs > p.n_max) flags |= KDA_FLAG_SEGMENT_OVERFLOW;
+    if (row_segs > p.n_max || (p.fin != nullptr && row_segs < p.n_max)) tail_work = true;
     // Pass 2: lengths, chunk counts and first chunk of each recorded
     // segment, and its entry; pass 3: its chunk entries (one thread per
     // segment, right after).
@@ -215,6 +220,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
     p.hdr->n_segments = seg_base;
     p.hdr->n_chunks = chunk_base;
     p.hdr->flags = flags;
+    p.hdr->tail_work = tail_work ? 1u : 0u;
   }
 }
 
@@ -229,6 +235,7 @@ __global__ __launch_bounds__(kTailThreads) void kda_prep_tail_kernel(PrepParams 
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kTailThreads / 64) + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * (kTailThreads / 64);
+  if (p.hdr->tail_work == 0) return;   // nothing to zero: no padding, every segment recorded, every slot reached
   const int64_t HV = p.H * p.V, KV = p.K * p.V;
   TO* o = static_cast<TO*>(p.o);
   if (o != nullptr) {
