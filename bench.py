@@ -417,6 +417,8 @@ def main():
                     help="skip the timing of the backward (kda_chunk_bwd)")
     ap.add_argument("--no-spare-slots", dest="spare_slots", action="store_false",
                     help="skip the timing of the packed workload with final states and spare state slots")
+    ap.add_argument("--no-fused", dest="fused", action="store_false",
+                    help="skip the timing of the opt-in fused forward on the headline workload")
     ap.add_argument("--no-cp", dest="cp", action="store_false",
                     help="skip the timing of the workload cut into 2 and 4 context-parallel slices")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -512,6 +514,24 @@ def main():
                                    "note": "raw N(0,1) gate, A_log = 0, dt_bias = 0, safe gate at -5: "
                                            "the same decay distribution, activated in the kernel"}
         del res3
+    if args.fused:
+        # The opt-in fused forward: one persistent kernel, records handed from
+        # producer to recurrence workgroups through L2 instead of HBM.
+        from gated_delta_rule_33_amd import kda as kda_mod
+        log(f"[bench] {w.name} with the fused forward")
+        kda_mod.set_fused_forward(True)
+        try:
+            res5 = time_workload(w, args.steps, args.warmup)
+        finally:
+            kda_mod.set_fused_forward(False)
+        s5 = summarize(w, res5, out_bytes=4)
+        extra["fused_forward"] = {"workload": w.name, "ms_per_step": round(s5["ms"], 4),
+                                  "tokens_per_s": round(s5["tokens_per_s"], 1), "kernels": s5["kernels"],
+                                  "traffic": measured_traffic("kda_fused", w.name)}
+        if not args.no_parity:
+            parities["fused_forward"] = oracle_parity(w, res5["inp"], gpu_outputs(res5))
+            log(f"[bench] parity fused forward {parities['fused_forward']}")
+        del res5
     if args.bwd:
         for wb in [w] + [WORKLOADS[n] for n in extra_names if WORKLOADS[n].T >= 8192]:
             log(f"[bench] backward of {wb.name}")
