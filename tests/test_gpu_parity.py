@@ -191,6 +191,24 @@ def test_packed_segments(case, with_state):
     assert np.all(o[seg == 0] == 0.0)
 
 
+@pytest.mark.parametrize("case", ["two_rows_padding", "many_short"])
+def test_packed_tables_past_lds_capacity(case):
+    """max_segments above what the table workgroup keeps in LDS (2048 per
+    row): the segment bounds pass between its passes through global memory."""
+    rows, T = PACKED[case]
+    rows = [[n for n in r if n > 0] for r in rows]
+    seg = segment_ids_from_lengths(rows, T)
+    if case == "two_rows_padding":
+        seg[0, 30:34] = 0
+    w = Workload(case + "_wide", "bf16", len(rows), T, 2, 128, 128, seed=23, max_segments=2100)
+    inp = make_inputs(w, segment_ids=seg)
+    _say(f"[parity] packed {case} with max_segments 2100")
+    o, _ = run_gpu(inp, w)
+    o_ref, _ = oracle_ref(inp, w)
+    check(f"{case} wide o", o, o_ref, TOL_BF16)
+    assert np.all(o[seg == 0] == 0.0)
+
+
 def test_segment_ids_all_ones_equals_fixed():
     w = Workload("ones", "bf16", 2, 190, 2, 128, 128, seed=31, final_state=True, max_segments=1)
     inp = make_inputs(w)
