@@ -379,12 +379,17 @@ template <> struct Prec<float> {
 //   Wn  : -W, rows = token r (4 blocks), k = key channel c     [4][K/32] tiles
 //   Kt  : k * exp(G_C - G) transposed, rows = c, k = token r   [K/16][2] tiles
 //   Qg  : scale * q * exp(G), rows = r, k = c                   [4][K/32] tiles
-//   Aqk : scale * A_qk (lower incl. diagonal), rows = r, k = i  [4][2] tiles
+//   Aqk : scale * A_qk (lower incl. diagonal), rows = r, k = i  6 tiles (aqk_tile)
 //   U   : T diag(beta) V in output-tile layout, rows = r, cols = value
 //         channel, [4][V/16] tiles of 64 lanes x 4 fp32
 //   Gc  : exp(G_C), K fp32 (decay of the whole chunk)
 //   Ks  : (bf16 inputs) 2^-s of each 16-key block of Kt, K/16 fp32: the
 //         stored block is Kt 2^s
+// Aqk (lower triangular) as operand tiles (row block rb, 32-token slab kb):
+// slab 1 of row blocks 0 and 1 is all zero and not stored, so tile (rb, kb)
+// is the record's tile number aqk_tile(rb, kb), 0..5, for kb <= rb / 2.
+__host__ __device__ constexpr int aqk_tile(int rb, int kb) { return rb < 2 ? rb : 2 * rb - 2 + kb; }
+
 template <class TI, int K, int V>
 struct RecordLayout {
   using P = Prec<TI>;
@@ -395,7 +400,7 @@ struct RecordLayout {
   static constexpr int64_t kQg = kKt + kKtBytes;
   static constexpr int64_t kQgBytes = 4 * (K / 32) * tile_bytes<typename P::Qg>();
   static constexpr int64_t kAqk = kQg + kQgBytes;
-  static constexpr int64_t kAqkBytes = 4 * 2 * tile_bytes<typename P::Aq>();
+  static constexpr int64_t kAqkBytes = 6 * tile_bytes<typename P::Aq>();   // aqk_tile: no all-zero tiles
   static constexpr int64_t kU = kAqk + kAqkBytes;
   static constexpr int64_t kUBytes = 4 * (V / 16) * kWave * 16;
   static constexpr int64_t kGc = kU + kUBytes;

@@ -205,7 +205,7 @@ __device__ __forceinline__ int64_t recur_lane(const FusedParams& p, int64_t sh, 
     for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PA>(), lane);
+      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)aqk_tile(w, kb) * tile_bytes<PA>(), lane);
   };
 
   // State slice: lane (column v0 + m, rows 16cb + 4gq + i) of its blocks,

@@ -562,6 +562,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+          if (kb > R / 2) continue;   // all zero: not stored
           float x[8];
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
@@ -570,7 +571,7 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
           }
           PAq af;
           af.set(x);
-          af.store(rec + L::kAqk + (int64_t)(R * 2 + kb) * tile_bytes<PAq>(), lane);
+          af.store(rec + L::kAqk + (int64_t)aqk_tile(R, kb) * tile_bytes<PAq>(), lane);
         }
       }
     }

@@ -539,6 +539,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
+      if (kb > R / 2) continue;   // all zero: not stored
       float x[8];
 #pragma unroll
       for (int ii = 0; ii < 4; ++ii) {
@@ -547,7 +548,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
       }
       PAq af;
       af.set(x);
-      af.store(rec + L::kAqk + (int64_t)(R * 2 + kb) * tile_bytes<PAq>(), lane);
+      af.store(rec + L::kAqk + (int64_t)aqk_tile(R, kb) * tile_bytes<PAq>(), lane);
     }
   }
   // Kt = (k exp(G_C - G))^T tiles [c-block][token slab] from columns of X:

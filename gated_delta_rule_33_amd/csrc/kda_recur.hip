@@ -466,7 +466,7 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
     for (int kb = 0; kb < KB; ++kb) qg[kb].load(r + L::kQg + (int64_t)(w * KB + kb) * tile_bytes<PQ>(), lane);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)(2 * w + kb) * tile_bytes<PA>(), lane);
+      if (kb <= w / 2) aq[kb].load(r + L::kAqk + (int64_t)aqk_tile(w, kb) * tile_bytes<PA>(), lane);
   };
   float* tl = s_out[w];
   load_q(record(cur, 0));
