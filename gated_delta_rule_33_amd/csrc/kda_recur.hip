@@ -124,16 +124,16 @@ __global__ __launch_bounds__((kComputeWaves + 1) * kWave) void kda_recur_trans_k
   auto record = [&](int64_t n) { return p.records + ((first_chunk + n) * H + h) * p.record_bytes; };
 
   // ---- L2 prefetch wave: this workgroup's 1/NV share of the record's Wn and
-  // Kt (every 64-byte segment once), one chunk ahead.
+  // Kt (one load per 128-byte L2 line), one chunk ahead.
   if (wave == kPrefetchWave) {
-    constexpr int SEGS = (int)(L::kQg / 64);
+    constexpr int SEGS = (int)(L::kQg / 128);   // L2 lines of 128 bytes
     constexpr int SHARE = (SEGS + NV - 1) / NV;
     auto prefetch = [&](int64_t n) {
       const char* r = record(n);
 #pragma unroll
       for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
         const int e = i * kWave + lane, seg = j * SHARE + e;
-        if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
+        if (e < SHARE && seg < SEGS) dma16(s_sink, r + 128 * (int64_t)seg);
       }
     };
     block_sync();
@@ -330,15 +330,15 @@ __global__ __launch_bounds__(kSplitWaves * kWave) void kda_recur_split_kernel(Re
   };
 
   if (prefetcher) {
-    // ---- every 64-byte segment of the workgroup's 1/NV share of a record,
-    //      two records ahead in the workgroup's sequence of records
+    // ---- one 16-byte load in every 128-byte L2 line of the workgroup's
+    //      1/NV share of a record, two records ahead in its sequence of records
     auto prefetch = [&](const char* r, int jj) {
-      constexpr int SEGS = (int)(L::kBytes / 64);
+      constexpr int SEGS = (int)(L::kBytes / 128);   // L2 lines of 128 bytes
       constexpr int SHARE = (SEGS + NV - 1) / NV;
 #pragma unroll
       for (int i = 0; i < (SHARE + kWave - 1) / kWave; ++i) {
         const int e = i * kWave + lane, seg = jj * SHARE + e;
-        if (e < SHARE && seg < SEGS) dma16(s_sink, r + 64 * (int64_t)seg);
+        if (e < SHARE && seg < SEGS) dma16(s_sink, r + 128 * (int64_t)seg);
       }
     };
     if (cur.n_chunks > 1) prefetch(record(cur, 1), cur.j);
