@@ -3,9 +3,13 @@
 // formulation" (page "feat(kda): integrate KDA attention with tokamax backend
 // and CP support", Implementation Details) in one persistent kernel, so that
 // the per-(chunk, head) records pass from their producer to their consumers
-// through the L2 of one XCD instead of through HBM.  The pages' own answer to
+// on one XCD, through its L2 while they stay there.  The pages' own answer to
 // the same problem is a fused forward ("Add packed KDA forward megakernel",
-// Summary); this is its MI355X form.
+// Summary); this is its MI355X form.  Producers are not held back to the
+// recurrence's pace, and an XCD's L2 holds about ten chunks of its heads'
+// records, so most records are still written back to HBM and read again;
+// with one producer workgroup per CU beside a lane the kernel is bound by
+// producing and stays behind the two-kernel schedule.
 //
 // Layout of the work.  Two workgroups of four waves run on every compute unit
 // (about 66 KB of LDS each).  The first to arrive on a CU runs recurrence

@@ -435,12 +435,14 @@ void kda_set_launch_observer(kda_launch_observer_t fn, void* user);
  * bf16 inputs, no segment_ids, no transition output and K = V = 128 on a
  * gfx950 device of 8 XCDs run both as one persistent kernel ("kda_fused",
  * the fused forward of the page "Add packed KDA forward megakernel",
- * Summary) whose records pass through L2; other calls keep the two kernels.
- * Both compute the same function of the inputs (up to fp32 rounding: the
- * kernels are compiled apart); the setting only selects the schedule.
- * Default 0: on MI355X the two kernels are the faster schedule at the sizes
- * measured so far.  Process-wide; set it while no other thread is inside a
- * forward call.
+ * Summary), which hands each record from the workgroup that produces it to
+ * the recurrence workgroups of the same XCD (the records still go through
+ * HBM when producers run far ahead of the recurrence, as they do); other
+ * calls keep the two kernels.  Both compute the same function of the inputs
+ * (up to fp32 rounding: the kernels are compiled apart); the setting only
+ * selects the schedule.  Default 0: on MI355X the two kernels are the faster
+ * schedule at the sizes measured so far.  Process-wide; set it while no
+ * other thread is inside a forward call.
  */
 void kda_set_fused_forward(int enable);
 
