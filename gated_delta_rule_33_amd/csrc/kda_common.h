@@ -449,7 +449,8 @@ struct TableHeader {
   int32_t n_chunks;     // chunks of recorded segments
   uint32_t flags;       // KDA_FLAG_* bits
   uint32_t tail_work;   // packed input: some output or final state needs zeroing after the tables
-  int32_t pad[60];      // keeps the header 256 bytes
+  uint32_t item_ticket; // intra-chunk items handed out past each workgroup's first (zeroed before the kernel)
+  int32_t pad[59];      // keeps the header 256 bytes
 };
 
 }  // namespace kda

@@ -836,21 +836,36 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 }
 
 
-// The next item of a workgroup that walks items with a constant stride: its
-// index (from LDS, so that it is a scalar) and its position, advanced with
-// borrows instead of the integer divisions of item_pos.
-struct StrideNextItem {
-  const int64_t* s_next;
-  ItemPos pos;
+// The next item of a workgroup that takes its items from a counter: thread 0
+// draws a ticket when the item starts (the atomic's latency passes under the
+// running sum); tickets past the n_items - gridDim.x items left after every
+// workgroup's first mean none.  Items are handed out from the last down, as
+// with a fixed stride, so the first chunks still run last.
+struct TicketNextItem {
+  int64_t* s_next;
+  TableHeader* hdr;
+  int64_t n_items, grid;
+  uint32_t ticket;   // thread 0's
+  __device__ void draw() {
+    if (threadIdx.x == 0) ticket = atomicAdd(&hdr->item_ticket, 1u);
+  }
+  __device__ void publish() const {
+    if (threadIdx.x == 0) {
+      const int64_t t = grid + (int64_t)ticket;
+      *s_next = t < n_items ? n_items - 1 - t : -1;
+    }
+  }
   __device__ int64_t operator()() const { return uniform_i64(s_next); }
-  __device__ ItemInfo info(const IntraParams& p, int64_t) const { return item_info(p, pos); }
+  __device__ ItemInfo info(const IntraParams& p, int64_t item) const { return item_info(p, item_pos(p, item)); }
 };
 
 // bf16 inputs: workgroups of four waves, two per CU (about 66 KB of LDS
-// each), each running items n_items - 1 - blockIdx.x, then gridDim.x fewer,
-// and so on (the last items to run are the first chunks, which the
-// recurrence reads first).  A workgroup loads the next item's rows while it
-// finishes the current one.
+// each), each running item n_items - 1 - blockIdx.x first and then the
+// items its tickets name (the counter is zeroed before the launch), so that
+// workgroups that run faster take more items: the per-item time varies
+// between compute units, and a fixed share of eight items per workgroup
+// left the last workgroups finishing 40 µs after the first.  A workgroup
+// loads the next item's rows while it finishes the current one.
 template <int K, int V>
 __global__ __launch_bounds__(256, 2) void kda_intra4_kernel(IntraParams p) {
   extern __shared__ __align__(16) char smem_raw[];
@@ -861,14 +876,12 @@ __global__ __launch_bounds__(256, 2) void kda_intra4_kernel(IntraParams p) {
   if (!KDA_DEBUG_CHECKS && !p.packed && blockIdx.x == 0 && threadIdx.x == 0) p.hdr->flags = 0;
   int64_t item = n_items - 1 - (int64_t)blockIdx.x;
   if (item < 0) return;
-  const ItemPos stride = item_pos(p, gridDim.x);
-  StrideNextItem nxi{&s_next, item_pos(p, item)};
-  ItemRows<K> in = load_item_rows<K>(p, item_info(p, nxi.pos)), nx;
+  TicketNextItem nxi{&s_next, p.hdr, n_items, (int64_t)gridDim.x, 0u};
+  ItemRows<K> in = load_item_rows<K>(p, item), nx;
   for (;;) {
-    const int64_t next = item - (int64_t)gridDim.x;
-    if (threadIdx.x == 0) s_next = next >= 0 ? next : -1;
-    nxi.pos = item_retreat(p, nxi.pos, stride);
+    nxi.draw();
     intra4_item<K, V>(p, item, smem_raw, in, nxi, nx);
+    const int64_t next = uniform_i64(&s_next);
     if (next < 0) break;
     block_sync();
     in = nx;
@@ -888,6 +901,10 @@ hipError_t launch_intra4_t(const CallArgs& a) {
   if (e != hipSuccess) return e;
   const int64_t items = (a.n_max > 0 ? a.cmax : a.B * a.nc_fixed) * a.H;
   if (items <= 0) return hipSuccess;
+  if (a.n_max == 0) {   // with segment ids the table kernel zeroes the item counter
+    e = launch_fill_zero(reinterpret_cast<float*>(&a.hdr->item_ticket), 1, a.stream);
+    if (e != hipSuccess) return e;
+  }
   const unsigned grid = (unsigned)std::min<int64_t>(items, 2 * (int64_t)cu_count());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, a.stream, p);
   return hipGetLastError();

@@ -259,6 +259,7 @@ __device__ __forceinline__ void widen8(const uint2 a[2], uint32_t keep, float x[
 
 // No next item (see intra4_item).
 struct NoNextItem {
+  __device__ void publish() const {}
   __device__ int64_t operator()() const { return -1; }
   __device__ ItemInfo info(const IntraParams& p, int64_t item) const { return item_info(p, item_pos(p, item)); }
 };
@@ -269,7 +270,9 @@ struct NoNextItem {
 // longer needed, next_item() (called by every lane, after the item's first
 // barriers, with a result alike in all lanes) names the next item this
 // workgroup will run, next_item.info(p, item) its head, tokens and length,
-// and that item's rows are loaded into `next` (nothing for -1), so that their
+// (next_item.publish(), called by every lane before the item's second
+// barrier, lets thread 0 put that answer in LDS), and that item's rows are
+// loaded into `next` (nothing for -1), so that their
 // latency overlaps the rest of this item.  kEarlyV issues the item's value
 // loads before the solve instead of after it (16 more registers live through
 // the solve).  The caller separates consecutive items with a barrier.
@@ -368,6 +371,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     if (m == 0) frag_wr(sm.Gf[R], 32 * kb, gq, gx[kb]);
     if (m == 15) frag_wr(sm.Gl[R], 32 * kb, gq, gx[kb]);
   }
+  next_item.publish();
   block_sync();   // B1: first and last rows of every block
 
   // ---- per-wave factor rows (read back only by this wave until B2):

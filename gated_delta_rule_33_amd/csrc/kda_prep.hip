@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_prep_kernel(PrepParams p) {
     p.hdr->n_chunks = chunk_base;
     p.hdr->flags = flags;
     p.hdr->tail_work = tail_work ? 1u : 0u;
+    p.hdr->item_ticket = 0u;   // the intra-chunk kernel's item counter
   }
 }
 
