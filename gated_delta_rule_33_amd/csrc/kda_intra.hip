@@ -846,13 +846,13 @@ struct TicketNextItem {
   TableHeader* hdr;
   int64_t n_items, grid;
   uint32_t ticket;   // thread 0's
-  __device__ void draw() {
-    if (threadIdx.x == 0) ticket = atomicAdd(&hdr->item_ticket, 1u);
+  __device__ void draw() {   // only while items outnumber workgroups (else the counter is not zeroed)
+    if (threadIdx.x == 0 && n_items > grid) ticket = atomicAdd(&hdr->item_ticket, 1u);
   }
   __device__ void publish() const {
     if (threadIdx.x == 0) {
       const int64_t t = grid + (int64_t)ticket;
-      *s_next = t < n_items ? n_items - 1 - t : -1;
+      *s_next = n_items > grid && t < n_items ? n_items - 1 - t : -1;
     }
   }
   __device__ int64_t operator()() const { return uniform_i64(s_next); }
@@ -901,11 +901,11 @@ hipError_t launch_intra4_t(const CallArgs& a) {
   if (e != hipSuccess) return e;
   const int64_t items = (a.n_max > 0 ? a.cmax : a.B * a.nc_fixed) * a.H;
   if (items <= 0) return hipSuccess;
-  if (a.n_max == 0) {   // with segment ids the table kernel zeroes the item counter
+  const unsigned grid = (unsigned)std::min<int64_t>(items, 2 * (int64_t)cu_count());
+  if (a.n_max == 0 && items > (int64_t)grid) {   // with segment ids the table kernel zeroes the item counter
     e = launch_fill_zero(reinterpret_cast<float*>(&a.hdr->item_ticket), 1, a.stream);
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = (unsigned)std::min<int64_t>(items, 2 * (int64_t)cu_count());
   hipLaunchKernelGGL(kern, dim3(grid), dim3(256), smem, a.stream, p);
   return hipGetLastError();
 }
