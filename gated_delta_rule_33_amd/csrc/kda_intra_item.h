@@ -270,7 +270,7 @@ struct NoNextItem {
 // longer needed, next_item() (called by every lane, after the item's first
 // barriers, with a result alike in all lanes) names the next item this
 // workgroup will run, next_item.info(p, item) its head, tokens and length,
-// (next_item.publish(), called by every lane before the item's second
+// (next_item.publish(), called by every lane before the item's third
 // barrier, lets thread 0 put that answer in LDS), and that item's rows are
 // loaded into `next` (nothing for -1), so that their
 // latency overlaps the rest of this item.  kEarlyV issues the item's value
@@ -371,7 +371,6 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     if (m == 0) frag_wr(sm.Gf[R], 32 * kb, gq, gx[kb]);
     if (m == 15) frag_wr(sm.Gl[R], 32 * kb, gq, gx[kb]);
   }
-  next_item.publish();
   block_sync();   // B1: first and last rows of every block
 
   // ---- per-wave factor rows (read back only by this wave until B2):
@@ -490,6 +489,7 @@ __device__ __forceinline__ void intra4_item(const IntraParams& p, int64_t item, 
     qf.store(rec + L::kQg + (int64_t)(R * KB + kb) * tile_bytes<PQ>(), lane);
     frag_wr(sm.X + r_own * S::XP, 32 * kb, gq, xx);
   }
+  next_item.publish();
   block_sync();   // B2: X, nk, beta, factor rows
   // The next item's rows (this item's are dead from here on), issued before
   // this item's larger stores.
