@@ -838,9 +838,10 @@ __global__ __launch_bounds__(kIntraThreads, 1) void kda_intra_kernel(IntraParams
 
 // The next item of a workgroup that takes its items from a counter: thread 0
 // draws a ticket when the item starts (the atomic's latency passes under the
-// item's first phases: its answer is needed only before the third barrier); tickets past the n_items - gridDim.x items left after every
-// workgroup's first mean none.  Items are handed out from the last down, as
-// with a fixed stride, so the first chunks still run last.
+// item's first phases: its answer is needed only before the third barrier);
+// tickets past the n_items - gridDim.x items left after every workgroup's
+// first mean none.  Items are handed out from the last down, as with a fixed
+// stride, so the first chunks still run last.
 struct TicketNextItem {
   int64_t* s_next;
   TableHeader* hdr;
